@@ -1,0 +1,187 @@
+/*
+ * sqkv.h -- C ABI of libsqkv: chunked ring attention and the Ulysses
+ * sequence<->head layout transform on one AMD MI355X (gfx950).
+ *
+ * Sources (the pages this library implements):
+ *   [RA] Ring-attention Q&A "Как работает sequence parallelism в контексте LLM?"
+ *        (aivaro.ru, answer 425): sections 2-3 (contiguous sequence chunks,
+ *        ring of devices, P-1 exchanges) and section 5 (per-chunk scores,
+ *        max, exp, normaliser, output, merged by an online softmax).
+ *   [UL] "Метод контекстного параллелизма Ulysses" (Telegram channel
+ *        stuffynlp, post 213): the all_to_all from [local_seqlen, global_heads,
+ *        head_dim] to [global_seqlen, local_heads, head_dim] and back, the
+ *        head-count limit and GQA key/value head copying.
+ *   [HF] "Paralelismo de secuencias en 🤗 accelerate": section "En qué se
+ *        diferencia Ulysses SP de FSDP CP" (heads divisible by the group size).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *   never allocates, frees or synchronises; each call validates its arguments
+ *   on the host and then enqueues kernels on `stream` (a hipStream_t; NULL is
+ *   the null stream).  Results are ready when the stream's work completes.
+ * - Validation happens before any HIP call.  A non-OK status means nothing was
+ *   enqueued; sqkv_last_error() then returns a message (thread-local).
+ * - All calls are stateless and may be called from several host threads.
+ *   Calls that overlap in time on one device must not write the same memory.
+ * - Attention tensors are 4-D [B, H, n, d] views: element (b, h, t, e) sits at
+ *   ptr + b*sb + h*sh + t*sn + e (strides in ELEMENTS, innermost stride 1).
+ *   A [S, H, d] tensor (one Ulysses share) is the view B=1, sb=0 (unused),
+ *   sh=d, sn=H*d.  Row statistics `lse` are dense float32 [B, H, n]:
+ *   element (b, h, t) at lse + (b*H + h)*n + t.
+ * - lse is the natural-log log-sum-exp of the scaled logits over the visible
+ *   keys.  A query row with no visible key has output 0 and lse = -inf; a
+ *   partial with lse = -inf is the identity of the merge.
+ */
+#ifndef SQKV_H_
+#define SQKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sqkv_status {
+  SQKV_OK = 0,
+  SQKV_EINVAL = 1,       /* inconsistent sizes, null pointers, bad aliasing */
+  SQKV_EUNSUPPORTED = 2, /* valid request outside what the kernels implement */
+  SQKV_EHIP = 3          /* the HIP runtime reported an error on launch */
+} sqkv_status;
+
+typedef enum sqkv_dtype {
+  SQKV_F32 = 0,  /* IEEE binary32 */
+  SQKV_BF16 = 1  /* bfloat16 (upper half of binary32), round-to-nearest-even */
+} sqkv_dtype;
+
+/* A strided [B, H, n, d] view; strides in elements; the d stride is 1. */
+typedef struct sqkv_view {
+  void* ptr;
+  int64_t sb, sh, sn;
+} sqkv_view;
+
+/*
+ * ra_chunk_attention -- one ring step: a query chunk against one key/value
+ * chunk, merged into a running result.  [RA] section 5: scores Q K^T, row
+ * max, exp, row sum (normaliser) and the weighted sum of V for the chunk,
+ * then the online-softmax rescale that folds this chunk's partial into the
+ * running output.
+ *
+ *   q      [B, Hq,  n_q, d]  in_dtype          query chunk
+ *   k, v   [B, Hkv, n_k, d]  in_dtype          key / value chunk
+ *   o_in   [B, Hq,  n_q, d]  acc_dtype         running output, or ptr == NULL
+ *   lse_in [B, Hq,  n_q]     float32           running lse (NULL iff o_in.ptr is)
+ *   o_out  [B, Hq,  n_q, d]  out_dtype         merged output
+ *   lse_out[B, Hq,  n_q]     float32           merged lse
+ *
+ * Query row t sits at global position q_pos0 + t and key u at k_pos0 + u;
+ * with causal != 0 a key is visible iff its position <= the query's.
+ * Logits are scale * (q . k) with scale > 0.  Query head h reads key/value
+ * head h / (Hq / Hkv) (GQA).  Without o_in the call writes this chunk's
+ * partial (O_j, lse_j); with o_in it writes merge((o_in, lse_in), (O_j, lse_j)).
+ * o_out may be exactly o_in (same pointer, strides and dtype) and lse_out may
+ * be exactly lse_in: the update is then in place.  Any other overlap between
+ * an output and an input is rejected.
+ *
+ * Supported: d in {64, 128}; in_dtype F32 (fp32 arithmetic throughout) or
+ * BF16 (bf16 MFMA products, fp32 accumulation, softmax weights rounded to
+ * bf16 for the P*V product); acc_dtype, out_dtype F32 or BF16.  Pointers must
+ * be 16-byte aligned and every stride a multiple of 16 bytes.
+ * Returns SQKV_OK, SQKV_EINVAL (null pointer, Hq % Hkv != 0, negative size,
+ * scale not finite and > 0, overlap), SQKV_EUNSUPPORTED (d, dtype,
+ * alignment) or SQKV_EHIP.
+ */
+sqkv_status ra_chunk_attention(sqkv_view q, sqkv_view k, sqkv_view v,
+                               sqkv_view o_in, const float* lse_in,
+                               sqkv_view o_out, float* lse_out,
+                               int B, int Hq, int Hkv, int n_q, int n_k, int d,
+                               sqkv_dtype in_dtype, sqkv_dtype acc_dtype, sqkv_dtype out_dtype,
+                               float scale, int causal, int64_t q_pos0, int64_t k_pos0,
+                               void* stream);
+
+/*
+ * ra_ring_attention -- the whole ring for one virtual rank, with the P
+ * key/value chunks resident in one HBM pool.  [RA] sections 2-3: the
+ * sequence of length L = P*n is cut into P contiguous chunks (chunk j holds
+ * positions j*n .. j*n + n - 1); the rank holding query chunk `rank` meets
+ * every key/value chunk once, its own first and then, at step s, the chunk
+ * that arrived from the previous device, j = (rank - s) mod P.  The send and
+ * receive of the pages become reading chunk j in place.
+ *
+ *   q        [B, Hq, n, d]  in_dtype      the rank's query chunk
+ *   k, v     [B, Hkv, n, d] in_dtype      chunk 0 of the pool; chunk j starts
+ *                                         j*k_chunk_stride (v_chunk_stride)
+ *                                         elements after it
+ *   o        [B, Hq, n, d]  out_dtype     result
+ *   lse      [B, Hq, n]     float32       result
+ *   o_work   [B, Hq, n, d]  float32       accumulator used between steps when
+ *                                         out_dtype is BF16 and more than one
+ *                                         chunk is visited; else may be NULL
+ *
+ * With causal != 0, chunks after the rank's own (j > rank) are skipped,
+ * earlier ones are fully visible and the rank's own chunk is masked on its
+ * diagonal.  Each visited chunk is one ra_chunk_attention launch merging in
+ * fp32; the last one writes o in out_dtype.  Same support and status codes as
+ * ra_chunk_attention; additionally EINVAL for rank outside [0, P) or P < 1.
+ */
+sqkv_status ra_ring_attention(sqkv_view q, sqkv_view k, sqkv_view v,
+                              int64_t k_chunk_stride, int64_t v_chunk_stride,
+                              sqkv_view o, float* lse, sqkv_view o_work,
+                              int B, int Hq, int Hkv, int n, int d, int P, int rank,
+                              sqkv_dtype in_dtype, sqkv_dtype out_dtype,
+                              float scale, int causal, void* stream);
+
+/*
+ * ra_lse_merge -- the online-softmax merge of two partial attentions over
+ * disjoint key sets ([RA] section 5, the rescale of the running output and
+ * normaliser by the exponent of the change in the running maximum), in the
+ * log-sum-exp form: lse = log(exp(lse_a) + exp(lse_b)),
+ * o = exp(lse_a - lse) * o_a + exp(lse_b - lse) * o_b, evaluated in fp32
+ * with the larger lse factored out.
+ *
+ *   o_a, lse_a (a_dtype), o_b, lse_b (b_dtype) : [B, H, n, d] and [B, H, n]
+ *   o_out, lse_out (out_dtype)                  : result
+ * o_out may be exactly o_a or o_b (same pointer, strides, dtype); lse_out may
+ * be exactly lse_a or lse_b.  d in {64, 128}; 16-byte alignment as above.
+ */
+sqkv_status ra_lse_merge(sqkv_view o_a, const float* lse_a, sqkv_dtype a_dtype,
+                         sqkv_view o_b, const float* lse_b, sqkv_dtype b_dtype,
+                         sqkv_view o_out, float* lse_out, sqkv_dtype out_dtype,
+                         int B, int H, int n, int d, void* stream);
+
+/*
+ * ulysses_seq_to_head -- the all_to_all before attention ([UL]), on one HBM
+ * pool holding all P shards.  dense src [P][L/P][H_src][d] (shard p = tokens
+ * p*L/P ..) becomes dense dst [P][L][H_dst/P][d] (rank r = the whole sequence
+ * for heads r*H_dst/P .. (r+1)*H_dst/P - 1):
+ *     dst[r][p*(L/P) + t][h'] = src[p][t][ (r*H_dst/P + h') / (H_dst/H_src) ]
+ * H_dst = H_src moves query (or output) heads; H_dst = R*H_src copies every
+ * key/value head R times in place (GQA: [UL] copies KV heads up to the group
+ * size; use H_dst = max(H_kv, P)).  Elements are moved as raw bits of
+ * elem_bytes (1, 2, 4 or 8) bytes.  src and dst must not overlap.
+ * EINVAL: null pointer, P < 1, L % P, H_dst % P, H_dst % H_src ([UL], [HF]:
+ * the group cannot exceed the head count and must divide it), overlap.
+ */
+sqkv_status ulysses_seq_to_head(const void* src, void* dst, int P, int64_t L,
+                                int H_src, int H_dst, int d, int elem_bytes, void* stream);
+
+/*
+ * ulysses_head_to_seq -- the all_to_all after attention ([UL]): dense src
+ * [P][L][H/P][d] becomes dense dst [P][L/P][H][d], the inverse of
+ * ulysses_seq_to_head with H_src = H_dst = H:
+ *     dst[p][t][r*H/P + h'] = src[r][p*(L/P) + t][h']
+ * Same arguments and errors as above.
+ */
+sqkv_status ulysses_head_to_seq(const void* src, void* dst, int P, int64_t L,
+                                int H, int d, int elem_bytes, void* stream);
+
+/* Message for the last non-OK status returned on this host thread ("" if the
+ * last call succeeded).  The string stays valid until the next call. */
+const char* sqkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQKV_H_ */

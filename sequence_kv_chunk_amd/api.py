@@ -1,0 +1,205 @@
+"""Thin ctypes binding of libsqkv (include/sqkv.h) for torch tensors.
+
+Argument marshalling only: every function passes device pointers, element
+strides, sizes and the current HIP stream of the tensors' device to the C ABI
+and raises ``SqkvError`` with the library's message on a non-OK status.  All
+computation happens in the HIP kernels; there is no fallback path.  Importing
+this module loads ``libsqkv.so`` and fails loudly if it has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("SQKV_LIB", os.path.join(_HERE, "libsqkv.so"))
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libsqkv.so not found at {LIB_PATH}; build it with `python -m sequence_kv_chunk_amd.build` "
+        "(or __graft_entry__.build()) -- there is no non-HIP fallback")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+SQKV_OK, SQKV_EINVAL, SQKV_EUNSUPPORTED, SQKV_EHIP = 0, 1, 2, 3
+SQKV_F32, SQKV_BF16 = 0, 1
+STATUS_NAMES = {0: "SQKV_OK", 1: "SQKV_EINVAL", 2: "SQKV_EUNSUPPORTED", 3: "SQKV_EHIP"}
+
+
+class SqkvView(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("sb", ctypes.c_int64), ("sh", ctypes.c_int64),
+                ("sn", ctypes.c_int64)]
+
+
+class SqkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_c_int, _c_i64, _c_f, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+_V = SqkvView
+
+_lib.sqkv_last_error.restype = ctypes.c_char_p
+_lib.sqkv_last_error.argtypes = []
+_lib.ra_chunk_attention.restype = _c_int
+_lib.ra_chunk_attention.argtypes = [_V, _V, _V, _V, _vp, _V, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                    _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _c_i64, _c_i64, _vp]
+_lib.ra_ring_attention.restype = _c_int
+_lib.ra_ring_attention.argtypes = [_V, _V, _V, _c_i64, _c_i64, _V, _vp, _V, _c_int, _c_int, _c_int, _c_int,
+                                   _c_int, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _vp]
+_lib.ra_lse_merge.restype = _c_int
+_lib.ra_lse_merge.argtypes = [_V, _vp, _c_int, _V, _vp, _c_int, _V, _vp, _c_int, _c_int, _c_int, _c_int,
+                              _c_int, _vp]
+_lib.ulysses_seq_to_head.restype = _c_int
+_lib.ulysses_seq_to_head.argtypes = [_vp, _vp, _c_int, _c_i64, _c_int, _c_int, _c_int, _c_int, _vp]
+_lib.ulysses_head_to_seq.restype = _c_int
+_lib.ulysses_head_to_seq.argtypes = [_vp, _vp, _c_int, _c_i64, _c_int, _c_int, _c_int, _vp]
+
+EXPORTED = ("ra_chunk_attention", "ra_ring_attention", "ra_lse_merge", "ulysses_seq_to_head",
+            "ulysses_head_to_seq", "sqkv_last_error")
+
+
+def _check(status: int):
+    if status != SQKV_OK:
+        raise SqkvError(status, _lib.sqkv_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SQKV_F32
+    if t.dtype == torch.bfloat16:
+        return SQKV_BF16
+    raise SqkvError(SQKV_EUNSUPPORTED, f"dtype {t.dtype} (need float32 or bfloat16)")
+
+
+def _bhnd(t: torch.Tensor) -> torch.Tensor:
+    """[B, H, n, d] as is; a [S, H, d] Ulysses share becomes the view [1, H, S, d]."""
+    if t.dim() == 3:
+        return t.unsqueeze(0).transpose(1, 2)
+    if t.dim() != 4:
+        raise SqkvError(SQKV_EINVAL, f"expected a [B, H, n, d] or [S, H, d] tensor, got {tuple(t.shape)}")
+    return t
+
+
+def _view(t: torch.Tensor | None) -> SqkvView:
+    if t is None:
+        return SqkvView(None, 0, 0, 0)
+    if t.stride(-1) != 1:
+        raise SqkvError(SQKV_EINVAL, "innermost (d) stride must be 1")
+    return SqkvView(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream(t: torch.Tensor) -> int:
+    if not t.is_cuda:
+        raise SqkvError(SQKV_EINVAL, "tensors must live on a GPU")
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) != 1:
+        raise SqkvError(SQKV_EINVAL, f"tensors on different devices: {devs}")
+
+
+def _lse_ptr(t: torch.Tensor | None, rows: int):
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != rows:
+        raise SqkvError(SQKV_EINVAL, f"lse must be a dense float32 tensor of {rows} elements")
+    return t.data_ptr()
+
+
+def ra_chunk_attention(q, k, v, o_out, lse_out, *, o_in=None, lse_in=None, scale: float = 1.0,
+                       causal: bool = False, q_pos0: int = 0, k_pos0: int = 0):
+    """One ring step: merge attention of ``q`` over chunk (k, v) into (o_in, lse_in)
+    (or write the chunk's own partial when o_in is None) as (o_out, lse_out)."""
+    q4, k4, v4, oo4 = _bhnd(q), _bhnd(k), _bhnd(v), _bhnd(o_out)
+    oi4 = _bhnd(o_in) if o_in is not None else None
+    _same_device(q4, k4, v4, oo4, oi4, lse_out, lse_in)
+    B, Hq, n_q, d = q4.shape
+    Hkv, n_k = k4.shape[1], k4.shape[2]
+    if k4.shape != v4.shape or tuple(oo4.shape) != (B, Hq, n_q, d) or k4.shape[0] != B or k4.shape[3] != d:
+        raise SqkvError(SQKV_EINVAL, "q/k/v/o shapes disagree")
+    if oi4 is not None and tuple(oi4.shape) != (B, Hq, n_q, d):
+        raise SqkvError(SQKV_EINVAL, "o_in shape disagrees")
+    if q4.dtype != k4.dtype or q4.dtype != v4.dtype:
+        raise SqkvError(SQKV_EINVAL, "q, k, v must share a dtype")
+    rows = B * Hq * n_q
+    acc_dt = _dtype_code(oi4) if oi4 is not None else SQKV_F32
+    with torch.cuda.device(q4.device):
+        st = _lib.ra_chunk_attention(_view(q4), _view(k4), _view(v4), _view(oi4), _lse_ptr(lse_in, rows),
+                                     _view(oo4), _lse_ptr(lse_out, rows), B, Hq, Hkv, n_q, n_k, d,
+                                     _dtype_code(q4), acc_dt, _dtype_code(oo4), float(scale), int(bool(causal)),
+                                     int(q_pos0), int(k_pos0), _stream(q4))
+    _check(st)
+
+
+def ra_ring_attention(q, k_pool, v_pool, o, lse, *, rank: int, o_work=None, scale: float = 1.0,
+                      causal: bool = False):
+    """Ring attention of query chunk ``q`` ([B, Hq, n, d]) of virtual rank ``rank``
+    over the P resident chunks of ``k_pool``/``v_pool`` ([P, B, Hkv, n, d])."""
+    if k_pool.dim() != 5 or v_pool.shape != k_pool.shape:
+        raise SqkvError(SQKV_EINVAL, "k_pool, v_pool must be [P, B, Hkv, n, d]")
+    _same_device(q, k_pool, v_pool, o, lse, o_work)
+    P = k_pool.shape[0]
+    B, Hq, n, d = q.shape
+    if tuple(o.shape) != (B, Hq, n, d) or k_pool.shape[3] != n or k_pool.shape[1] != B:
+        raise SqkvError(SQKV_EINVAL, "shapes disagree")
+    if o_work is not None and (o_work.dtype != torch.float32 or tuple(o_work.shape) != (B, Hq, n, d)):
+        raise SqkvError(SQKV_EINVAL, "o_work must be float32 [B, Hq, n, d]")
+    with torch.cuda.device(q.device):
+        st = _lib.ra_ring_attention(_view(q), _view(k_pool[0]), _view(v_pool[0]), k_pool.stride(0),
+                                    v_pool.stride(0), _view(o), _lse_ptr(lse, B * Hq * n), _view(o_work),
+                                    B, Hq, k_pool.shape[2], n, d, P, int(rank), _dtype_code(q),
+                                    _dtype_code(o), float(scale), int(bool(causal)), _stream(q))
+    _check(st)
+
+
+def ra_lse_merge(o_a, lse_a, o_b, lse_b, o_out, lse_out):
+    """(o_out, lse_out) = merge((o_a, lse_a), (o_b, lse_b)) over [B, H, n, d] tensors."""
+    a4, b4, o4 = _bhnd(o_a), _bhnd(o_b), _bhnd(o_out)
+    _same_device(a4, b4, o4, lse_a, lse_b, lse_out)
+    B, H, n, d = a4.shape
+    if b4.shape != a4.shape or o4.shape != a4.shape:
+        raise SqkvError(SQKV_EINVAL, "shapes disagree")
+    rows = B * H * n
+    with torch.cuda.device(a4.device):
+        st = _lib.ra_lse_merge(_view(a4), _lse_ptr(lse_a, rows), _dtype_code(a4), _view(b4), _lse_ptr(lse_b, rows),
+                               _dtype_code(b4), _view(o4), _lse_ptr(lse_out, rows), _dtype_code(o4), B, H, n, d,
+                               _stream(a4))
+    _check(st)
+
+
+def _dense(t: torch.Tensor, name: str):
+    if not t.is_contiguous():
+        raise SqkvError(SQKV_EINVAL, f"{name} must be contiguous")
+
+
+def ulysses_seq_to_head(src, dst, *, H_dst: int | None = None):
+    """src [P, L/P, H_src, d] -> dst [P, L, H_dst/P, d] (H_dst defaults to H_src)."""
+    _dense(src, "src"); _dense(dst, "dst")
+    _same_device(src, dst)
+    P, n, H_src, d = src.shape
+    H_dst = H_src if H_dst is None else int(H_dst)
+    if dst.dtype != src.dtype or tuple(dst.shape) != (P, P * n, H_dst // P, d):
+        raise SqkvError(SQKV_EINVAL, f"dst must be {src.dtype} [{P}, {P * n}, {H_dst // P}, {d}]")
+    with torch.cuda.device(src.device):
+        st = _lib.ulysses_seq_to_head(src.data_ptr(), dst.data_ptr(), P, P * n, H_src, H_dst, d,
+                                      src.element_size(), _stream(src))
+    _check(st)
+
+
+def ulysses_head_to_seq(src, dst):
+    """src [P, L, H/P, d] -> dst [P, L/P, H, d]."""
+    _dense(src, "src"); _dense(dst, "dst")
+    _same_device(src, dst)
+    P, L, Hl, d = src.shape
+    if dst.dtype != src.dtype or tuple(dst.shape) != (P, L // P, Hl * P, d):
+        raise SqkvError(SQKV_EINVAL, f"dst must be {src.dtype} [{P}, {L // P}, {Hl * P}, {d}]")
+    with torch.cuda.device(src.device):
+        st = _lib.ulysses_head_to_seq(src.data_ptr(), dst.data_ptr(), P, L, Hl * P, d, src.element_size(),
+                                      _stream(src))
+    _check(st)

@@ -1,0 +1,349 @@
+// Host side of the C ABI declared in include/sqkv.h: argument validation
+// (before any HIP call), kernel selection and the ring loop over resident
+// chunks.  No allocation, no synchronisation; every launch goes on the
+// caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/sqkv.h"
+#include "sqkv_internal.h"
+
+#define SQKV_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sqkv_status fail(sqkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+sqkv_status ok() {
+  g_last_error.clear();
+  return SQKV_OK;
+}
+
+sqkv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SQKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int dtype_bytes(int dt) { return dt == SQKV_F32 ? 4 : 2; }
+bool dtype_ok(int dt) { return dt == SQKV_F32 || dt == SQKV_BF16; }
+
+// Byte range [lo, hi) touched by a [B, H, n, d] view (strides >= 0).
+struct Range {
+  uintptr_t lo = 0, hi = 0;
+  bool empty() const { return hi <= lo; }
+};
+
+Range view_range(const sqkv_view& v, int B, int H, int64_t n, int d, int eb) {
+  Range r;
+  if (B <= 0 || H <= 0 || n <= 0 || d <= 0) return r;
+  int64_t last = (int64_t)(B - 1) * v.sb + (int64_t)(H - 1) * v.sh + (n - 1) * v.sn + d;
+  r.lo = (uintptr_t)v.ptr;
+  r.hi = r.lo + (uintptr_t)(last * eb);
+  return r;
+}
+
+Range dense_range(const void* p, int64_t elems, int eb) {
+  Range r;
+  if (elems <= 0) return r;
+  r.lo = (uintptr_t)p;
+  r.hi = r.lo + (uintptr_t)(elems * eb);
+  return r;
+}
+
+bool overlap(const Range& a, const Range& b) {
+  if (a.empty() || b.empty()) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool same_view(const sqkv_view& a, const sqkv_view& b) {
+  return a.ptr == b.ptr && a.sb == b.sb && a.sh == b.sh && a.sn == b.sn;
+}
+
+// 16-byte alignment of the base pointer and of every stride (in bytes).
+bool view_aligned(const sqkv_view& v, int eb) {
+  if (((uintptr_t)v.ptr) % 16) return false;
+  return (v.sb * eb) % 16 == 0 && (v.sh * eb) % 16 == 0 && (v.sn * eb) % 16 == 0;
+}
+
+bool strides_nonneg(const sqkv_view& v) { return v.sb >= 0 && v.sh >= 0 && v.sn >= 0; }
+
+struct AttnCheck {
+  sqkv_view q, k, v, o_in, o_out;
+  const float* lse_in;
+  float* lse_out;
+  int B, Hq, Hkv;
+  int64_t n_q, n_k, kv_extent_extra_bytes;  // extra bytes past chunk 0 (ring pools)
+  int d, in_dt, acc_dt, out_dt;
+  float scale;
+};
+
+// Validation shared by ra_chunk_attention and ra_ring_attention.
+sqkv_status check_attention(const AttnCheck& a) {
+  if (a.B < 1 || a.Hq < 1 || a.Hkv < 1 || a.n_q < 0 || a.n_k < 0)
+    return fail(SQKV_EINVAL, "sizes must be positive (B=%d Hq=%d Hkv=%d n_q=%lld n_k=%lld)", a.B, a.Hq,
+                a.Hkv, (long long)a.n_q, (long long)a.n_k);
+  if (a.Hq % a.Hkv != 0)
+    return fail(SQKV_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", a.Hq, a.Hkv);
+  if (!(a.scale > 0.f) || !std::isfinite(a.scale))
+    return fail(SQKV_EINVAL, "scale must be finite and > 0 (got %g)", (double)a.scale);
+  if (a.d != 64 && a.d != 128) return fail(SQKV_EUNSUPPORTED, "head dim d=%d not in {64, 128}", a.d);
+  if (!dtype_ok(a.in_dt) || !dtype_ok(a.acc_dt) || !dtype_ok(a.out_dt))
+    return fail(SQKV_EUNSUPPORTED, "dtype must be SQKV_F32 or SQKV_BF16");
+  if (a.B > 65535 || a.Hq > 65535) return fail(SQKV_EUNSUPPORTED, "B and Hq must be <= 65535");
+  if (a.n_q > (1ll << 30) || a.n_k > (1ll << 30))
+    return fail(SQKV_EUNSUPPORTED, "chunk lengths above 2^30 are not supported");
+  if (a.n_q == 0) return ok();
+  if (!a.q.ptr || !a.o_out.ptr || !a.lse_out) return fail(SQKV_EINVAL, "null q, o_out or lse_out");
+  if (a.n_k > 0 && (!a.k.ptr || !a.v.ptr)) return fail(SQKV_EINVAL, "null k or v");
+  if ((a.o_in.ptr == nullptr) != (a.lse_in == nullptr))
+    return fail(SQKV_EINVAL, "o_in and lse_in must both be given or both be NULL");
+  for (const sqkv_view* v : {&a.q, &a.k, &a.v, &a.o_in, &a.o_out})
+    if (!strides_nonneg(*v)) return fail(SQKV_EINVAL, "negative stride");
+  const int ieb = dtype_bytes(a.in_dt);
+  if (!view_aligned(a.q, ieb) || (a.n_k > 0 && (!view_aligned(a.k, ieb) || !view_aligned(a.v, ieb))))
+    return fail(SQKV_EUNSUPPORTED, "q/k/v pointers and strides must be 16-byte aligned");
+  if (!view_aligned(a.o_out, dtype_bytes(a.out_dt)) ||
+      (a.o_in.ptr && !view_aligned(a.o_in, dtype_bytes(a.acc_dt))))
+    return fail(SQKV_EUNSUPPORTED, "output pointers and strides must be 16-byte aligned");
+  if (((uintptr_t)a.lse_out) % 4 || ((uintptr_t)a.lse_in) % 4)
+    return fail(SQKV_EUNSUPPORTED, "lse must be 4-byte aligned");
+  // aliasing: outputs may only coincide exactly with the running state
+  const int64_t rows = (int64_t)a.B * a.Hq * a.n_q;
+  Range ro = view_range(a.o_out, a.B, a.Hq, a.n_q, a.d, dtype_bytes(a.out_dt));
+  Range rl = dense_range(a.lse_out, rows, 4);
+  Range rq = view_range(a.q, a.B, a.Hq, a.n_q, a.d, ieb);
+  Range rk = view_range(a.k, a.B, a.Hkv, a.n_k, a.d, ieb);
+  Range rv = view_range(a.v, a.B, a.Hkv, a.n_k, a.d, ieb);
+  if (!rk.empty()) rk.hi += a.kv_extent_extra_bytes;
+  if (!rv.empty()) rv.hi += a.kv_extent_extra_bytes;
+  for (const Range* r : {&rq, &rk, &rv}) {
+    if (overlap(ro, *r)) return fail(SQKV_EINVAL, "o_out overlaps q, k or v");
+    if (overlap(rl, *r)) return fail(SQKV_EINVAL, "lse_out overlaps q, k or v");
+  }
+  if (overlap(ro, rl)) return fail(SQKV_EINVAL, "o_out overlaps lse_out");
+  if (a.o_in.ptr) {
+    Range ri = view_range(a.o_in, a.B, a.Hq, a.n_q, a.d, dtype_bytes(a.acc_dt));
+    Range rli = dense_range(a.lse_in, rows, 4);
+    bool o_alias = same_view(a.o_in, a.o_out) && a.acc_dt == a.out_dt;
+    if (!o_alias && overlap(ri, ro)) return fail(SQKV_EINVAL, "o_out partially overlaps o_in");
+    if (a.lse_in != a.lse_out && overlap(rli, rl)) return fail(SQKV_EINVAL, "lse_out partially overlaps lse_in");
+    if (overlap(ri, rl) || overlap(rli, ro)) return fail(SQKV_EINVAL, "o and lse buffers overlap");
+  }
+  return ok();
+}
+
+sqkv::AttnParams make_params(const sqkv_view& q, const sqkv_view& k, const sqkv_view& v, const sqkv_view& o_in,
+                             const float* lse_in, const sqkv_view& o_out, float* lse_out, int B, int Hq,
+                             int Hkv, int n_q, int n_k, int acc_dt, int out_dt, float scale, int causal,
+                             int64_t q_pos0, int64_t k_pos0) {
+  sqkv::AttnParams p;
+  p.q = q.ptr; p.q_sb = q.sb; p.q_sh = q.sh; p.q_sn = q.sn;
+  p.k = k.ptr; p.k_sb = k.sb; p.k_sh = k.sh; p.k_sn = k.sn;
+  p.v = v.ptr; p.v_sb = v.sb; p.v_sh = v.sh; p.v_sn = v.sn;
+  p.o_in = o_in.ptr; p.oi_sb = o_in.sb; p.oi_sh = o_in.sh; p.oi_sn = o_in.sn;
+  p.lse_in = o_in.ptr ? lse_in : nullptr;
+  p.o_out = o_out.ptr; p.oo_sb = o_out.sb; p.oo_sh = o_out.sh; p.oo_sn = o_out.sn;
+  p.lse_out = lse_out;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.n_q = n_q; p.n_k = n_k;
+  p.group = Hq / Hkv;
+  p.acc_dtype = acc_dt;
+  p.out_dtype = out_dt;
+  p.scale_log2 = scale * 1.44269504088896340736f;
+  p.causal = causal ? 1 : 0;
+  p.q_pos0 = q_pos0;
+  p.k_pos0 = k_pos0;
+  return p;
+}
+
+hipError_t launch_attention(const sqkv::AttnParams& p, int d, int in_dt, hipStream_t s) {
+  return in_dt == SQKV_BF16 ? sqkv::launch_attn_bf16(p, d, s) : sqkv::launch_attn_f32(p, d, s);
+}
+
+}  // namespace
+
+SQKV_EXPORT const char* sqkv_last_error(void) { return g_last_error.c_str(); }
+
+SQKV_EXPORT sqkv_status ra_chunk_attention(sqkv_view q, sqkv_view k, sqkv_view v, sqkv_view o_in,
+                                           const float* lse_in, sqkv_view o_out, float* lse_out, int B,
+                                           int Hq, int Hkv, int n_q, int n_k, int d, sqkv_dtype in_dtype,
+                                           sqkv_dtype acc_dtype, sqkv_dtype out_dtype, float scale,
+                                           int causal, int64_t q_pos0, int64_t k_pos0, void* stream) {
+  AttnCheck a{q, k, v, o_in, o_out, lse_in, lse_out, B, Hq, Hkv, n_q, n_k, 0, d,
+              in_dtype, acc_dtype, out_dtype, scale};
+  sqkv_status st = check_attention(a);
+  if (st != SQKV_OK || n_q == 0) return st;
+  sqkv::AttnParams p = make_params(q, k, v, o_in, lse_in, o_out, lse_out, B, Hq, Hkv, n_q, n_k, acc_dtype,
+                                   out_dtype, scale, causal, q_pos0, k_pos0);
+  return hip_status(launch_attention(p, d, in_dtype, (hipStream_t)stream), "ra_chunk_attention launch");
+}
+
+SQKV_EXPORT sqkv_status ra_ring_attention(sqkv_view q, sqkv_view k, sqkv_view v, int64_t k_chunk_stride,
+                                          int64_t v_chunk_stride, sqkv_view o, float* lse, sqkv_view o_work,
+                                          int B, int Hq, int Hkv, int n, int d, int P, int rank,
+                                          sqkv_dtype in_dtype, sqkv_dtype out_dtype, float scale, int causal,
+                                          void* stream) {
+  if (P < 1 || rank < 0 || rank >= P) return fail(SQKV_EINVAL, "need P >= 1 and 0 <= rank < P (P=%d rank=%d)", P, rank);
+  if (k_chunk_stride < 0 || v_chunk_stride < 0) return fail(SQKV_EINVAL, "negative chunk stride");
+  const int ieb = dtype_bytes(in_dtype);
+  if ((k_chunk_stride * ieb) % 16 || (v_chunk_stride * ieb) % 16)
+    return fail(SQKV_EUNSUPPORTED, "chunk strides must be multiples of 16 bytes");
+  // chunks visited, own chunk first, then the one arriving from the previous rank
+  std::vector<int> visit;
+  for (int s = 0; s < P; ++s) {
+    int j = ((rank - s) % P + P) % P;
+    if (causal && j > rank) continue;  // entirely in the future of every query
+    visit.push_back(j);
+  }
+  const bool direct = out_dtype == SQKV_F32 || visit.size() == 1;
+  sqkv_view acc = (out_dtype == SQKV_F32) ? o : o_work;
+  AttnCheck a{q, k, v, sqkv_view{nullptr, 0, 0, 0}, o, nullptr, lse, B, Hq, Hkv, n, n,
+              (int64_t)(P - 1) * std::max(k_chunk_stride, v_chunk_stride) * ieb, d,
+              in_dtype, SQKV_F32, out_dtype, scale};
+  sqkv_status st = check_attention(a);
+  if (st != SQKV_OK || n == 0) return st;
+  if (!direct) {
+    if (!o_work.ptr) return fail(SQKV_EINVAL, "o_work (fp32) is required for a bf16 result over several chunks");
+    AttnCheck w = a;
+    w.o_out = o_work;
+    w.out_dt = SQKV_F32;
+    st = check_attention(w);
+    if (st != SQKV_OK) return st;
+    Range rw = view_range(o_work, B, Hq, n, d, 4);
+    if (overlap(rw, view_range(o, B, Hq, n, d, dtype_bytes(out_dtype))))
+      return fail(SQKV_EINVAL, "o_work overlaps o");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  for (size_t i = 0; i < visit.size(); ++i) {
+    const int j = visit[i];
+    const bool first = i == 0, last = i + 1 == visit.size();
+    sqkv_view kj = k, vj = v;
+    kj.ptr = (char*)k.ptr + (int64_t)j * k_chunk_stride * ieb;
+    vj.ptr = (char*)v.ptr + (int64_t)j * v_chunk_stride * ieb;
+    sqkv_view in = first ? sqkv_view{nullptr, 0, 0, 0} : acc;
+    sqkv_view out = last ? o : acc;
+    const int out_dt = last ? out_dtype : SQKV_F32;
+    sqkv::AttnParams p = make_params(q, kj, vj, in, first ? nullptr : lse, out, lse, B, Hq, Hkv, n, n,
+                                     SQKV_F32, out_dt, scale, causal, (int64_t)rank * n, (int64_t)j * n);
+    hipError_t e = launch_attention(p, d, in_dtype, s);
+    if (e != hipSuccess) return hip_status(e, "ra_ring_attention launch");
+  }
+  return ok();
+}
+
+SQKV_EXPORT sqkv_status ra_lse_merge(sqkv_view o_a, const float* lse_a, sqkv_dtype a_dtype, sqkv_view o_b,
+                                     const float* lse_b, sqkv_dtype b_dtype, sqkv_view o_out, float* lse_out,
+                                     sqkv_dtype out_dtype, int B, int H, int n, int d, void* stream) {
+  if (B < 1 || H < 1 || n < 0) return fail(SQKV_EINVAL, "sizes must be positive");
+  if (d != 64 && d != 128) return fail(SQKV_EUNSUPPORTED, "head dim d=%d not in {64, 128}", d);
+  if (!dtype_ok(a_dtype) || !dtype_ok(b_dtype) || !dtype_ok(out_dtype))
+    return fail(SQKV_EUNSUPPORTED, "dtype must be SQKV_F32 or SQKV_BF16");
+  if (B > 65535 || H > 65535) return fail(SQKV_EUNSUPPORTED, "B and H must be <= 65535");
+  if (n == 0) return ok();
+  if (!o_a.ptr || !o_b.ptr || !o_out.ptr || !lse_a || !lse_b || !lse_out)
+    return fail(SQKV_EINVAL, "null pointer");
+  for (const sqkv_view* v : {&o_a, &o_b, &o_out})
+    if (!strides_nonneg(*v)) return fail(SQKV_EINVAL, "negative stride");
+  if (!view_aligned(o_a, dtype_bytes(a_dtype)) || !view_aligned(o_b, dtype_bytes(b_dtype)) ||
+      !view_aligned(o_out, dtype_bytes(out_dtype)))
+    return fail(SQKV_EUNSUPPORTED, "pointers and strides must be 16-byte aligned");
+  if (((uintptr_t)lse_a | (uintptr_t)lse_b | (uintptr_t)lse_out) % 4)
+    return fail(SQKV_EUNSUPPORTED, "lse must be 4-byte aligned");
+  const int64_t rows = (int64_t)B * H * n;
+  Range ro = view_range(o_out, B, H, n, d, dtype_bytes(out_dtype));
+  Range rl = dense_range(lse_out, rows, 4);
+  Range ra = view_range(o_a, B, H, n, d, dtype_bytes(a_dtype));
+  Range rb = view_range(o_b, B, H, n, d, dtype_bytes(b_dtype));
+  Range rla = dense_range(lse_a, rows, 4), rlb = dense_range(lse_b, rows, 4);
+  bool alias_a = same_view(o_out, o_a) && out_dtype == a_dtype;
+  bool alias_b = same_view(o_out, o_b) && out_dtype == b_dtype;
+  if ((!alias_a && overlap(ro, ra)) || (!alias_b && overlap(ro, rb)))
+    return fail(SQKV_EINVAL, "o_out partially overlaps an input");
+  if ((lse_out != lse_a && overlap(rl, rla)) || (lse_out != lse_b && overlap(rl, rlb)))
+    return fail(SQKV_EINVAL, "lse_out partially overlaps an input");
+  if (overlap(ro, rl) || overlap(ro, rla) || overlap(ro, rlb) || overlap(rl, ra) || overlap(rl, rb))
+    return fail(SQKV_EINVAL, "o and lse buffers overlap");
+  sqkv::MergeParams p;
+  p.oa = o_a.ptr; p.a_sb = o_a.sb; p.a_sh = o_a.sh; p.a_sn = o_a.sn; p.lse_a = lse_a; p.a_dtype = a_dtype;
+  p.ob = o_b.ptr; p.b_sb = o_b.sb; p.b_sh = o_b.sh; p.b_sn = o_b.sn; p.lse_b = lse_b; p.b_dtype = b_dtype;
+  p.oo = o_out.ptr; p.o_sb = o_out.sb; p.o_sh = o_out.sh; p.o_sn = o_out.sn; p.lse_o = lse_out;
+  p.o_dtype = out_dtype;
+  p.B = B; p.H = H; p.n = n;
+  return hip_status(sqkv::launch_lse_merge(p, d, (hipStream_t)stream), "ra_lse_merge launch");
+}
+
+namespace {
+
+sqkv_status check_permute(const void* src, void* dst, int P, int64_t L, int H_src, int H_dst, int d,
+                          int elem_bytes, const char* who) {
+  if (P < 1 || L < 0 || H_src < 1 || H_dst < 1 || d < 1)
+    return fail(SQKV_EINVAL, "%s: sizes must be positive", who);
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
+    return fail(SQKV_EINVAL, "%s: elem_bytes must be 1, 2, 4 or 8", who);
+  if (L % P) return fail(SQKV_EINVAL, "%s: L=%lld not divisible by P=%d", who, (long long)L, P);
+  if (H_dst % P) return fail(SQKV_EINVAL, "%s: heads (%d) not divisible by the group size P=%d", who, H_dst, P);
+  if (H_dst % H_src) return fail(SQKV_EINVAL, "%s: H_dst=%d is not a multiple of H_src=%d", who, H_dst, H_src);
+  const int64_t bytes_src = L * H_src * (int64_t)d * elem_bytes;
+  const int64_t bytes_dst = L * H_dst * (int64_t)d * elem_bytes;
+  if (bytes_dst == 0) return ok();
+  if (!src || !dst) return fail(SQKV_EINVAL, "%s: null pointer", who);
+  if (((uintptr_t)src | (uintptr_t)dst) % elem_bytes)
+    return fail(SQKV_EUNSUPPORTED, "%s: pointers must be aligned to the element size", who);
+  if (overlap(dense_range(src, bytes_src, 1), dense_range(dst, bytes_dst, 1)))
+    return fail(SQKV_EINVAL, "%s: src and dst overlap", who);
+  if (bytes_dst / elem_bytes >= (1ll << 32) - 4096)
+    return fail(SQKV_EUNSUPPORTED, "%s: more than 2^32 elements per call", who);
+  if (L >= (1ll << 31)) return fail(SQKV_EUNSUPPORTED, "%s: L must be < 2^31", who);
+  return ok();
+}
+
+}  // namespace
+
+SQKV_EXPORT sqkv_status ulysses_seq_to_head(const void* src, void* dst, int P, int64_t L, int H_src, int H_dst,
+                                            int d, int elem_bytes, void* stream) {
+  sqkv_status st = check_permute(src, dst, P, L, H_src, H_dst, d, elem_bytes, "ulysses_seq_to_head");
+  if (st != SQKV_OK || L == 0) return st;
+  sqkv::PermuteParams p;
+  p.src = (const unsigned char*)src;
+  p.dst = (unsigned char*)dst;
+  p.L = L;
+  p.n = L / P;
+  p.P = P;
+  p.H_src = H_src;
+  p.Hl = H_dst / P;
+  p.R = H_dst / H_src;
+  p.row_bytes = (int64_t)d * elem_bytes;
+  return hip_status(sqkv::launch_seq_to_head(p, (hipStream_t)stream), "ulysses_seq_to_head launch");
+}
+
+SQKV_EXPORT sqkv_status ulysses_head_to_seq(const void* src, void* dst, int P, int64_t L, int H, int d,
+                                            int elem_bytes, void* stream) {
+  sqkv_status st = check_permute(src, dst, P, L, H, H, d, elem_bytes, "ulysses_head_to_seq");
+  if (st != SQKV_OK || L == 0) return st;
+  sqkv::PermuteParams p;
+  p.src = (const unsigned char*)src;
+  p.dst = (unsigned char*)dst;
+  p.L = L;
+  p.n = L / P;
+  p.P = P;
+  p.H_src = H;
+  p.Hl = H / P;
+  p.R = 1;
+  p.row_bytes = (int64_t)d * elem_bytes;
+  return hip_status(sqkv::launch_head_to_seq(p, (hipStream_t)stream), "ulysses_head_to_seq launch");
+}

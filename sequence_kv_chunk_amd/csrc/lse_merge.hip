@@ -1,0 +1,65 @@
+// Log-sum-exp merge of two partial attentions over disjoint key sets.
+//
+// Ring-attention Q&A (aivaro.ru answer 425), section 5: each new chunk's
+// partial is folded into the running output by rescaling both with the
+// exponent of their distance to the new running maximum.  In log-sum-exp form
+// (one fp32 lse per row, normalised outputs):
+//     lse = log(exp(lse_a) + exp(lse_b))
+//     o   = exp(lse_a - lse) * o_a + exp(lse_b - lse) * o_b
+// An empty partial (lse = -inf) contributes nothing.
+//
+// HBM-bound elementwise kernel: each thread owns four consecutive elements of
+// one row (16-byte fp32 / 8-byte bf16 accesses); the D/4 threads of a row sit
+// in the same wavefront, so in-place updates of lse (lse_out == lse_a) read
+// before they write within one wave.
+#include "attn_common.h"
+
+namespace sqkv {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int D>
+__global__ void __launch_bounds__(kThreads) lse_merge_kernel(MergeParams p) {
+  constexpr int TPR = D / 4;  // threads per row
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t t = gid / TPR;
+  const int c = (int)(gid % TPR) * 4;
+  if (t >= p.n) return;
+  const int64_t row = ((int64_t)b * p.H + h) * p.n + t;
+  float la = p.lse_a[row];
+  float lb = p.lse_b[row];
+  float wa, wb;
+  float lse = lse_merge_weights(la, lb, wa, wb);
+  float xa[4], xb[4], y[4];
+  load4(p.oa, b * p.a_sb + h * p.a_sh + t * p.a_sn + c, p.a_dtype, xa);
+  load4(p.ob, b * p.b_sb + h * p.b_sh + t * p.b_sn + c, p.b_dtype, xb);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // terms with zero weight are skipped so that an empty partial's payload
+    // (whatever it holds) cannot leak in as NaN * 0
+    float acc = 0.f;
+    if (wa != 0.f) acc = wa * xa[i];
+    if (wb != 0.f) acc = fmaf(wb, xb[i], acc);
+    y[i] = acc;
+  }
+  store4(p.oo, b * p.o_sb + h * p.o_sh + t * p.o_sn + c, p.o_dtype, y);
+  if (c == 0) p.lse_o[row] = lse;
+}
+
+}  // namespace
+
+hipError_t launch_lse_merge(const MergeParams& p, int d, hipStream_t s) {
+  if (p.n == 0 || p.B == 0 || p.H == 0) return hipSuccess;
+  int64_t threads = (int64_t)p.n * (d / 4);
+  dim3 grid((unsigned)((threads + kThreads - 1) / kThreads), (unsigned)p.H, (unsigned)p.B);
+  if (d == 128)
+    hipLaunchKernelGGL(lse_merge_kernel<128>, grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(lse_merge_kernel<64>, grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace sqkv

@@ -1,0 +1,70 @@
+// Internal declarations shared by the host layer (api.cpp) and the kernel
+// translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sqkv {
+
+enum DType : int { kF32 = 0, kBF16 = 1 };
+
+// One chunk-attention launch.  Views are [B, H, n, d] with element strides.
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  const void* o_in;  // nullptr: no running state
+  int64_t oi_sb, oi_sh, oi_sn;
+  const float* lse_in;
+  void* o_out;
+  int64_t oo_sb, oo_sh, oo_sn;
+  float* lse_out;
+  int B, Hq, Hkv, n_q, n_k;
+  int group;          // Hq / Hkv
+  int acc_dtype;      // dtype of o_in
+  int out_dtype;      // dtype of o_out
+  float scale_log2;   // scale * log2(e): logits are handled in base 2
+  int causal;
+  int64_t q_pos0, k_pos0;
+};
+
+struct MergeParams {
+  const void* oa;
+  int64_t a_sb, a_sh, a_sn;
+  const float* lse_a;
+  int a_dtype;
+  const void* ob;
+  int64_t b_sb, b_sh, b_sn;
+  const float* lse_b;
+  int b_dtype;
+  void* oo;
+  int64_t o_sb, o_sh, o_sn;
+  float* lse_o;
+  int o_dtype;
+  int B, H, n;
+};
+
+// Ulysses run copy: `units` runs of `run_bytes` bytes each.
+struct PermuteParams {
+  const unsigned char* src;
+  unsigned char* dst;
+  int64_t L;       // full sequence length
+  int64_t n;       // L / P
+  int P;
+  int H_src;       // heads in the seq-sharded layout
+  int Hl;          // heads per rank in the head-sharded layout
+  int R;           // replication factor (H_dst / H_src), 1 for head->seq
+  int64_t row_bytes;  // d * elem_bytes
+};
+
+hipError_t launch_attn_bf16(const AttnParams& p, int d, hipStream_t s);
+hipError_t launch_attn_f32(const AttnParams& p, int d, hipStream_t s);
+hipError_t launch_lse_merge(const MergeParams& p, int d, hipStream_t s);
+hipError_t launch_seq_to_head(const PermuteParams& p, hipStream_t s);
+hipError_t launch_head_to_seq(const PermuteParams& p, hipStream_t s);
+
+}  // namespace sqkv

@@ -1,0 +1,198 @@
+"""The C-ABI library loads, exports every symbol include/sqkv.h declares, and
+rejects invalid arguments on the host before any HIP call (no GPU needed).
+
+The invalid-argument cases pass fake, never-dereferenced device addresses; each
+case is built so that validation must fail, which is also asserted.  They are
+skipped on a machine with a visible GPU (the same cases run there against real
+allocations in test_gpu_validation.py)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sqkv.h")
+LIB = os.path.join(ROOT, "sequence_kv_chunk_amd", "libsqkv.so")
+
+EINVAL, EUNSUP = 1, 2
+F32, BF16 = 0, 1
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libsqkv.so is not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    for n in ("ra_chunk_attention", "ra_ring_attention", "ra_lse_merge", "ulysses_seq_to_head",
+              "ulysses_head_to_seq", "sqkv_last_error"):
+        assert n in names
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in sqkv.h but not exported"
+
+
+def test_binding_signatures_cover_header():
+    src = open(os.path.join(ROOT, "sequence_kv_chunk_amd", "api.py")).read()
+    for name in declared_functions():
+        assert f"_lib.{name}.argtypes" in src, f"binding lacks a signature for {name}"
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+no_gpu = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer validation only on GPU-less hosts")
+
+
+class View(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("sb", ctypes.c_int64), ("sh", ctypes.c_int64), ("sn", ctypes.c_int64)]
+
+
+def _setup(lib):
+    V = View
+    i, i64, f, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+    lib.ra_chunk_attention.argtypes = [V, V, V, V, vp, V, vp, i, i, i, i, i, i, i, i, i, f, i, i64, i64, vp]
+    lib.ra_ring_attention.argtypes = [V, V, V, i64, i64, V, vp, V, i, i, i, i, i, i, i, i, i, f, i, vp]
+    lib.ra_lse_merge.argtypes = [V, vp, i, V, vp, i, V, vp, i, i, i, i, i, vp]
+    lib.ulysses_seq_to_head.argtypes = [vp, vp, i, i64, i, i, i, i, vp]
+    lib.ulysses_head_to_seq.argtypes = [vp, vp, i, i64, i, i, i, vp]
+    lib.sqkv_last_error.restype = ctypes.c_char_p
+
+
+GB = 1 << 30
+
+
+def _dense(base, H, n, d):
+    return View(base, H * n * d, n * d, d)
+
+
+def _attn_args(**kw):
+    """A valid bf16 chunk-attention call on fake, disjoint addresses, overridden by kw."""
+    B, Hq, Hkv, nq, nk, d = 1, 4, 2, 64, 64, 128
+    a = dict(q=_dense(1 * GB, Hq, nq, d), k=_dense(2 * GB, Hkv, nk, d), v=_dense(3 * GB, Hkv, nk, d),
+             o_in=View(None, 0, 0, 0), lse_in=None, o_out=_dense(4 * GB, Hq, nq, d), lse_out=5 * GB,
+             B=B, Hq=Hq, Hkv=Hkv, n_q=nq, n_k=nk, d=d, in_dt=BF16, acc_dt=F32, out_dt=BF16, scale=0.5,
+             causal=0, q_pos0=0, k_pos0=0, stream=None)
+    a.update(kw)
+    return a
+
+
+def _call_attn(lib, a):
+    return lib.ra_chunk_attention(a["q"], a["k"], a["v"], a["o_in"], a["lse_in"], a["o_out"], a["lse_out"],
+                                  a["B"], a["Hq"], a["Hkv"], a["n_q"], a["n_k"], a["d"], a["in_dt"], a["acc_dt"],
+                                  a["out_dt"], a["scale"], a["causal"], a["q_pos0"], a["k_pos0"], a["stream"])
+
+
+ATTN_BAD = [
+    ("d=96", dict(d=96), EUNSUP),
+    ("Hq%Hkv", dict(Hq=6, Hkv=4), EINVAL),
+    ("scale=0", dict(scale=0.0), EINVAL),
+    ("scale<0", dict(scale=-1.0), EINVAL),
+    ("scale=inf", dict(scale=float("inf")), EINVAL),
+    ("null q", dict(q=View(None, 0, 0, 0)), EINVAL),
+    ("null lse_out", dict(lse_out=None), EINVAL),
+    ("null k", dict(k=View(None, 0, 0, 0)), EINVAL),
+    ("o_in without lse_in", dict(o_in=_dense(6 * GB, 4, 64, 128)), EINVAL),
+    ("negative size", dict(n_q=-1), EINVAL),
+    ("bad dtype", dict(in_dt=7), EUNSUP),
+    ("misaligned q ptr", dict(q=View(1 * GB + 8, 4 * 64 * 128, 64 * 128, 128)), EUNSUP),
+    ("misaligned q stride", dict(q=View(1 * GB, 4 * 64 * 130, 64 * 130, 130)), EUNSUP),
+    ("negative stride", dict(q=View(1 * GB, 0, -64 * 128, 128)), EINVAL),
+    ("o_out overlaps q", dict(o_out=_dense(1 * GB + 4096, 4, 64, 128)), EINVAL),
+    ("lse_out overlaps k", dict(lse_out=2 * GB + 64), EINVAL),
+    ("o_out partially overlaps o_in", dict(o_in=_dense(6 * GB, 4, 64, 128), lse_in=7 * GB,
+                                            o_out=_dense(6 * GB + 1024, 4, 64, 128), acc_dt=BF16), EINVAL),
+    ("in-place with dtype change", dict(o_in=_dense(6 * GB, 4, 64, 128), lse_in=7 * GB,
+                                         o_out=_dense(6 * GB, 4, 64, 128), acc_dt=F32, out_dt=BF16), EINVAL),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,want", ATTN_BAD, ids=[c[0] for c in ATTN_BAD])
+def test_chunk_attention_rejects(lib, name, kw, want):
+    _setup(lib)
+    st = _call_attn(lib, _attn_args(**kw))
+    assert st == want, f"{name}: got {st}"
+    assert lib.sqkv_last_error().decode() != ""
+
+
+@no_gpu
+def test_ring_rejects(lib):
+    _setup(lib)
+    q, k, v = _dense(1 * GB, 4, 64, 128), _dense(2 * GB, 4, 64, 128), _dense(3 * GB, 4, 64, 128)
+    o, lse, none = _dense(4 * GB, 4, 64, 128), 5 * GB, View(None, 0, 0, 0)
+    cs = 4 * 64 * 128
+
+    def call(P=4, rank=0, out_dt=BF16, work=none, causal=0, kcs=cs):
+        return lib.ra_ring_attention(q, k, v, kcs, cs, o, lse, work, 1, 4, 4, 64, 128, P, rank, BF16, out_dt,
+                                     1.0, causal, None)
+
+    assert call(rank=4) == EINVAL
+    assert call(rank=-1) == EINVAL
+    assert call(P=0) == EINVAL
+    assert call(out_dt=BF16) == EINVAL, "bf16 result over several chunks needs o_work"
+    assert call(kcs=cs + 3) == EUNSUP
+    assert call(work=_dense(4 * GB + 64, 4, 64, 128)) == EINVAL, "o_work overlapping o"
+    # the pool of 4 chunks reaches into o when o sits right after chunk 0
+    assert lib.ra_ring_attention(q, k, v, cs, cs, _dense(2 * GB + 2 * cs, 4, 64, 128), lse, none, 1, 4, 4, 64,
+                                 128, 4, 1, BF16, F32, 1.0, 0, None) == EINVAL
+
+
+@no_gpu
+def test_merge_rejects(lib):
+    _setup(lib)
+    a, b, o = _dense(1 * GB, 4, 8, 64), _dense(2 * GB, 4, 8, 64), _dense(3 * GB, 4, 8, 64)
+
+    def call(d=64, oa=a, ob=b, oo=o, la=4 * GB, lb=5 * GB, lo=6 * GB, dt=F32):
+        return lib.ra_lse_merge(oa, la, dt, ob, lb, dt, oo, lo, dt, 1, 4, 8, d, None)
+
+    assert call(d=32) == EUNSUP
+    assert call(la=None) == EINVAL
+    assert call(oo=_dense(1 * GB + 256, 4, 8, 64)) == EINVAL
+    assert call(lo=4 * GB + 4) == EINVAL
+    assert call(dt=5) == EUNSUP
+
+
+@no_gpu
+def test_ulysses_rejects(lib):
+    _setup(lib)
+    s2h, h2s = lib.ulysses_seq_to_head, lib.ulysses_head_to_seq
+    src, dst = 1 * GB, 2 * GB
+    assert s2h(src, dst, 4, 10, 8, 8, 2, 2, None) == EINVAL        # L % P
+    assert s2h(src, dst, 3, 12, 8, 8, 2, 2, None) == EINVAL        # H % P
+    assert s2h(src, dst, 8, 16, 4, 4, 2, 2, None) == EINVAL        # P > H
+    assert s2h(src, dst, 4, 16, 8, 12, 2, 2, None) == EINVAL       # H_dst % P
+    assert s2h(src, dst, 4, 16, 3, 8, 2, 2, None) == EINVAL        # H_dst % H_src
+    assert s2h(src, dst, 4, 16, 8, 8, 2, 3, None) == EINVAL        # elem_bytes
+    assert s2h(None, dst, 4, 16, 8, 8, 2, 2, None) == EINVAL
+    assert s2h(src, src + 64, 4, 16, 8, 8, 2, 2, None) == EINVAL   # overlap
+    assert s2h(src + 1, dst, 4, 16, 8, 8, 2, 2, None) == EUNSUP    # misaligned element
+    assert h2s(src, dst, 4, 10, 8, 2, 2, None) == EINVAL
+    assert h2s(src, dst, 8, 16, 4, 2, 2, None) == EINVAL
+    assert lib.sqkv_last_error().decode() != ""
+
+
+@no_gpu
+def test_empty_sizes_are_noops(lib):
+    _setup(lib)
+    # nothing to do: OK without touching memory
+    assert _call_attn(lib, _attn_args(n_q=0)) == 0
+    assert lib.ulysses_seq_to_head(1 * GB, 2 * GB, 4, 0, 8, 8, 2, 2, None) == 0
+    assert lib.sqkv_last_error().decode() == ""
