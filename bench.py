@@ -1,0 +1,266 @@
+"""Benchmark of the chunked ring-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = the whole 32k-token ring on one GPU: 8 virtual ranks, each
+attending with its 4096-row query chunk to all 8 resident key/value chunks
+(64 fused chunk-attention + LSE-merge launches, bf16 in, fp32 accumulation,
+bf16 out), B=1, 32 heads, d=128, non-causal.  Inputs are drawn on the device
+from a seeded generator and are resident in HBM before timing starts.
+
+Printed: ONE JSON line on stdout with the metric, the roofline of the
+chunk-attention kernel (MFMA-bound) and the CPU oracle timed on a bounded
+sample of the same workload.  Extra figures on the other workloads (Ulysses
+permute GB/s on 8 x [16384, 32, 128] bf16, the causal 128k rank-7 ring share,
+the causal 128k GQA Ulysses share) go in "extras".  Logs go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
+METRIC = "chunked-attention TFLOP/s (% bf16 MFMA peak); Ulysses permute GB/s (% HBM)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_ring32k_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "sequence_kv_chunk_amd", "csrc", "attn_bf16.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    passes, if they were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_ring(api, torch, w, x, steps, warmup):
+    """Times `steps` ring passes over all query ranks; returns (ms_per_step, launches/step)."""
+    P = w.P
+    qs, kp, vp = x["q"], x["k"], x["v"]
+    B, H, n, d = qs.shape[1:]
+    o = torch.empty((B, H, n, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B * H * n, dtype=torch.float32, device="cuda")
+    work = torch.empty((B, H, n, d), dtype=torch.float32, device="cuda")
+    ranks = w.query_ranks
+
+    def step():
+        for idx, i in enumerate(ranks):
+            api.ra_ring_attention(qs[idx], kp, vp, o, lse, rank=i, o_work=work, scale=1.0, causal=w.causal)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    gpu = ev0.elapsed_time(ev1) / steps
+    launches = sum(1 for i in ranks for j in range(P) if not w.causal or j <= i)
+    return wall, gpu, launches
+
+
+def bench_ulysses(api, torch, iters=10):
+    from sequence_kv_chunk_amd.synth import ULYSSES_WORKLOADS, device_ulysses_input
+    w = ULYSSES_WORKLOADS["ulysses_131k_32h"]
+    src = device_ulysses_input(w)
+    mid = torch.empty((w.P, w.L, w.H // w.P, w.d), dtype=torch.bfloat16, device="cuda")
+    back = torch.empty_like(src)
+    flush = torch.empty(768 << 20, dtype=torch.uint8, device="cuda")   # > 256 MiB MALL
+    res = {}
+    for name, fn in (("seq_to_head", lambda: api.ulysses_seq_to_head(src, mid)),
+                     ("head_to_seq", lambda: api.ulysses_head_to_seq(mid, back))):
+        fn()
+        ts = []
+        for _ in range(iters):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        med = ts[len(ts) // 2]
+        gbs = w.bytes_per_direction() / (med * 1e-3) / 1e9
+        res[name] = {"ms_median": round(med, 4), "ms_min": round(ts[0], 4), "GB/s": round(gbs, 1),
+                     "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    torch.cuda.synchronize()
+    ok = bool(torch.equal(back.view(torch.int16), src.view(torch.int16)))
+    res["round_trip_bit_exact"] = ok
+    res["workload"] = "ulysses_131k_32h: 8 shards [16384, 32, 128] bf16 <-> [131072, 4, 128]"
+    res["bytes_per_direction"] = w.bytes_per_direction()
+    return res
+
+
+def bench_attention_extra(api, torch, name, steps=3):
+    from sequence_kv_chunk_amd.synth import WORKLOADS, device_attention_inputs
+    w = WORKLOADS[name]
+    x = device_attention_inputs(w)
+    if w.layout == "shd":
+        o = torch.empty((w.L, w.Hq, w.d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(w.Hq * w.L, dtype=torch.float32, device="cuda")
+        fn = lambda: api.ra_chunk_attention(x["q"], x["k"], x["v"], o, lse, scale=1.0, causal=w.causal)
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+    else:
+        _, ms, _ = time_ring(api, torch, w, x, steps, 1)
+    tf = w.flops() / (ms * 1e-3) / 1e12
+    del x
+    torch.cuda.empty_cache()
+    return {"ms": round(ms, 3), "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4),
+            "flops": w.flops()}
+
+
+def cpu_baseline(x_dev, w, torch, budget_rows=4096, heads=4):
+    """The fp64 oracle on a bounded sample of the workload: query chunk 0
+    (4096 rows) of the first `heads` heads against all 32768 keys."""
+    import oracle
+    from sequence_kv_chunk_amd.synth import bf16_bits_to_f64
+
+    def bits(t):
+        return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    q = bf16_bits_to_f64(bits(x_dev["q"][0][:, :heads, :budget_rows]))          # [B, h, rows, d]
+    kp = bf16_bits_to_f64(bits(x_dev["k"][:, :, :heads]))                          # [P, B, h, n, d]
+    vp = bf16_bits_to_f64(bits(x_dev["v"][:, :, :heads]))
+    P, B, h, n, d = kp.shape
+    k = kp.transpose(1, 2, 0, 3, 4).reshape(B, h, P * n, d)
+    v = vp.transpose(1, 2, 0, 3, 4).reshape(B, h, P * n, d)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    oracle.attention_fp64(q, k, v, scale=1.0, causal=False)
+    dt = time.perf_counter() - t0
+    flops = 4 * d * (P * n) * budget_rows * heads * B
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"query rows 0..{budget_rows - 1} (chunk 0) of heads 0..{heads - 1} against all "
+                      f"{P * n} keys, fp64 numpy oracle, {dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-extras", action="store_true", help="skip the other workloads' figures")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU (the ring's P chunks are resident in one HBM "
+              "pool); --gpus N with N > 1 is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sequence_kv_chunk_amd import api
+    from sequence_kv_chunk_amd.synth import WORKLOADS, device_attention_inputs
+
+    w = WORKLOADS["ring_bf16_32k"]
+    x = device_attention_inputs(w)
+    torch.cuda.synchronize()
+    log(f"workload {w.name}: inputs resident ({sum(t.numel() * 2 for t in x.values()) / 2**30:.2f} GiB)")
+
+    if args.calibrate_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    wall_ms, gpu_ms, launches = time_ring(api, torch, w, x, args.steps, args.warmup)
+    flops = w.flops()
+    value = flops / (wall_ms * 1e-3) / 1e12
+    per_launch_flops = flops // launches
+    launch_ms = gpu_ms / launches      # the timed region holds only chunk-attention launches
+    achieved = per_launch_flops / (launch_ms * 1e-3) / 1e12
+    traffic = load_traffic()
+    log(f"ring step {wall_ms:.3f} ms (events {gpu_ms:.3f} ms), {value:.1f} TFLOP/s, "
+        f"{launches} launches of {launch_ms:.4f} ms")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) on device; Q scaled by d^-0.5)",
+        "config": {"workload": "ring_bf16_32k: 32768 tokens as 8 chunks of 4096, all 8 query chunks x 8 "
+                               "resident KV chunks, B=1, 32 heads, d=128, non-causal",
+                   "global_batch": 1, "seq_len": w.L, "heads": w.Hq, "head_dim": w.d, "chunks": w.P,
+                   "parallelism": "single GPU; 8 virtual ranks"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "attn_bf16_kernel<128>", "flops_per_launch": per_launch_flops,
+                     "launch_ms": round(launch_ms, 4)},
+    }
+    extras = {}
+    if not args.no_extras:
+        try:
+            extras["ulysses"] = bench_ulysses(api, torch)
+            log(f"ulysses: {extras['ulysses']}")
+            extras["ring_bf16_128k_rank7_causal"] = bench_attention_extra(api, torch, "ring_bf16_128k_rank7_causal")
+            log(f"rank7 causal: {extras['ring_bf16_128k_rank7_causal']}")
+            extras["ulysses_share_gqa_128k_causal"] = bench_attention_extra(api, torch,
+                                                                            "ulysses_share_gqa_128k_causal")
+            log(f"ulysses share: {extras['ulysses_share_gqa_128k_causal']}")
+        except Exception as e:  # extras never hide the main line
+            extras["error"] = repr(e)
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(x, w, torch)
+        log(f"cpu baseline: {result['cpu_baseline']}")
+    else:
+        result["cpu_baseline"] = None
+    if extras:
+        result["extras"] = extras
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -243,3 +243,33 @@ def tag_pattern_u32(shape) -> np.ndarray:
     """uint32 array holding each element's flat index (unique below 2**32)."""
     size = int(np.prod(shape))
     return np.arange(size, dtype=np.uint32).reshape(shape)
+
+
+def device_attention_inputs(w: AttnWorkload, device="cuda"):
+    """Q, K, V of workload ``w`` drawn directly on the GPU from torch's seeded
+    generator (same shapes and distributions as ``attention_inputs``; used for
+    timing at full size, where drawing on the host would dominate)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    d = w.d
+    if w.layout == "shd":
+        qs, ks = (w.L, w.Hq, d), (w.L, w.Hkv, d)
+    else:
+        qs = (len(w.query_ranks), w.B, w.Hq, w.n, d)
+        ks = (w.P, w.B, w.Hkv, w.n, d)
+    q = torch.randn(qs, generator=g, device=device, dtype=torch.float32)
+    if w.q_scaled:
+        q *= 1.0 / math.sqrt(d)
+    q = q.to(dt)
+    k = torch.randn(ks, generator=g, device=device, dtype=torch.float32).to(dt)
+    v = torch.randn(ks, generator=g, device=device, dtype=torch.float32).to(dt)
+    return {"q": q, "k": k, "v": v}
+
+
+def device_ulysses_input(w: UlyssesWorkload, device="cuda"):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed)
+    return torch.randn((w.P, w.n, w.H, w.d), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
