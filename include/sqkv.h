@@ -87,7 +87,10 @@ typedef struct sqkv_view {
  * Supported: d in {64, 128}; in_dtype F32 (fp32 arithmetic throughout) or
  * BF16 (bf16 MFMA products, fp32 accumulation, softmax weights rounded to
  * bf16 for the P*V product); acc_dtype, out_dtype F32 or BF16.  Pointers must
- * be 16-byte aligned and every stride a multiple of 16 bytes.
+ * be 16-byte aligned, every stride a multiple of 16 bytes and key/value row
+ * strides below 16 MiB.  Keys a query cannot see (masked, or past the chunk)
+ * still pass through the P*V product with weight 0, so K and V must be
+ * finite.
  * Returns SQKV_OK, SQKV_EINVAL (null pointer, Hq % Hkv != 0, negative size,
  * scale not finite and > 0, overlap), SQKV_EUNSUPPORTED (d, dtype,
  * alignment) or SQKV_EHIP.
@@ -107,27 +110,27 @@ sqkv_status ra_chunk_attention(sqkv_view q, sqkv_view k, sqkv_view v,
  * positions j*n .. j*n + n - 1); the rank holding query chunk `rank` meets
  * every key/value chunk once, its own first and then, at step s, the chunk
  * that arrived from the previous device, j = (rank - s) mod P.  The send and
- * receive of the pages become reading chunk j in place.
+ * receive of the pages become reading chunk j in place, and [RA] section 5's
+ * per-step merge is the online-softmax rescale of one running (max, sum,
+ * output) state that a single launch carries across the chunks.
  *
- *   q        [B, Hq, n, d]  in_dtype      the rank's query chunk
+ *   q        [B, Hq, n, d]  in_dtype      the rank's query chunk (positions
+ *                                         rank*n ..)
  *   k, v     [B, Hkv, n, d] in_dtype      chunk 0 of the pool; chunk j starts
  *                                         j*k_chunk_stride (v_chunk_stride)
  *                                         elements after it
  *   o        [B, Hq, n, d]  out_dtype     result
- *   lse      [B, Hq, n]     float32       result
- *   o_work   [B, Hq, n, d]  float32       accumulator used between steps when
- *                                         out_dtype is BF16 and more than one
- *                                         chunk is visited; else may be NULL
+ *   lse      [B, Hq, n]     float32       result (natural log)
  *
  * With causal != 0, chunks after the rank's own (j > rank) are skipped,
  * earlier ones are fully visible and the rank's own chunk is masked on its
- * diagonal.  Each visited chunk is one ra_chunk_attention launch merging in
- * fp32; the last one writes o in out_dtype.  Same support and status codes as
- * ra_chunk_attention; additionally EINVAL for rank outside [0, P) or P < 1.
+ * diagonal.  Same support and status codes as ra_chunk_attention;
+ * additionally EINVAL for rank outside [0, P) or P < 1, EUNSUPPORTED for
+ * chunk strides that are not multiples of 16 bytes.
  */
 sqkv_status ra_ring_attention(sqkv_view q, sqkv_view k, sqkv_view v,
                               int64_t k_chunk_stride, int64_t v_chunk_stride,
-                              sqkv_view o, float* lse, sqkv_view o_work,
+                              sqkv_view o, float* lse,
                               int B, int Hq, int Hkv, int n, int d, int P, int rank,
                               sqkv_dtype in_dtype, sqkv_dtype out_dtype,
                               float scale, int causal, void* stream);

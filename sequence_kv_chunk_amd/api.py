@@ -48,7 +48,7 @@ _lib.ra_chunk_attention.restype = _c_int
 _lib.ra_chunk_attention.argtypes = [_V, _V, _V, _V, _vp, _V, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _c_i64, _c_i64, _vp]
 _lib.ra_ring_attention.restype = _c_int
-_lib.ra_ring_attention.argtypes = [_V, _V, _V, _c_i64, _c_i64, _V, _vp, _V, _c_int, _c_int, _c_int, _c_int,
+_lib.ra_ring_attention.argtypes = [_V, _V, _V, _c_i64, _c_i64, _V, _vp, _c_int, _c_int, _c_int, _c_int,
                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _vp]
 _lib.ra_lse_merge.restype = _c_int
 _lib.ra_lse_merge.argtypes = [_V, _vp, _c_int, _V, _vp, _c_int, _V, _vp, _c_int, _c_int, _c_int, _c_int,
@@ -137,22 +137,19 @@ def ra_chunk_attention(q, k, v, o_out, lse_out, *, o_in=None, lse_in=None, scale
     _check(st)
 
 
-def ra_ring_attention(q, k_pool, v_pool, o, lse, *, rank: int, o_work=None, scale: float = 1.0,
-                      causal: bool = False):
+def ra_ring_attention(q, k_pool, v_pool, o, lse, *, rank: int, scale: float = 1.0, causal: bool = False):
     """Ring attention of query chunk ``q`` ([B, Hq, n, d]) of virtual rank ``rank``
     over the P resident chunks of ``k_pool``/``v_pool`` ([P, B, Hkv, n, d])."""
     if k_pool.dim() != 5 or v_pool.shape != k_pool.shape:
         raise SqkvError(SQKV_EINVAL, "k_pool, v_pool must be [P, B, Hkv, n, d]")
-    _same_device(q, k_pool, v_pool, o, lse, o_work)
+    _same_device(q, k_pool, v_pool, o, lse)
     P = k_pool.shape[0]
     B, Hq, n, d = q.shape
     if tuple(o.shape) != (B, Hq, n, d) or k_pool.shape[3] != n or k_pool.shape[1] != B:
         raise SqkvError(SQKV_EINVAL, "shapes disagree")
-    if o_work is not None and (o_work.dtype != torch.float32 or tuple(o_work.shape) != (B, Hq, n, d)):
-        raise SqkvError(SQKV_EINVAL, "o_work must be float32 [B, Hq, n, d]")
     with torch.cuda.device(q.device):
         st = _lib.ra_ring_attention(_view(q), _view(k_pool[0]), _view(v_pool[0]), k_pool.stride(0),
-                                    v_pool.stride(0), _view(o), _lse_ptr(lse, B * Hq * n), _view(o_work),
+                                    v_pool.stride(0), _view(o), _lse_ptr(lse, B * Hq * n),
                                     B, Hq, k_pool.shape[2], n, d, P, int(rank), _dtype_code(q),
                                     _dtype_code(o), float(scale), int(bool(causal)), _stream(q))
     _check(st)

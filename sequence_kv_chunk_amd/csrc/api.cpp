@@ -9,7 +9,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
-#include <vector>
 
 #include "../../include/sqkv.h"
 #include "sqkv_internal.h"
@@ -123,6 +122,9 @@ sqkv_status check_attention(const AttnCheck& a) {
     return fail(SQKV_EUNSUPPORTED, "output pointers and strides must be 16-byte aligned");
   if (((uintptr_t)a.lse_out) % 4 || ((uintptr_t)a.lse_in) % 4)
     return fail(SQKV_EUNSUPPORTED, "lse must be 4-byte aligned");
+  // the bf16 kernel addresses a key/value tile through a 32-bit byte range
+  if (a.k.sn * ieb >= (1ll << 24) || a.v.sn * ieb >= (1ll << 24))
+    return fail(SQKV_EUNSUPPORTED, "key/value row strides must be below 16 MiB");
   // aliasing: outputs may only coincide exactly with the running state
   const int64_t rows = (int64_t)a.B * a.Hq * a.n_q;
   Range ro = view_range(a.o_out, a.B, a.Hq, a.n_q, a.d, dtype_bytes(a.out_dt));
@@ -168,6 +170,12 @@ sqkv::AttnParams make_params(const sqkv_view& q, const sqkv_view& k, const sqkv_
   p.causal = causal ? 1 : 0;
   p.q_pos0 = q_pos0;
   p.k_pos0 = k_pos0;
+  // a single chunk; ra_ring_attention widens this to the ring visit
+  p.k_cs = p.v_cs = 0;
+  p.k_posstride = 0;
+  p.nseg = 1;
+  p.P = 1;
+  p.rank = 0;
   return p;
 }
 
@@ -194,56 +202,32 @@ SQKV_EXPORT sqkv_status ra_chunk_attention(sqkv_view q, sqkv_view k, sqkv_view v
 }
 
 SQKV_EXPORT sqkv_status ra_ring_attention(sqkv_view q, sqkv_view k, sqkv_view v, int64_t k_chunk_stride,
-                                          int64_t v_chunk_stride, sqkv_view o, float* lse, sqkv_view o_work,
-                                          int B, int Hq, int Hkv, int n, int d, int P, int rank,
-                                          sqkv_dtype in_dtype, sqkv_dtype out_dtype, float scale, int causal,
-                                          void* stream) {
+                                          int64_t v_chunk_stride, sqkv_view o, float* lse, int B, int Hq,
+                                          int Hkv, int n, int d, int P, int rank, sqkv_dtype in_dtype,
+                                          sqkv_dtype out_dtype, float scale, int causal, void* stream) {
   if (P < 1 || rank < 0 || rank >= P) return fail(SQKV_EINVAL, "need P >= 1 and 0 <= rank < P (P=%d rank=%d)", P, rank);
   if (k_chunk_stride < 0 || v_chunk_stride < 0) return fail(SQKV_EINVAL, "negative chunk stride");
   const int ieb = dtype_bytes(in_dtype);
   if ((k_chunk_stride * ieb) % 16 || (v_chunk_stride * ieb) % 16)
     return fail(SQKV_EUNSUPPORTED, "chunk strides must be multiples of 16 bytes");
-  // chunks visited, own chunk first, then the one arriving from the previous rank
-  std::vector<int> visit;
-  for (int s = 0; s < P; ++s) {
-    int j = ((rank - s) % P + P) % P;
-    if (causal && j > rank) continue;  // entirely in the future of every query
-    visit.push_back(j);
-  }
-  const bool direct = out_dtype == SQKV_F32 || visit.size() == 1;
-  sqkv_view acc = (out_dtype == SQKV_F32) ? o : o_work;
   AttnCheck a{q, k, v, sqkv_view{nullptr, 0, 0, 0}, o, nullptr, lse, B, Hq, Hkv, n, n,
               (int64_t)(P - 1) * std::max(k_chunk_stride, v_chunk_stride) * ieb, d,
               in_dtype, SQKV_F32, out_dtype, scale};
   sqkv_status st = check_attention(a);
   if (st != SQKV_OK || n == 0) return st;
-  if (!direct) {
-    if (!o_work.ptr) return fail(SQKV_EINVAL, "o_work (fp32) is required for a bf16 result over several chunks");
-    AttnCheck w = a;
-    w.o_out = o_work;
-    w.out_dt = SQKV_F32;
-    st = check_attention(w);
-    if (st != SQKV_OK) return st;
-    Range rw = view_range(o_work, B, Hq, n, d, 4);
-    if (overlap(rw, view_range(o, B, Hq, n, d, dtype_bytes(out_dtype))))
-      return fail(SQKV_EINVAL, "o_work overlaps o");
-  }
-  hipStream_t s = (hipStream_t)stream;
-  for (size_t i = 0; i < visit.size(); ++i) {
-    const int j = visit[i];
-    const bool first = i == 0, last = i + 1 == visit.size();
-    sqkv_view kj = k, vj = v;
-    kj.ptr = (char*)k.ptr + (int64_t)j * k_chunk_stride * ieb;
-    vj.ptr = (char*)v.ptr + (int64_t)j * v_chunk_stride * ieb;
-    sqkv_view in = first ? sqkv_view{nullptr, 0, 0, 0} : acc;
-    sqkv_view out = last ? o : acc;
-    const int out_dt = last ? out_dtype : SQKV_F32;
-    sqkv::AttnParams p = make_params(q, kj, vj, in, first ? nullptr : lse, out, lse, B, Hq, Hkv, n, n,
-                                     SQKV_F32, out_dt, scale, causal, (int64_t)rank * n, (int64_t)j * n);
-    hipError_t e = launch_attention(p, d, in_dtype, s);
-    if (e != hipSuccess) return hip_status(e, "ra_ring_attention launch");
-  }
-  return ok();
+  // One launch visits the chunks in ring order, the rank's own first, then the
+  // one arriving from the previous rank: j = (rank - s) mod P.  With a causal
+  // mask the chunks after the rank's own (j > rank) are entirely in the future
+  // of its queries, so the visit stops after chunk 0 (s = rank).
+  sqkv::AttnParams p = make_params(q, k, v, sqkv_view{nullptr, 0, 0, 0}, nullptr, o, lse, B, Hq, Hkv, n, n,
+                                   SQKV_F32, out_dtype, scale, causal, (int64_t)rank * n, 0);
+  p.k_cs = k_chunk_stride;
+  p.v_cs = v_chunk_stride;
+  p.k_posstride = n;
+  p.P = P;
+  p.rank = rank;
+  p.nseg = causal ? rank + 1 : P;
+  return hip_status(launch_attention(p, d, in_dtype, (hipStream_t)stream), "ra_ring_attention launch");
 }
 
 SQKV_EXPORT sqkv_status ra_lse_merge(sqkv_view o_a, const float* lse_a, sqkv_dtype a_dtype, sqkv_view o_b,

@@ -1,34 +1,55 @@
 // Chunk attention with bf16 inputs on gfx950 matrix cores.
 //
 // Ring-attention Q&A (aivaro.ru answer 425), section 5: for a query chunk and
-// one resident key/value chunk compute the scores Q K^T, the row maximum, the
-// exponentials, the row sum and P V; merge the chunk's partial into the
-// running output with an online-softmax rescale.
+// each resident key/value chunk compute the scores Q K^T, the row maximum, the
+// exponentials, the row sum and P V, and fold every chunk into the running
+// output with the online-softmax rescale.  Sections 2-3: the chunks are met in
+// ring order, the rank's own chunk first.  One launch walks all the chunks a
+// query block has to see (one chunk for a single ring step), so the running
+// (max, sum, output) state stays in registers across chunk boundaries.
 //
 // Design (gfx950, wave64, v_mfma_f32_32x32x16_bf16):
 // * A workgroup of 4 wavefronts owns 256 query rows of one (batch, head); each
-//   wavefront owns 64 rows (two 32-column MFMA blocks) and keeps its Q
-//   fragments in registers for the whole key loop.
-// * The scores are computed transposed, S^T = K Q^T (keys on the MFMA M axis,
+//   wavefront owns 64 rows and keeps their Q fragments in registers.  Keys
+//   are processed in tiles of 32, which keeps a tile's scores in 32 registers
+//   per lane so that two tiles can be in flight at once.
+// * Scores are computed transposed, S^T = K Q^T (keys on the MFMA M axis,
 //   queries on N).  In the 32x32 accumulator layout a lane then holds 16 keys
-//   of ONE query column, so the row max and row sum are in-lane reductions plus
-//   one exchange with the lane 32 apart -- no cross-lane reduction trees.
-// * The same accumulator registers, rounded to bf16, are directly the B
-//   operand of O^T = V^T P^T: the key order inside each 16-key contraction
-//   step is taken from the accumulator layout, and V^T is read from LDS in
-//   that same order.
-// * K tiles (64 keys x d) sit in LDS row-major with a 16-byte row pad; V tiles
-//   are transposed into LDS (V^T, d rows of 64 keys) with an XOR swizzle of
-//   8-byte key groups so that both the transposing writes and the fragment
-//   reads avoid bank conflicts.  Both are double-buffered: the global loads of
-//   tile t+1 are in flight while tile t is computed.
+//   of ONE query, so the row max and row sum are in-lane reductions plus one
+//   v_permlane32_swap with the lane 32 apart.
+// * Those accumulators, rounded to bf16, are directly the B operand of
+//   O^T = V^T P^T; the key order inside a 16-key contraction step follows the
+//   accumulator layout and the V^T operand is read in that order with
+//   ds_read_b64_tr_b16 (a 4x16 block of V rows transposed across 16 lanes),
+//   so V is stored in LDS exactly as it sits in memory.
+// * K and V tiles (64 keys x d) are copied global -> LDS by buffer_load ...
+//   lds (16 bytes per lane, no register staging); rows past the end of a
+//   chunk fall outside the buffer's range and arrive as zeros.  16-byte chunks
+//   of a row are XOR-swizzled so that the K fragment reads (ds_read_b128) and
+//   the V transpose reads hit distinct banks.
+// * Software pipeline, per wavefront and iteration t:
+//       S(t+2) = K(t+2) Q^T      (MFMA)
+//       O     += V(t)^T P(t)^T   (MFMA)
+//       softmax of S(t+1)        (VALU / transcendental, overlaps the MFMAs)
+//   The three streams are interleaved by hand, two MFMAs at a time with a
+//   slice of the softmax between them, and fenced with sched_barrier so the
+//   compiler keeps that order.  K and V tiles go through four LDS stages each
+//   and are fetched three iterations before use.  The loop is unrolled by four
+//   so that every stage address is an instruction immediate.  The DMA loads are inline assembly,
+//   their completion counted with explicit s_waitcnt vmcnt, because the
+//   compiler would otherwise wait for every in-flight LDS DMA before each LDS
+//   read.  The tile count is padded to 4k+1 with empty tiles (fully masked,
+//   zero-filled), which contribute nothing.
 // * Softmax runs in base 2 with scale*log2(e) folded into one FMA.  The
-//   running maximum is only moved (and the accumulator rescaled) when a tile
-//   raises it by more than kRescaleLog2; in between, weights are taken against
-//   the slightly stale maximum, which leaves the normalised result unchanged
-//   and bounds weights by 2^kRescaleLog2.
-// * Causal masking is applied only on tiles that straddle the diagonal or the
-//   ragged end of the chunk; tiles entirely above the diagonal are skipped.
+//   running maximum is only moved (and O rescaled) when a tile raises it by
+//   more than kRescaleLog2; weights are taken against the slightly stale
+//   maximum in between, which leaves the normalised result unchanged and
+//   bounds weights by 2^kRescaleLog2.
+// * Masks (causal diagonal, ragged chunk end) are applied only to tiles that
+//   need them; tiles entirely in the future of the whole block are never
+//   fetched.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace sqkv {
@@ -39,55 +60,165 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+#define SQKV_LDS __attribute__((address_space(3)))
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQW = 64;              // query rows per wavefront
 constexpr int kBM = kQW * kWaves;    // query rows per workgroup
-constexpr int kBN = 64;              // keys per tile
+constexpr int kBN = 32;              // keys per tile (one 32-row MFMA block)
+constexpr int kStages = 4;           // LDS stages per tensor (= loop unroll)
 constexpr float kRescaleLog2 = 8.0f;
 
 template <int D>
 struct Cfg {
-  static constexpr int KC = D / 16;           // 16-wide contraction steps over d
-  static constexpr int MD = D / 32;           // 32-row blocks of d in O^T
-  static constexpr int KPITCH = D + 8;        // bf16 per K row in LDS
-  static constexpr int K_STAGE = kBN * KPITCH;
-  static constexpr int VT_STAGE = D * kBN;
-  static constexpr int VPR = D / 8;           // 16-byte vectors per row
-  static constexpr int KPT = D / 32;          // rows (keys) loaded per thread
-  static constexpr int LDS_BYTES = 2 * (K_STAGE + VT_STAGE) * 2;
+  static constexpr int KC = D / 16;                      // 16-wide contraction steps over d
+  static constexpr int MD = D / 32;                      // 32-row blocks of d in O^T
+  static constexpr int NCH = D / 8;                      // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;                     // bytes per row
+  static constexpr int TILE = kBN * ROWB;                // bytes per K or V tile
+  static constexpr int RPW = 1024 / ROWB;                // rows per wave-wide 1 KiB load
+  static constexpr int NL = TILE / (1024 * kWaves);      // loads per thread per tile
+  static constexpr int K_LDS = 0;                        // kStages K tiles
+  static constexpr int V_LDS = kStages * TILE;           // kStages V tiles
+  static constexpr int LDS_BYTES = 2 * kStages * TILE;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-// V^T tile: row d holds 64 keys as 16 groups of 4; group g of row d is stored
-// at group position g ^ (d & 15) ^ ((d >> 4) & 7).
-__device__ __forceinline__ int vt_index(int d, int key) {
-  int g = (key >> 2) ^ (d & 15) ^ ((d >> 4) & 7);
-  return d * kBN + g * 4 + (key & 3);
+// Position of 16-byte chunk c of tile row r: c ^ swizzle(r).
+template <int D>
+__device__ __forceinline__ int swz_k(int r) { return r & (Cfg<D>::NCH - 1); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  // rows r..r+3 of a transpose read touch chunk pairs {c, c+1}: these four
+  // masks send the 8 (or 16, for four consecutive chunks) reads to distinct
+  // bank groups
+  const int f = (r & 3) == 0 ? 0 : (r & 3) == 1 ? 6 : (r & 3) == 2 ? 12 : 10;
+  return f & (Cfg<D>::NCH - 1);
 }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2_t v = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Max / sum with the lane 32 apart (the other half of a query's keys):
+// v_permlane32_swap of x with itself yields both halves in every lane.
+__device__ __forceinline__ float max_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Keeps a value's computation where it is written: the compiler may not sink
+// it past this point (e.g. into the next loop iteration), which would undo
+// the hand interleaving of VALU work with the MFMAs.
+template <typename T>
+__device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
+
+__device__ __forceinline__ u32x4_t lds_b128(uint32_t addr) {
+  return *reinterpret_cast<SQKV_LDS const u32x4_t*>((size_t)addr);
+}
+
+__device__ __forceinline__ i16x4_t lds_tr16(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<SQKV_LDS i16x4_t*>((size_t)addr));
+}
+
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = (int)(uint32_t)b;
+  r[1] = (int)(uint32_t)(b >> 32);   // stride 0: a raw byte range
+  r[2] = (int)bytes;                 // num_records: bytes past this read as 0
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from the buffer at `voff` into LDS at m0 + 16 * lane.
+__device__ __forceinline__ void dma16(uint32_t voff, i32x4_t rsrc, uint32_t lds) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
+}
+
+// s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8).
+constexpr unsigned waitcnt_imm(int vm, int lgkm) {
+  return (unsigned)((vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8));
+}
+constexpr unsigned kWaitVm0 = waitcnt_imm(0, 15);
+constexpr unsigned kWaitLgkm0 = waitcnt_imm(63, 0);
+
+// Meet the other wavefronts once every LDS read of this wave has returned:
+// after it, LDS that all waves have finished reading may be overwritten.
+__device__ __forceinline__ void lds_reads_done_sync() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// As above, and first wait until at most N of this wave's vector-memory
+// operations are in flight: every DMA issued before the last N has landed,
+// so after the barrier it is visible in LDS to the whole workgroup.
+template <int N>
+__device__ __forceinline__ void wait_dma_and_sync() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(N, 0));
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// One 64-key tile of the visit: chunk j, tile tt inside it, nvalid keys
+// (0 for "past the end").
+struct Tile {
+  int j, tt, nvalid;
+};
+
+// Walks the tiles a workgroup visits: chunks in ring order, and in each chunk
+// the tiles holding keys visible to at least one of its query rows.  Only the
+// first chunk (the rank's own, or the single chunk of one ring step) can be
+// cut short by the causal mask; every later chunk of a ring lies entirely in
+// the past of the rank's queries and is visited whole.  next() is branch-free
+// scalar code so that it can sit inside the pipelined loop.
+struct TileWalk {
+  int s, tt, ntl, lim;       // current chunk of the visit, tile in it, its tiles / keys
+  int ntl_full, n_k, nseg, rank, P;
+
+  __device__ Tile next() {
+    tt += 1;
+    const bool wrap = tt >= ntl;
+    s += wrap ? 1 : 0;
+    tt = wrap ? 0 : tt;
+    ntl = wrap ? ntl_full : ntl;
+    lim = wrap ? n_k : lim;
+    int j = rank - s;
+    j = j < 0 ? j + P : j;
+    const int nv = s < nseg ? min(kBN, lim - tt * kBN) : 0;
+    return Tile{j, tt, nv};
+  }
+};
+
+template <int R>
+using Step = std::integral_constant<int, R>;
+
 template <int D>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_bf16_kernel(AttnParams p, int n_qtiles) {
   using C = Cfg<D>;
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t* k_lds = smem;                       // 2 stages
-  uint16_t* vt_lds = smem + 2 * C::K_STAGE;     // 2 stages
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  // LDS offset of the dynamic allocation (no static LDS in this kernel)
+  const uint32_t lds0 = (uint32_t)(size_t)(SQKV_LDS unsigned char*)smem;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  const int a16 = lane & 15;
 
   // Workgroup -> (b, h, q-tile).  Heads vary fastest so that consecutive
   // workgroups (spread round-robin over the XCDs) cover all heads; with a
@@ -104,217 +235,309 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   const int qw0 = q0 + wave * kQW;         // first row of this wavefront
 
   const uint16_t* qg = static_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh;
-  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + b * p.k_sb + hk * p.k_sh;
-  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + b * p.v_sb + hk * p.v_sh;
+  const unsigned char* kg = reinterpret_cast<const unsigned char*>(
+      static_cast<const uint16_t*>(p.k) + b * p.k_sb + hk * p.k_sh);
+  const unsigned char* vg = reinterpret_cast<const unsigned char*>(
+      static_cast<const uint16_t*>(p.v) + b * p.v_sb + hk * p.v_sh);
+  const int k_snb = (int)(p.k_sn * 2), v_snb = (int)(p.v_sn * 2);   // row strides in bytes
+  const int64_t k_csb = p.k_cs * 2, v_csb = p.v_cs * 2;             // chunk strides in bytes
 
   // ---- Q fragments (B operand of S^T = K Q^T) -------------------------------
   // lane holds Q[row = qw0 + 32*nb + l32][16*kc + 8*hi .. +7]
   u32x4_t qf[2][C::KC];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    int row = qw0 + 32 * nb + l32;
-    bool ok = row < p.n_q;
+    const int row = qw0 + 32 * nb + l32;
+    const bool ok = row < p.n_q;
     const uint16_t* src = qg + (int64_t)(ok ? row : 0) * p.q_sn + 8 * hi;
 #pragma unroll
     for (int kc = 0; kc < C::KC; ++kc) {
-      u32x4_t z = {0u, 0u, 0u, 0u};
+      const u32x4_t z = {0u, 0u, 0u, 0u};
       qf[nb][kc] = ok ? *reinterpret_cast<const u32x4_t*>(src + 16 * kc) : z;
     }
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // Q is in registers before any DMA is counted
 
-  // ---- key range -------------------------------------------------------------
-  int64_t n_keys = p.n_k;
-  const int q_last_wg = min(q0 + kBM, p.n_q) - 1;
-  if (p.causal) {
-    int64_t lim = p.q_pos0 + q_last_wg - p.k_pos0 + 1;
-    n_keys = max((int64_t)0, min(n_keys, lim));
-  }
-  const int ntiles = (int)((n_keys + kBN - 1) / kBN);
-  const int q_last_w = min(qw0 + kQW, p.n_q) - 1;   // last valid row of the wave
-  const bool wave_active = qw0 < p.n_q;
-
-  // ---- global -> register -> LDS staging -------------------------------------
-  // thread owns rows kq*KPT .. kq*KPT+KPT-1 and the 8 columns 8*dg .. 8*dg+7
-  const int dg = tid % C::VPR;
-  const int kq = tid / C::VPR;
-  u32x4_t kreg[C::KPT], vreg[C::KPT];
-
-  auto load_tile = [&](int t) {
+  // ---- per-lane LDS offsets ---------------------------------------------------
+  // K fragment (A operand of S^T): row 32*mb + l32, 16-byte chunk 2*kc + hi
+  uint32_t kofs[C::KC];
 #pragma unroll
-    for (int r = 0; r < C::KPT; ++r) {
-      int64_t u = (int64_t)t * kBN + kq * C::KPT + r;
-      u32x4_t z = {0u, 0u, 0u, 0u};
-      bool ok = u < n_keys;
-      int64_t uu = ok ? u : 0;
-      kreg[r] = ok ? *reinterpret_cast<const u32x4_t*>(kg + uu * p.k_sn + 8 * dg) : z;
-      vreg[r] = ok ? *reinterpret_cast<const u32x4_t*>(vg + uu * p.v_sn + 8 * dg) : z;
+  for (int kc = 0; kc < C::KC; ++kc)
+    kofs[kc] = lds0 + C::K_LDS + l32 * C::ROWB + (((2 * kc + hi) ^ swz_k<D>(l32)) * 16);
+  // V^T fragment via transpose reads: the 16-lane group g = lane/16 reads key
+  // rows 16*cc + 4*hi + {0..3} (and +8) at d columns 32*md + 16*(g&1) + {0..15};
+  // group lane a16 supplies row a16/4, columns 4*(a16%4) .. +3
+  uint32_t vofs[C::MD];
+#pragma unroll
+  for (int md = 0; md < C::MD; ++md) {
+    const int r = 4 * hi + (a16 >> 2);
+    const int c = 4 * md + 2 * ((lane >> 4) & 1) + ((a16 & 3) >> 1);
+    vofs[md] = lds0 + C::V_LDS + r * C::ROWB + ((c ^ swz_v<D>(r)) * 16) + (a16 & 1) * 8;
+  }
+  // DMA source offsets: lane fills LDS row r0 + lane/NCH, chunk position
+  // lane%NCH, so it reads source chunk (lane%NCH) ^ swizzle(row)
+  const int lrow = lane / C::NCH;
+  const uint32_t dk = (uint32_t)(lrow * k_snb) + (((lane % C::NCH) ^ swz_k<D>(wave * C::RPW + lrow)) * 16);
+  const uint32_t dv = (uint32_t)(lrow * v_snb) + (((lane % C::NCH) ^ swz_v<D>(lrow)) * 16);
+
+  auto issue = [&](const unsigned char* hbase, int64_t csb, int snb, const Tile& t, uint32_t stage,
+                   uint32_t voff) {
+    const unsigned char* tb = hbase + (t.j * csb + (int64_t)t.tt * kBN * snb);
+#pragma unroll
+    for (int i = 0; i < C::NL; ++i) {
+      const int r0 = (i * kWaves + wave) * C::RPW;
+      const int rows = t.nvalid - r0;
+      const uint32_t bytes = rows > 0 ? (uint32_t)(rows * snb) : 0u;
+      dma16(voff, buffer_rsrc(tb + r0 * snb, bytes), stage + r0 * C::ROWB);
     }
   };
-  auto store_tile = [&](int stage) {
-    uint16_t* kd = k_lds + stage * C::K_STAGE;
-    uint16_t* vd = vt_lds + stage * C::VT_STAGE;
+  auto issue_k = [&](const Tile& t, int stage) { issue(kg, k_csb, k_snb, t, lds0 + C::K_LDS + stage * C::TILE, dk); };
+  auto issue_v = [&](const Tile& t, int stage) { issue(vg, v_csb, v_snb, t, lds0 + C::V_LDS + stage * C::TILE, dv); };
+
+  // ---- scores and masks --------------------------------------------------------
+  // S^T tile: 32 keys (M) x 64 queries (2 N-blocks of 32); accumulator element
+  // j of block nb holds key 8*(j/4) + 4*hi + j%4 of query qw0 + 32*nb + l32
+  auto kfrag = [&](int kc, auto stage) {
+    return lds_b128(kofs[kc] + decltype(stage)::value * C::TILE);
+  };
+  auto mfma_s = [&](f32x16_t (&s)[2], u32x4_t kf, int kc) {
 #pragma unroll
-    for (int r = 0; r < C::KPT; ++r)
-      *reinterpret_cast<u32x4_t*>(kd + (kq * C::KPT + r) * C::KPITCH + 8 * dg) = kreg[r];
-    // transpose: word w of a 16-byte row vector holds columns 8*dg+2w (low
-    // half) and 8*dg+2w+1 (high half); gather the KPT keys of one column into
-    // one 4- or 8-byte LDS chunk
+    for (int nb = 0; nb < 2; ++nb) {
+      const f32x16_t z = {};
+      s[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[nb][kc]), kc == 0 ? z : s[nb],
+                                                      0, 0, 0);
+    }
+  };
+  auto scores = [&](f32x16_t (&s)[2], auto stage) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int kc = 0; kc < C::KC; ++kc) mfma_s(s, kfrag(kc, stage), kc);
+  };
+
+  const int64_t qpos_w = p.q_pos0 + qw0;
+  auto mask = [&](f32x16_t (&s)[2], const Tile& t) {
+    const int64_t kpos = p.k_pos0 + (int64_t)t.j * p.k_posstride + (int64_t)t.tt * kBN;
+    const bool need = t.nvalid < kBN || (p.causal && kpos + kBN - 1 > qpos_w);
+    if (!need) return;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int d = 8 * dg + 2 * w + half;
-        uint16_t* dst = vd + vt_index(d, kq * C::KPT);
-        auto pick = [&](int r) -> uint32_t {
-          return half ? (vreg[r][w] >> 16) : (vreg[r][w] & 0xffffu);
-        };
-        if constexpr (C::KPT == 4) {
-          u32x2_t pk;
-          pk[0] = pick(0) | (pick(1) << 16);
-          pk[1] = pick(2) | (pick(3) << 16);
-          *reinterpret_cast<u32x2_t*>(dst) = pk;
-        } else {
-          *reinterpret_cast<uint32_t*>(dst) = pick(0) | (pick(1) << 16);
-        }
+    for (int nb = 0; nb < 2; ++nb) {
+      int64_t rel = qpos_w + 32 * nb + l32 - kpos;   // last visible key of the tile
+      if (!p.causal || rel > kBN) rel = kBN;
+      const int lastk = (int)min(rel, (int64_t)t.nvalid - 1);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int u = 8 * (j >> 2) + 4 * hi + (j & 3);
+        if (u > lastk) s[nb][j] = kNegInf;
       }
     }
   };
 
-  // ---- accumulators -------------------------------------------------------------
+  // ---- online softmax, in slices that interleave with the MFMAs ----------------
   f32x16_t oacc[C::MD][2];
 #pragma unroll
   for (int md = 0; md < C::MD; ++md)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) oacc[md][nb][j] = 0.f;
+    for (int nb = 0; nb < 2; ++nb) oacc[md][nb] = (f32x16_t){};
   float m_run[2] = {kNegInf, kNegInf};  // running max, base-2 units
   float l_run[2] = {0.f, 0.f};          // this lane's half of the row sum
+  float alpha[2] = {1.f, 1.f};
+  float pmax[2], mneg[2], lsum[2];
+  bool resc = false;
   const float c = p.scale_log2;
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int stage = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-
-    const int64_t key0 = (int64_t)t * kBN;        // first key of the tile
-    // wave-level classification of this tile
-    const bool skip = !wave_active || (p.causal && p.k_pos0 + key0 > p.q_pos0 + q_last_w);
-    if (!skip) {
-      const bool need_mask = (key0 + kBN > n_keys) ||
-                             (p.causal && p.k_pos0 + key0 + kBN - 1 > p.q_pos0 + qw0);
-      const uint16_t* kd = k_lds + stage * C::K_STAGE;
-      const uint16_t* vd = vt_lds + stage * C::VT_STAGE;
-
-      // S^T[key][query] for 64 keys (2 M-blocks) x 64 queries (2 N-blocks)
-      f32x16_t s[2][2];
+  // slice k of the softmax of tile s: 0-1 in-lane max, 2-3 row statistics,
+  // 4-11 exponentials (4 per slice), 12 the row sums
+  constexpr int kSlices = 13;
+  auto softmax_slice = [&](f32x16_t (&s)[2], int k) {
+    if (k < 2) {
+      const int nb = k;
+      float mx = s[nb][0];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int j = 1; j < 16; ++j) mx = __builtin_fmaxf(mx, s[nb][j]);
+      pmax[nb] = mx;
+    } else if (k < 4) {
+      const int nb = k - 2;
+      const float mxs = max_half(pmax[nb]) * c;
+      const bool upd = __any(mxs > m_run[nb] + kRescaleLog2);
+      const float mn = upd ? __builtin_fmaxf(m_run[nb], mxs) : m_run[nb];
+      alpha[nb] = (mn == m_run[nb]) ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - mn);
+      resc = resc || upd;
+      m_run[nb] = mn;
+      mneg[nb] = (mn == kNegInf) ? 0.f : -mn;
+      lsum[nb] = 0.f;
+    } else if (k < 12) {
+      const int nb = (k - 4) >> 2, j0 = ((k - 4) & 3) * 4;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) s[mb][nb][j] = 0.f;
-#pragma unroll
-      for (int kc = 0; kc < C::KC; ++kc) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kd + (32 * mb + l32) * C::KPITCH + 16 * kc + 8 * hi);
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[nb][kc]),
-                                                                  s[mb][nb], 0, 0, 0);
-        }
+      for (int j = j0; j < j0 + 4; ++j) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[nb][j], c, mneg[nb]));
+        s[nb][j] = e;
+        lsum[nb] += e;
       }
-
-      // accumulator element j of block mb holds key 32*mb + 8*(j/4) + 4*hi + j%4
-      if (need_mask) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int64_t qpos = p.q_pos0 + qw0 + 32 * nb + l32;
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              int64_t u = key0 + 32 * mb + 8 * (j >> 2) + 4 * hi + (j & 3);
-              bool vis = u < n_keys && (!p.causal || p.k_pos0 + u <= qpos);
-              if (!vis) s[mb][nb][j] = kNegInf;
-            }
-        }
-      }
-
-      u32x4_t pf[2][4];   // bf16 weights: B operand of O^T = V^T P^T
+    } else {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[mb][nb][j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mxs = mx * c;
-        if (__any(mxs > m_run[nb] + kRescaleLog2)) {
-          const float mn = fmaxf(m_run[nb], mxs);
-          const float alpha = (mn == m_run[nb]) ? 1.f : exp2f(m_run[nb] - mn);
-          l_run[nb] *= alpha;
-#pragma unroll
-          for (int md = 0; md < C::MD; ++md)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) oacc[md][nb][j] *= alpha;
-          m_run[nb] = mn;
-        }
-        const float mneg = (m_run[nb] == kNegInf) ? 0.f : -m_run[nb];
-        float ls = 0.f;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            float e = __builtin_amdgcn_exp2f(fmaf(s[mb][nb][j], c, mneg));
-            s[mb][nb][j] = e;
-            ls += e;
-          }
-        l_run[nb] += ls;
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const int mb = cc >> 1, j0 = 8 * (cc & 1);
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            pf[nb][cc][w] = pack_bf16x2(s[mb][nb][j0 + 2 * w], s[mb][nb][j0 + 2 * w + 1]);
-        }
-      }
-
-      // O^T[d][query] += V^T[d][key] P^T[key][query]; contraction step cc covers
-      // keys 16*cc + {4*hi .. 4*hi+3} and 16*cc + 8 + {4*hi .. 4*hi+3}
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-#pragma unroll
-        for (int md = 0; md < C::MD; ++md) {
-          const int d = 32 * md + l32;
-          u32x2_t a0 = *reinterpret_cast<const u32x2_t*>(vd + vt_index(d, 16 * cc + 4 * hi));
-          u32x2_t a1 = *reinterpret_cast<const u32x2_t*>(vd + vt_index(d, 16 * cc + 8 + 4 * hi));
-          u32x4_t vf = {a0[0], a0[1], a1[0], a1[1]};
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            oacc[md][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[nb][cc]),
-                                                                     oacc[md][nb], 0, 0, 0);
-        }
+        l_run[nb] = fmaf(l_run[nb], alpha[nb], lsum[nb]);
+        pin(l_run[nb]);
       }
     }
+  };
 
-    if (t + 1 < ntiles) store_tile(stage ^ 1);
-    __syncthreads();
+  u32x4_t pf[2][2];   // bf16 weights: B operand of O^T = V^T P^T, [nb][cc]
+  auto pack = [&](const f32x16_t (&s)[2], int cc) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+    {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pf[nb][cc][w] = pack_bf16x2(s[nb][8 * cc + 2 * w], s[nb][8 * cc + 2 * w + 1]);
+      pin(pf[nb][cc]);
+    }
+  };
+  // O *= alpha when the running max moved (rare).  O lives in accumulation
+  // registers; each element goes through a VGPR, four at a time.  Stating the
+  // registers as "a" operands keeps the compiler from moving all of O to VGPRs.
+  auto rescale = [&]() {
+#pragma unroll
+    for (int md = 0; md < C::MD; ++md)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; i += 4) {
+          float x0 = oacc[md][nb][i], x1 = oacc[md][nb][i + 1], x2 = oacc[md][nb][i + 2], x3 = oacc[md][nb][i + 3];
+          float tmp;
+          asm volatile(
+              "v_accvgpr_read_b32 %4, %0\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %0, %4\n\t"
+              "v_accvgpr_read_b32 %4, %1\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %1, %4\n\t"
+              "v_accvgpr_read_b32 %4, %2\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %2, %4\n\t"
+              "v_accvgpr_read_b32 %4, %3\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %3, %4"
+              : "+a"(x0), "+a"(x1), "+a"(x2), "+a"(x3), "=&v"(tmp)
+              : "v"(alpha[nb]));
+          oacc[md][nb][i] = x0;
+          oacc[md][nb][i + 1] = x1;
+          oacc[md][nb][i + 2] = x2;
+          oacc[md][nb][i + 3] = x3;
+        }
+  };
+
+  // O^T[d][query] += V^T[d][key] P^T[key][query]; contraction step cc covers
+  // keys 16*cc + {4*hi .. 4*hi+3} and 16*cc + 8 + {4*hi .. 4*hi+3}
+  auto vfrag = [&](int cc, int md, auto stage) {
+    const uint32_t a = vofs[md] + decltype(stage)::value * C::TILE + (16 * cc) * C::ROWB;
+    const i16x4_t lo = lds_tr16(a);
+    const i16x4_t up = lds_tr16(a + 8 * C::ROWB);
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto mfma_pv = [&](bf16x8_t vf, int cc, int md) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      oacc[md][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pf[nb][cc]), oacc[md][nb], 0, 0, 0);
+  };
+  auto pv = [&](auto stage) {
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int md = 0; md < C::MD; ++md) mfma_pv(vfrag(cc, md, stage), cc, md);
+  };
+
+  // ---- main loop -----------------------------------------------------------------
+  // first chunk of the visit: the rank's own; its visible keys for this block
+  int64_t lim0 = p.n_k;
+  if (p.causal) {
+    const int64_t qpos_last = p.q_pos0 + min(q0 + kBM, p.n_q) - 1;
+    lim0 = max((int64_t)0, min(lim0, qpos_last - (p.k_pos0 + (int64_t)p.rank * p.k_posstride) + 1));
   }
+  const int ntl0 = (int)((lim0 + kBN - 1) / kBN);
+  const int ntl_full = (p.n_k + kBN - 1) / kBN;
+  const int T = ntl0 == 0 ? 0 : ntl0 + (p.nseg - 1) * ntl_full;
+  TileWalk walk{0, -1, ntl0, (int)lim0, ntl_full, p.n_k, p.nseg, p.rank, p.P};
+  if (T > 0) {
+    f32x16_t sa[2], sb[2];
+    const Tile t0 = walk.next(), t1 = walk.next(), t2 = walk.next(), t3 = walk.next();
+    const Tile t4 = walk.next();
+    issue_k(t0, 0);
+    issue_k(t1, 1);
+    issue_k(t2, 2);
+    issue_v(t0, 0);
+    issue_k(t3, 3);
+    issue_v(t1, 1);
+    wait_dma_and_sync<4 * C::NL>();      // K(0), K(1) landed
+    scores(sa, Step<0>{});
+    scores(sb, Step<1>{});
+    mask(sa, t0);
+    mask(sb, t1);
+#pragma unroll
+    for (int k = 0; k < kSlices; ++k) softmax_slice(sa, k);   // O is still zero: no rescale
+    pack(sa, 0);
+    pack(sa, 1);
+    lds_reads_done_sync();               // K stage 0 is free
+    issue_k(t4, 0);
+    issue_v(t2, 2);
+    // tiles t+2 .. t+5 at the top of iteration t
+    Tile d2 = t2, d3 = t3, d4 = t4, d5 = walk.next();
+
+    // iteration t = 4k + R: K(t+5) and V(t+3) are fetched; S(t+2) computed into
+    // `nx`; O += V(t) P(t); S(t+1) in `cu` goes through the softmax into P(t+1).
+    // Step i issues the LDS reads of step i+1, two MFMAs and softmax slice i.
+    // Columns 0-15 of P(t+1) are packed once the MFMAs reading those of P(t)
+    // are issued (PV step MD) and their exponentials exist (slice 9).
+    constexpr int kPack0Step = C::MD > 9 - C::KC ? C::MD : 9 - C::KC;
+    auto body = [&](auto R, f32x16_t (&nx)[2], f32x16_t (&cu)[2]) {
+      constexpr int r = decltype(R)::value;
+      constexpr int ks = (r + 2) % kStages, vs = r;
+      wait_dma_and_sync<4 * C::NL>();    // K(t+2), V(t) landed
+      issue_k(d5, (r + 5) % kStages);
+      issue_v(d3, (r + 3) % kStages);
+      resc = false;
+      u32x4_t kf = kfrag(0, Step<ks>{});
+      bf16x8_t vf;
+#pragma unroll
+      for (int kc = 0; kc < C::KC; ++kc) {
+        u32x4_t kn;
+        if (kc + 1 < C::KC) kn = kfrag(kc + 1, Step<ks>{});
+        else vf = vfrag(0, 0, Step<vs>{});
+        mfma_s(nx, kf, kc);
+        softmax_slice(cu, kc);
+        __builtin_amdgcn_sched_barrier(0);
+        kf = kn;
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * C::MD; ++i) {
+        const int cc = i / C::MD, md = i % C::MD;
+        bf16x8_t vn;
+        if (i + 1 < 2 * C::MD) vn = vfrag((i + 1) / C::MD, (i + 1) % C::MD, Step<vs>{});
+        mfma_pv(vf, cc, md);
+        if (C::KC + i < kSlices) softmax_slice(cu, C::KC + i);
+        if (i == kPack0Step) pack(cu, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        vf = vn;
+      }
+#pragma unroll
+      for (int k = C::KC + 2 * C::MD; k < kSlices; ++k) softmax_slice(cu, k);
+      if (kPack0Step >= 2 * C::MD) pack(cu, 0);
+      pack(cu, 1);
+      if (resc) rescale();
+      mask(nx, d2);
+      d2 = d3;
+      d3 = d4;
+      d4 = d5;
+      d5 = walk.next();
+    };
+    // T - 1 iterations, padded to a multiple of 4 with empty tiles
+    const int iters = (T - 1 + 3) & ~3;
+    for (int t = 0; t < iters; t += 4) {
+      body(Step<0>{}, sa, sb);
+      body(Step<1>{}, sb, sa);
+      body(Step<2>{}, sa, sb);
+      body(Step<3>{}, sb, sa);
+    }
+    wait_dma_and_sync<4 * C::NL>();      // V of the last (padded) tile landed
+    pv(Step<0>{});
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no DMA may outlive the workgroup's LDS
 
   // ---- epilogue: normalise, merge into the running (O, lse), store ------------
-  if (!wave_active) return;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int row = qw0 + 32 * nb + l32;
-    const float lt = l_run[nb] + __shfl_xor(l_run[nb], 32);
+    const float lt = sum_half(l_run[nb]);
     if (row >= p.n_q) continue;
     const float lse_j = (lt > 0.f) ? (m_run[nb] + log2f(lt)) * kLn2 : kNegInf;
     const float inv = (lt > 0.f) ? 1.f / lt : 0.f;

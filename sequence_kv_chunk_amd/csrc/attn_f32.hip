@@ -8,7 +8,8 @@
 // This is the exact-precision variant (no reduced-precision products): one
 // lane owns one query row, keeps q and its output accumulator in registers
 // and runs the online softmax over 32-key tiles of K and V staged in LDS
-// (every lane reads the same K/V element at a time: an LDS broadcast).  It is
+// (every lane reads the same K/V element at a time: an LDS broadcast).  The
+// key/value chunks of a ring visit are met in ring order within one launch.  It is
 // meant for correctness-critical fp32 use; the bf16 MFMA kernel is the
 // throughput path.
 #include "attn_common.h"
@@ -29,8 +30,8 @@ __global__ void __launch_bounds__(kRows) attn_f32_kernel(AttnParams p) {
   const int t = blockIdx.x * kRows + threadIdx.x;
   const bool row_ok = t < p.n_q;
   const float* qrow = static_cast<const float*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)(row_ok ? t : 0) * p.q_sn;
-  const float* kb = static_cast<const float*>(p.k) + b * p.k_sb + hk * p.k_sh;
-  const float* vb = static_cast<const float*>(p.v) + b * p.v_sb + hk * p.v_sh;
+  const float* kb0 = static_cast<const float*>(p.k) + b * p.k_sb + hk * p.k_sh;
+  const float* vb0 = static_cast<const float*>(p.v) + b * p.v_sb + hk * p.v_sh;
 
   float q[D];
   float o[D];
@@ -42,54 +43,58 @@ __global__ void __launch_bounds__(kRows) attn_f32_kernel(AttnParams p) {
   }
   const float c = p.scale_log2;
   const int64_t qpos = p.q_pos0 + t;
-  // causal: keys u with k_pos0 + u <= max query position of this block
-  int64_t n_keys = p.n_k;
-  if (p.causal) {
-    int64_t tmax = min((int64_t)blockIdx.x * kRows + kRows - 1, (int64_t)p.n_q - 1);
-    int64_t lim = p.q_pos0 + tmax - p.k_pos0 + 1;
-    n_keys = max((int64_t)0, min(n_keys, lim));
-  }
+  const int64_t tmax = min((int64_t)blockIdx.x * kRows + kRows - 1, (int64_t)p.n_q - 1);
   float m = kNegInf;  // running max of logits, base-2 units
   float l = 0.f;      // running normaliser
-  for (int64_t k0 = 0; k0 < n_keys; k0 += kTile) {
-    __syncthreads();
-    for (int i = threadIdx.x; i < kTile * D / 4; i += kRows) {
-      int r = i / (D / 4), e = (i % (D / 4)) * 4;
-      int64_t u = k0 + r;
-      float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
-      if (u < n_keys) {
-        kx = *reinterpret_cast<const float4*>(kb + u * p.k_sn + e);
-        vx = *reinterpret_cast<const float4*>(vb + u * p.v_sn + e);
+  // chunks in ring order: visit s reads chunk j = (rank - s) mod P
+  for (int s = 0; s < p.nseg; ++s) {
+    const int j = (p.rank - s + p.P) % p.P;
+    const float* kb = kb0 + (int64_t)j * p.k_cs;
+    const float* vb = vb0 + (int64_t)j * p.v_cs;
+    const int64_t kpos0 = p.k_pos0 + (int64_t)j * p.k_posstride;
+    // causal: keys u with kpos0 + u <= max query position of this block
+    int64_t n_keys = p.n_k;
+    if (p.causal) n_keys = max((int64_t)0, min(n_keys, p.q_pos0 + tmax - kpos0 + 1));
+    for (int64_t k0 = 0; k0 < n_keys; k0 += kTile) {
+      __syncthreads();
+      for (int i = threadIdx.x; i < kTile * D / 4; i += kRows) {
+        int r = i / (D / 4), e = (i % (D / 4)) * 4;
+        int64_t u = k0 + r;
+        float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
+        if (u < n_keys) {
+          kx = *reinterpret_cast<const float4*>(kb + u * p.k_sn + e);
+          vx = *reinterpret_cast<const float4*>(vb + u * p.v_sn + e);
+        }
+        *reinterpret_cast<float4*>(&ks[r][e]) = kx;
+        *reinterpret_cast<float4*>(&vs[r][e]) = vx;
       }
-      *reinterpret_cast<float4*>(&ks[r][e]) = kx;
-      *reinterpret_cast<float4*>(&vs[r][e]) = vx;
-    }
-    __syncthreads();
-    float s[kTile];
-    float tmax = kNegInf;
+      __syncthreads();
+      float sc[kTile];
+      float tmx = kNegInf;
 #pragma unroll
-    for (int j = 0; j < kTile; ++j) {
-      float acc = 0.f;
+      for (int jj = 0; jj < kTile; ++jj) {
+        float acc = 0.f;
 #pragma unroll
-      for (int e = 0; e < D; ++e) acc = fmaf(q[e], ks[j][e], acc);
-      int64_t u = k0 + j;
-      bool vis = u < n_keys && (!p.causal || p.k_pos0 + u <= qpos);
-      s[j] = vis ? acc * c : kNegInf;
-      tmax = fmaxf(tmax, s[j]);
-    }
-    float mn = fmaxf(m, tmax);
-    if (mn != kNegInf) {
-      float alpha = (m == mn) ? 1.f : exp2f(m - mn);
-      l *= alpha;
+        for (int e = 0; e < D; ++e) acc = fmaf(q[e], ks[jj][e], acc);
+        int64_t u = k0 + jj;
+        bool vis = u < n_keys && (!p.causal || kpos0 + u <= qpos);
+        sc[jj] = vis ? acc * c : kNegInf;
+        tmx = fmaxf(tmx, sc[jj]);
+      }
+      float mn = fmaxf(m, tmx);
+      if (mn != kNegInf) {
+        float alpha = (m == mn) ? 1.f : exp2f(m - mn);
+        l *= alpha;
 #pragma unroll
-      for (int e = 0; e < D; ++e) o[e] *= alpha;
-      m = mn;
+        for (int e = 0; e < D; ++e) o[e] *= alpha;
+        m = mn;
 #pragma unroll
-      for (int j = 0; j < kTile; ++j) {
-        float pj = exp2f(s[j] - m);
-        l += pj;
+        for (int jj = 0; jj < kTile; ++jj) {
+          float pj = exp2f(sc[jj] - m);
+          l += pj;
 #pragma unroll
-        for (int e = 0; e < D; ++e) o[e] = fmaf(pj, vs[j][e], o[e]);
+          for (int e = 0; e < D; ++e) o[e] = fmaf(pj, vs[jj][e], o[e]);
+        }
       }
     }
   }

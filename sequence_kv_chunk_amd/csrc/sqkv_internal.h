@@ -9,7 +9,11 @@ namespace sqkv {
 
 enum DType : int { kF32 = 0, kBF16 = 1 };
 
-// One chunk-attention launch.  Views are [B, H, n, d] with element strides.
+// One attention launch: a query chunk against `nseg` key/value chunks visited
+// in ring order.  Views are [B, H, n, d] with element strides.  Visit s reads
+// chunk j = (rank - s) mod P, which starts j*k_cs (j*v_cs) elements after k
+// (v) and whose key 0 sits at global position k_pos0 + j*k_posstride.  A
+// single chunk is nseg = P = 1, rank = 0.
 struct AttnParams {
   const void* q;
   const void* k;
@@ -17,6 +21,9 @@ struct AttnParams {
   int64_t q_sb, q_sh, q_sn;
   int64_t k_sb, k_sh, k_sn;
   int64_t v_sb, v_sh, v_sn;
+  int64_t k_cs, v_cs;         // chunk strides of the key / value pools
+  int64_t k_posstride;        // positions between consecutive chunks
+  int nseg, P, rank;
   const void* o_in;  // nullptr: no running state
   int64_t oi_sb, oi_sh, oi_sn;
   const float* lse_in;

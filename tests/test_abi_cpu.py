@@ -69,7 +69,7 @@ def _setup(lib):
     V = View
     i, i64, f, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
     lib.ra_chunk_attention.argtypes = [V, V, V, V, vp, V, vp, i, i, i, i, i, i, i, i, i, f, i, i64, i64, vp]
-    lib.ra_ring_attention.argtypes = [V, V, V, i64, i64, V, vp, V, i, i, i, i, i, i, i, i, i, f, i, vp]
+    lib.ra_ring_attention.argtypes = [V, V, V, i64, i64, V, vp, i, i, i, i, i, i, i, i, i, f, i, vp]
     lib.ra_lse_merge.argtypes = [V, vp, i, V, vp, i, V, vp, i, i, i, i, i, vp]
     lib.ulysses_seq_to_head.argtypes = [vp, vp, i, i64, i, i, i, i, vp]
     lib.ulysses_head_to_seq.argtypes = [vp, vp, i, i64, i, i, i, vp]
@@ -140,18 +140,16 @@ def test_ring_rejects(lib):
     o, lse, none = _dense(4 * GB, 4, 64, 128), 5 * GB, View(None, 0, 0, 0)
     cs = 4 * 64 * 128
 
-    def call(P=4, rank=0, out_dt=BF16, work=none, causal=0, kcs=cs):
-        return lib.ra_ring_attention(q, k, v, kcs, cs, o, lse, work, 1, 4, 4, 64, 128, P, rank, BF16, out_dt,
+    def call(P=4, rank=0, out_dt=BF16, causal=0, kcs=cs):
+        return lib.ra_ring_attention(q, k, v, kcs, cs, o, lse, 1, 4, 4, 64, 128, P, rank, BF16, out_dt,
                                      1.0, causal, None)
 
     assert call(rank=4) == EINVAL
     assert call(rank=-1) == EINVAL
     assert call(P=0) == EINVAL
-    assert call(out_dt=BF16) == EINVAL, "bf16 result over several chunks needs o_work"
     assert call(kcs=cs + 3) == EUNSUP
-    assert call(work=_dense(4 * GB + 64, 4, 64, 128)) == EINVAL, "o_work overlapping o"
     # the pool of 4 chunks reaches into o when o sits right after chunk 0
-    assert lib.ra_ring_attention(q, k, v, cs, cs, _dense(2 * GB + 2 * cs, 4, 64, 128), lse, none, 1, 4, 4, 64,
+    assert lib.ra_ring_attention(q, k, v, cs, cs, _dense(2 * GB + 2 * cs, 4, 64, 128), lse, 1, 4, 4, 64,
                                  128, 4, 1, BF16, F32, 1.0, 0, None) == EINVAL
 
 

@@ -160,8 +160,7 @@ def _ring_run(api, w, qb, kb, vb, ranks, L=None, P=None):
         qi = dev(qb[idx])
         B, H, n, d = qi.shape
         o, lse = _out(B, H, n, d, dt)
-        work = torch.empty((B, H, n, d), dtype=torch.float32, device="cuda") if dt == torch.bfloat16 else None
-        api.ra_ring_attention(qi, kp, vp, o, lse, rank=i, o_work=work, scale=1.0, causal=w.causal)
+        api.ra_ring_attention(qi, kp, vp, o, lse, rank=i, scale=1.0, causal=w.causal)
         torch.cuda.synchronize()
         outs.append((host_f64(o), host_f64(lse).reshape(B, H, n)))
     return outs
