@@ -11,8 +11,8 @@
 // Design (gfx950, wave64, v_mfma_f32_32x32x16_bf16):
 // * A workgroup of 4 wavefronts owns 256 query rows of one (batch, head); each
 //   wavefront owns 64 rows and keeps their Q fragments in registers.  Keys
-//   are processed in tiles of 32, which keeps a tile's scores in 32 registers
-//   per lane so that two tiles can be in flight at once.
+//   are processed in tiles of 64 (two 32-key MFMA blocks); a tile's scores
+//   take 64 registers per lane and two tiles are in flight at once.
 // * Scores are computed transposed, S^T = K Q^T (keys on the MFMA M axis,
 //   queries on N).  In the 32x32 accumulator layout a lane then holds 16 keys
 //   of ONE query, so the row max and row sum are in-lane reductions plus one
@@ -31,9 +31,9 @@
 //       S(t+2) = K(t+2) Q^T      (MFMA)
 //       O     += V(t)^T P(t)^T   (MFMA)
 //       softmax of S(t+1)        (VALU / transcendental, overlaps the MFMAs)
-//   The three streams are interleaved by hand, two MFMAs at a time with a
-//   slice of the softmax between them, and fenced with sched_barrier so the
-//   compiler keeps that order.  K and V tiles go through four LDS stages each
+//   The three streams are interleaved by hand: S steps and PV steps
+//   alternate, two MFMAs each, with a slice of the softmax after each, fenced
+//   with sched_barrier so the compiler keeps that order.  K and V tiles go through four LDS stages each
 //   and are fetched three iterations before use.  The loop is unrolled by four
 //   so that every stage address is an instruction immediate.  The DMA loads are inline assembly,
 //   their completion counted with explicit s_waitcnt vmcnt, because the
@@ -68,9 +68,17 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQW = 64;              // query rows per wavefront
 constexpr int kBM = kQW * kWaves;    // query rows per workgroup
-constexpr int kBN = 32;              // keys per tile (one 32-row MFMA block)
+#ifndef SQKV_MB
+#define SQKV_MB 1
+#endif
+constexpr int kMB = SQKV_MB;         // 32-key MFMA blocks per tile
+constexpr int kBN = 32 * kMB;        // keys per tile
+constexpr int kNCC = 2 * kMB;        // 16-key contraction steps of P V per tile
 constexpr int kStages = 4;           // LDS stages per tensor (= loop unroll)
 constexpr float kRescaleLog2 = 8.0f;
+#ifndef SQKV_PF
+#define SQKV_PF 2
+#endif
 
 template <int D>
 struct Cfg {
@@ -172,10 +180,10 @@ __device__ __forceinline__ void wait_dma_and_sync() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// One 64-key tile of the visit: chunk j, tile tt inside it, nvalid keys
-// (0 for "past the end").
+// One tile of the visit: visit position s (chunk j = (rank - s) mod P), tile
+// tt inside that chunk, nvalid keys (0 for "past the end").
 struct Tile {
-  int j, tt, nvalid;
+  int s, tt, nvalid;
 };
 
 // Walks the tiles a workgroup visits: chunks in ring order, and in each chunk
@@ -185,8 +193,8 @@ struct Tile {
 // the past of the rank's queries and is visited whole.  next() is branch-free
 // scalar code so that it can sit inside the pipelined loop.
 struct TileWalk {
-  int s, tt, ntl, lim;       // current chunk of the visit, tile in it, its tiles / keys
-  int ntl_full, n_k, nseg, rank, P;
+  int s, tt, ntl, lim;       // current visit position, tile in it, its tiles / keys
+  int ntl_full, n_k, nseg;
 
   __device__ Tile next() {
     tt += 1;
@@ -195,10 +203,8 @@ struct TileWalk {
     tt = wrap ? 0 : tt;
     ntl = wrap ? ntl_full : ntl;
     lim = wrap ? n_k : lim;
-    int j = rank - s;
-    j = j < 0 ? j + P : j;
     const int nv = s < nseg ? min(kBN, lim - tt * kBN) : 0;
-    return Tile{j, tt, nv};
+    return Tile{s, tt, nv};
   }
 };
 
@@ -280,9 +286,14 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   const uint32_t dk = (uint32_t)(lrow * k_snb) + (((lane % C::NCH) ^ swz_k<D>(wave * C::RPW + lrow)) * 16);
   const uint32_t dv = (uint32_t)(lrow * v_snb) + (((lane % C::NCH) ^ swz_v<D>(lrow)) * 16);
 
+  // chunk of visit position s
+  auto chunk_of = [&](int s) {
+    const int j = p.rank - s;
+    return j < 0 ? j + p.P : j;
+  };
   auto issue = [&](const unsigned char* hbase, int64_t csb, int snb, const Tile& t, uint32_t stage,
                    uint32_t voff) {
-    const unsigned char* tb = hbase + (t.j * csb + (int64_t)t.tt * kBN * snb);
+    const unsigned char* tb = hbase + (chunk_of(t.s) * csb + (int64_t)(t.tt * kBN) * snb);
 #pragma unroll
     for (int i = 0; i < C::NL; ++i) {
       const int r0 = (i * kWaves + wave) * C::RPW;
@@ -295,39 +306,49 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   auto issue_v = [&](const Tile& t, int stage) { issue(vg, v_csb, v_snb, t, lds0 + C::V_LDS + stage * C::TILE, dv); };
 
   // ---- scores and masks --------------------------------------------------------
-  // S^T tile: 32 keys (M) x 64 queries (2 N-blocks of 32); accumulator element
-  // j of block nb holds key 8*(j/4) + 4*hi + j%4 of query qw0 + 32*nb + l32
-  auto kfrag = [&](int kc, auto stage) {
-    return lds_b128(kofs[kc] + decltype(stage)::value * C::TILE);
+  // S^T tile: kBN keys (kMB M-blocks of 32) x 64 queries (2 N-blocks of 32);
+  // accumulator element j of block (mb, nb) holds key 32*mb + 8*(j/4) + 4*hi +
+  // j%4 of query qw0 + 32*nb + l32
+  auto kfrag = [&](int kc, int mb, auto stage) {
+    return lds_b128(kofs[kc] + decltype(stage)::value * C::TILE + mb * 32 * C::ROWB);
   };
-  auto mfma_s = [&](f32x16_t (&s)[2], u32x4_t kf, int kc) {
+  auto mfma_s = [&](f32x16_t (&s)[kMB][2], u32x4_t kf, int kc, int mb) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const f32x16_t z = {};
-      s[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[nb][kc]), kc == 0 ? z : s[nb],
-                                                      0, 0, 0);
+      s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[nb][kc]),
+                                                          kc == 0 ? z : s[mb][nb], 0, 0, 0);
     }
   };
-  auto scores = [&](f32x16_t (&s)[2], auto stage) {
+  auto scores = [&](f32x16_t (&s)[kMB][2], auto stage) {
 #pragma unroll
-    for (int kc = 0; kc < C::KC; ++kc) mfma_s(s, kfrag(kc, stage), kc);
+    for (int kc = 0; kc < C::KC; ++kc)
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) mfma_s(s, kfrag(kc, mb, stage), kc, mb);
   };
 
+  // Causal masks only touch tiles of the first chunk of the visit (the rank's
+  // own): those at or after tile tt_mask can hold a key after this wave's
+  // first query.
   const int64_t qpos_w = p.q_pos0 + qw0;
-  auto mask = [&](f32x16_t (&s)[2], const Tile& t) {
-    const int64_t kpos = p.k_pos0 + (int64_t)t.j * p.k_posstride + (int64_t)t.tt * kBN;
-    const bool need = t.nvalid < kBN || (p.causal && kpos + kBN - 1 > qpos_w);
-    if (!need) return;
+  const int64_t kpos_own = p.k_pos0 + (int64_t)p.rank * p.k_posstride;
+  const int tt_mask = (int)max((int64_t)0, (qpos_w - kpos_own - kBN + 1 + kBN) / kBN);
+  auto mask = [&](f32x16_t (&s)[kMB][2], const Tile& t) {
+    const bool diag = p.causal && t.s == 0 && t.tt >= tt_mask;
+    if (!(t.nvalid < kBN || diag)) return;
+    const int64_t kpos = kpos_own + (int64_t)t.tt * kBN;   // only read for the own chunk
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       int64_t rel = qpos_w + 32 * nb + l32 - kpos;   // last visible key of the tile
-      if (!p.causal || rel > kBN) rel = kBN;
+      if (!diag || rel > kBN) rel = kBN;
       const int lastk = (int)min(rel, (int64_t)t.nvalid - 1);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int u = 8 * (j >> 2) + 4 * hi + (j & 3);
-        if (u > lastk) s[nb][j] = kNegInf;
-      }
+      for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int u = 32 * mb + 8 * (j >> 2) + 4 * hi + (j & 3);
+          if (u > lastk) s[mb][nb][j] = kNegInf;
+        }
     }
   };
 
@@ -340,54 +361,88 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   float m_run[2] = {kNegInf, kNegInf};  // running max, base-2 units
   float l_run[2] = {0.f, 0.f};          // this lane's half of the row sum
   float alpha[2] = {1.f, 1.f};
-  float pmax[2], mneg[2], lsum[2];
+  float pmax[2], mneg[2];
   bool resc = false;
   const float c = p.scale_log2;
 
-  // slice k of the softmax of tile s: 0-1 in-lane max, 2-3 row statistics,
-  // 4-11 exponentials (4 per slice), 12 the row sums
-  constexpr int kSlices = 13;
-  auto softmax_slice = [&](f32x16_t (&s)[2], int k) {
-    if (k < 2) {
-      const int nb = k;
-      float mx = s[nb][0];
+  // P columns cc (16 keys of the P V contraction step cc) are accumulator
+  // elements 8*(cc%2) .. +7 of block mb = cc/2.
+  // Slices of the softmax of tile s, each short and free of long dependency
+  // chains (the wave issues in order, so a chain would stall the MFMAs too):
+  //   0  in-lane max of both query blocks as trees of v_max3
+  //   1  max with the other half of the keys, scaled, compared to the
+  //      running max
+  //   2  new running max (moved only if some lane needs it), alpha, -max
+  //   3 + 2*cc + nb  the 8 exponentials of columns cc of query block nb and
+  //      their sum as a tree
+  //   last  the row sums
+  constexpr int kSlices = 3 + 2 * kNCC + 1;
+  float mxs[2], lpart[2][kNCC];
+  bool upd[2];
+  auto max16 = [&](const f32x16_t& v, float x) {
+    // max of x and 16 values, depth 3
+    const float a0 = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
+    const float a1 = __builtin_fmaxf(__builtin_fmaxf(v[3], v[4]), v[5]);
+    const float a2 = __builtin_fmaxf(__builtin_fmaxf(v[6], v[7]), v[8]);
+    const float a3 = __builtin_fmaxf(__builtin_fmaxf(v[9], v[10]), v[11]);
+    const float a4 = __builtin_fmaxf(__builtin_fmaxf(v[12], v[13]), v[14]);
+    const float a5 = __builtin_fmaxf(__builtin_fmaxf(v[15], x), a0);
+    return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(a1, a2), a3), __builtin_fmaxf(a4, a5));
+  };
+  auto softmax_slice = [&](f32x16_t (&s)[kMB][2], int k) {
+    if (k == 0) {
 #pragma unroll
-      for (int j = 1; j < 16; ++j) mx = __builtin_fmaxf(mx, s[nb][j]);
-      pmax[nb] = mx;
-    } else if (k < 4) {
-      const int nb = k - 2;
-      const float mxs = max_half(pmax[nb]) * c;
-      const bool upd = __any(mxs > m_run[nb] + kRescaleLog2);
-      const float mn = upd ? __builtin_fmaxf(m_run[nb], mxs) : m_run[nb];
-      alpha[nb] = (mn == m_run[nb]) ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - mn);
-      resc = resc || upd;
-      m_run[nb] = mn;
-      mneg[nb] = (mn == kNegInf) ? 0.f : -mn;
-      lsum[nb] = 0.f;
-    } else if (k < 12) {
-      const int nb = (k - 4) >> 2, j0 = ((k - 4) & 3) * 4;
+      for (int nb = 0; nb < 2; ++nb) {
+        float mx = kNegInf;
 #pragma unroll
-      for (int j = j0; j < j0 + 4; ++j) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[nb][j], c, mneg[nb]));
-        s[nb][j] = e;
-        lsum[nb] += e;
+        for (int mb = 0; mb < kMB; ++mb) mx = max16(s[mb][nb], mx);
+        pmax[nb] = mx;
       }
+    } else if (k == 1) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        mxs[nb] = max_half(pmax[nb]) * c;
+        upd[nb] = mxs[nb] > m_run[nb] + kRescaleLog2;
+      }
+    } else if (k == 2) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const bool u = __any(upd[nb]);
+        const float mn = u ? __builtin_fmaxf(m_run[nb], mxs[nb]) : m_run[nb];
+        alpha[nb] = (mn == m_run[nb]) ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - mn);
+        resc = resc || u;
+        m_run[nb] = mn;
+        mneg[nb] = (mn == kNegInf) ? 0.f : -mn;
+      }
+    } else if (k < 3 + 2 * kNCC) {
+      const int cc = (k - 3) >> 1, nb = (k - 3) & 1;
+      const int mb = cc >> 1, j0 = 8 * (cc & 1);
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        e[j] = __builtin_amdgcn_exp2f(fmaf(s[mb][nb][j0 + j], c, mneg[nb]));
+        s[mb][nb][j0 + j] = e[j];
+      }
+      lpart[nb][cc] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
     } else {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        l_run[nb] = fmaf(l_run[nb], alpha[nb], lsum[nb]);
+        float t = lpart[nb][0];
+#pragma unroll
+        for (int cc = 1; cc < kNCC; ++cc) t += lpart[nb][cc];
+        l_run[nb] = fmaf(l_run[nb], alpha[nb], t);
         pin(l_run[nb]);
       }
     }
   };
 
-  u32x4_t pf[2][2];   // bf16 weights: B operand of O^T = V^T P^T, [nb][cc]
-  auto pack = [&](const f32x16_t (&s)[2], int cc) {
+  u32x4_t pf[2][kNCC];   // bf16 weights: B operand of O^T = V^T P^T, [nb][cc]
+  auto pack = [&](const f32x16_t (&s)[kMB][2], int cc) {
+    const int mb = cc >> 1, j0 = 8 * (cc & 1);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-    {
+    for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) pf[nb][cc][w] = pack_bf16x2(s[nb][8 * cc + 2 * w], s[nb][8 * cc + 2 * w + 1]);
+      for (int w = 0; w < 4; ++w) pf[nb][cc][w] = pack_bf16x2(s[mb][nb][j0 + 2 * w], s[mb][nb][j0 + 2 * w + 1]);
       pin(pf[nb][cc]);
     }
   };
@@ -432,7 +487,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   };
   auto pv = [&](auto stage) {
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
+    for (int cc = 0; cc < kNCC; ++cc)
 #pragma unroll
       for (int md = 0; md < C::MD; ++md) mfma_pv(vfrag(cc, md, stage), cc, md);
   };
@@ -442,14 +497,14 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   int64_t lim0 = p.n_k;
   if (p.causal) {
     const int64_t qpos_last = p.q_pos0 + min(q0 + kBM, p.n_q) - 1;
-    lim0 = max((int64_t)0, min(lim0, qpos_last - (p.k_pos0 + (int64_t)p.rank * p.k_posstride) + 1));
+    lim0 = max((int64_t)0, min(lim0, qpos_last - kpos_own + 1));
   }
   const int ntl0 = (int)((lim0 + kBN - 1) / kBN);
   const int ntl_full = (p.n_k + kBN - 1) / kBN;
   const int T = ntl0 == 0 ? 0 : ntl0 + (p.nseg - 1) * ntl_full;
-  TileWalk walk{0, -1, ntl0, (int)lim0, ntl_full, p.n_k, p.nseg, p.rank, p.P};
+  TileWalk walk{0, -1, ntl0, (int)lim0, ntl_full, p.n_k, p.nseg};
   if (T > 0) {
-    f32x16_t sa[2], sb[2];
+    f32x16_t sa[kMB][2], sb[kMB][2];
     const Tile t0 = walk.next(), t1 = walk.next(), t2 = walk.next(), t3 = walk.next();
     const Tile t4 = walk.next();
     issue_k(t0, 0);
@@ -465,54 +520,72 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     mask(sb, t1);
 #pragma unroll
     for (int k = 0; k < kSlices; ++k) softmax_slice(sa, k);   // O is still zero: no rescale
-    pack(sa, 0);
-    pack(sa, 1);
+#pragma unroll
+    for (int cc = 0; cc < kNCC; ++cc) pack(sa, cc);
     lds_reads_done_sync();               // K stage 0 is free
     issue_k(t4, 0);
     issue_v(t2, 2);
     // tiles t+2 .. t+5 at the top of iteration t
     Tile d2 = t2, d3 = t3, d4 = t4, d5 = walk.next();
 
-    // iteration t = 4k + R: K(t+5) and V(t+3) are fetched; S(t+2) computed into
-    // `nx`; O += V(t) P(t); S(t+1) in `cu` goes through the softmax into P(t+1).
-    // Step i issues the LDS reads of step i+1, two MFMAs and softmax slice i.
-    // Columns 0-15 of P(t+1) are packed once the MFMAs reading those of P(t)
-    // are issued (PV step MD) and their exponentials exist (slice 9).
-    constexpr int kPack0Step = C::MD > 9 - C::KC ? C::MD : 9 - C::KC;
-    auto body = [&](auto R, f32x16_t (&nx)[2], f32x16_t (&cu)[2]) {
+    // Iteration t = 4k + R: K(t+5) and V(t+3) are fetched; S(t+2) computed
+    // into `nx`; O += V(t) P(t); S(t+1) in `cu` goes through the softmax into
+    // P(t+1).  Steps alternate between an S step (two MFMAs: contraction step
+    // kc of M-block mb) and a PV step (two MFMAs: columns cc, d-block md); the
+    // LDS fragments of a step are read kPF steps ahead; slice g of the softmax
+    // follows step 2g.  Columns cc of P(t+1) are packed once the PV MFMAs
+    // reading those of P(t) are issued and their exponentials exist.
+    constexpr int kHalf = C::KC * kMB;   // S steps = PV steps = kHalf
+    constexpr int kPF = SQKV_PF;
+    auto body = [&](auto R, f32x16_t (&nx)[kMB][2], f32x16_t (&cu)[kMB][2]) {
       constexpr int r = decltype(R)::value;
       constexpr int ks = (r + 2) % kStages, vs = r;
       wait_dma_and_sync<4 * C::NL>();    // K(t+2), V(t) landed
+#ifdef SQKV_PINQ
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int kc = 0; kc < C::KC; ++kc) pin(qf[nb][kc]);
+#endif
       issue_k(d5, (r + 5) % kStages);
       issue_v(d3, (r + 3) % kStages);
       resc = false;
-      u32x4_t kf = kfrag(0, Step<ks>{});
-      bf16x8_t vf;
+      u32x4_t kfr[kHalf];
+      bf16x8_t vfr[kHalf];
+      // S step i: kc = i / kMB, mb = i % kMB.  PV step i: cc = i / MD, md = i % MD.
+      auto read = [&](int g) {
+        if (g >= 2 * kHalf) return;
+        const int i = g >> 1;
+        if ((g & 1) == 0) kfr[i] = kfrag(i / kMB, i % kMB, Step<ks>{});
+        else vfr[i] = vfrag(i / C::MD, i % C::MD, Step<vs>{});
+      };
+      int packed = 0;
 #pragma unroll
-      for (int kc = 0; kc < C::KC; ++kc) {
-        u32x4_t kn;
-        if (kc + 1 < C::KC) kn = kfrag(kc + 1, Step<ks>{});
-        else vf = vfrag(0, 0, Step<vs>{});
-        mfma_s(nx, kf, kc);
-        softmax_slice(cu, kc);
+      for (int g = 0; g < kPF; ++g) read(g);
+#pragma unroll
+      for (int g = 0; g < 2 * kHalf; ++g) {
+        read(g + kPF);
+        const int i = g >> 1;
+        if ((g & 1) == 0) {
+          mfma_s(nx, kfr[i], i / kMB, i % kMB);
+        } else {
+          mfma_pv(vfr[i], i / C::MD, i % C::MD);
+          // columns cc are free once PV step (cc+1)*MD - 1 is issued; their
+          // exponentials come from slice 3 + 2*cc + 1 (run after step 2*slice)
+          while (packed < kNCC && (packed + 1) * C::MD <= i + 1 && 3 + 2 * packed + 1 < (g >> 1)) {
+            pack(cu, packed);
+            ++packed;
+          }
+        }
+        if ((g & 1) == 0 && (g >> 1) < kSlices) softmax_slice(cu, g >> 1);
         __builtin_amdgcn_sched_barrier(0);
-        kf = kn;
       }
 #pragma unroll
-      for (int i = 0; i < 2 * C::MD; ++i) {
-        const int cc = i / C::MD, md = i % C::MD;
-        bf16x8_t vn;
-        if (i + 1 < 2 * C::MD) vn = vfrag((i + 1) / C::MD, (i + 1) % C::MD, Step<vs>{});
-        mfma_pv(vf, cc, md);
-        if (C::KC + i < kSlices) softmax_slice(cu, C::KC + i);
-        if (i == kPack0Step) pack(cu, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        vf = vn;
+      for (int k = kHalf; k < kSlices; ++k) softmax_slice(cu, k);
+      while (packed < kNCC) {
+        pack(cu, packed);
+        ++packed;
       }
-#pragma unroll
-      for (int k = C::KC + 2 * C::MD; k < kSlices; ++k) softmax_slice(cu, k);
-      if (kPack0Step >= 2 * C::MD) pack(cu, 0);
-      pack(cu, 1);
       if (resc) rescale();
       mask(nx, d2);
       d2 = d3;
