@@ -49,6 +49,7 @@
 //   need them; tiles entirely in the future of the whole block are never
 //   fetched.
 #include <type_traits>
+#include <utility>
 
 #include "attn_common.h"
 
@@ -211,6 +212,16 @@ struct TileWalk {
 template <int R>
 using Step = std::integral_constant<int, R>;
 
+// f(Step<0>{}), ..., f(Step<N-1>{}) as straight-line code.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(Step<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 template <int D>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -365,85 +376,81 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   bool resc = false;
   const float c = p.scale_log2;
 
+  // ---- the softmax of one tile in small work groups ------------------------------
   // P columns cc (16 keys of the P V contraction step cc) are accumulator
-  // elements 8*(cc%2) .. +7 of block mb = cc/2.
-  // Slices of the softmax of tile s, each short and free of long dependency
-  // chains (the wave issues in order, so a chain would stall the MFMAs too):
-  //   0  in-lane max of both query blocks as trees of v_max3
-  //   1  max with the other half of the keys, scaled, compared to the
-  //      running max
-  //   2  new running max (moved only if some lane needs it), alpha, -max
-  //   3 + 2*cc + nb  the 8 exponentials of columns cc of query block nb and
-  //      their sum as a tree
-  //   last  the row sums
-  constexpr int kSlices = 3 + 2 * kNCC + 1;
-  float mxs[2], lpart[2][kNCC];
+  // elements 8*cc .. 8*cc+7 (one 32-key block per tile).  The groups are
+  // spread one or two per MFMA so that the VALU work of a tile hides under
+  // the MFMAs of the next two; none of them is a long dependency chain (the
+  // wave issues in order, so a chain would hold back the MFMAs too).
+  static_assert(kMB == 1, "the group schedule assumes one 32-key block per tile");
+  float mpart[2][3], mxs[2], lpart[2][kNCC];
   bool upd[2];
-  auto max16 = [&](const f32x16_t& v, float x) {
-    // max of x and 16 values, depth 3
-    const float a0 = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
-    const float a1 = __builtin_fmaxf(__builtin_fmaxf(v[3], v[4]), v[5]);
-    const float a2 = __builtin_fmaxf(__builtin_fmaxf(v[6], v[7]), v[8]);
-    const float a3 = __builtin_fmaxf(__builtin_fmaxf(v[9], v[10]), v[11]);
-    const float a4 = __builtin_fmaxf(__builtin_fmaxf(v[12], v[13]), v[14]);
-    const float a5 = __builtin_fmaxf(__builtin_fmaxf(v[15], x), a0);
-    return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(a1, a2), a3), __builtin_fmaxf(a4, a5));
-  };
-  auto softmax_slice = [&](f32x16_t (&s)[kMB][2], int k) {
-    if (k == 0) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) mx = max16(s[mb][nb], mx);
-        pmax[nb] = mx;
+  auto sm_group = [&](f32x16_t (&s)[kMB][2], int g) {
+    if (g < 6) {                       // partial maxima, query block g % 2
+      const int nb = g & 1, part = g >> 1;
+      const f32x16_t& v = s[0][nb];
+      if (part == 0) {
+        mpart[nb][0] = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
+        mpart[nb][1] = __builtin_fmaxf(__builtin_fmaxf(v[3], v[4]), v[5]);
+      } else if (part == 1) {
+        mpart[nb][2] = __builtin_fmaxf(__builtin_fmaxf(v[6], v[7]), v[8]);
+        mpart[nb][0] = __builtin_fmaxf(__builtin_fmaxf(v[9], v[10]), mpart[nb][0]);
+      } else {
+        mpart[nb][1] = __builtin_fmaxf(__builtin_fmaxf(v[11], v[12]), mpart[nb][1]);
+        mpart[nb][2] = __builtin_fmaxf(__builtin_fmaxf(v[13], v[14]), mpart[nb][2]);
+        pmax[nb] = __builtin_fmaxf(__builtin_fmaxf(v[15], mpart[nb][0]),
+                                   __builtin_fmaxf(mpart[nb][1], mpart[nb][2]));
       }
-    } else if (k == 1) {
+    } else if (g < 8) {                // the other half of the keys; compare
+      const int nb = g - 6;
+      mxs[nb] = max_half(pmax[nb]) * c;
+      upd[nb] = mxs[nb] > m_run[nb] + kRescaleLog2;
+    } else if (g < 10) {               // move the running max if any lane needs it
+      const int nb = g - 8;
+      const bool u = __any(upd[nb]);
+      const float mn = u ? __builtin_fmaxf(m_run[nb], mxs[nb]) : m_run[nb];
+      alpha[nb] = (mn == m_run[nb]) ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - mn);
+      resc = resc || u;
+      m_run[nb] = mn;
+      mneg[nb] = (mn == kNegInf) ? 0.f : -mn;
+    } else if (g < 10 + 4 * kNCC) {    // 4 exponentials: columns cc, block nb, half
+      const int e = g - 10, cc = e >> 2, nb = (e >> 1) & 1, j0 = 8 * cc + 4 * (e & 1);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        mxs[nb] = max_half(pmax[nb]) * c;
-        upd[nb] = mxs[nb] > m_run[nb] + kRescaleLog2;
-      }
-    } else if (k == 2) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const bool u = __any(upd[nb]);
-        const float mn = u ? __builtin_fmaxf(m_run[nb], mxs[nb]) : m_run[nb];
-        alpha[nb] = (mn == m_run[nb]) ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - mn);
-        resc = resc || u;
-        m_run[nb] = mn;
-        mneg[nb] = (mn == kNegInf) ? 0.f : -mn;
-      }
-    } else if (k < 3 + 2 * kNCC) {
-      const int cc = (k - 3) >> 1, nb = (k - 3) & 1;
-      const int mb = cc >> 1, j0 = 8 * (cc & 1);
-      float e[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        e[j] = __builtin_amdgcn_exp2f(fmaf(s[mb][nb][j0 + j], c, mneg[nb]));
-        s[mb][nb][j0 + j] = e[j];
-      }
-      lpart[nb][cc] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-    } else {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        float t = lpart[nb][0];
-#pragma unroll
-        for (int cc = 1; cc < kNCC; ++cc) t += lpart[nb][cc];
-        l_run[nb] = fmaf(l_run[nb], alpha[nb], t);
-        pin(l_run[nb]);
-      }
+      for (int j = j0; j < j0 + 4; ++j) s[0][nb][j] = __builtin_amdgcn_exp2f(fmaf(s[0][nb][j], c, mneg[nb]));
     }
   };
+  constexpr int kGroups = 10 + 4 * kNCC;
 
-  u32x4_t pf[2][kNCC];   // bf16 weights: B operand of O^T = V^T P^T, [nb][cc]
-  auto pack = [&](const f32x16_t (&s)[kMB][2], int cc) {
-    const int mb = cc >> 1, j0 = 8 * (cc & 1);
+  // bf16 weights: B operand of O^T = V^T P^T, [nb][cc]; the row sum is taken
+  // over the weights as they enter that product (rounded to bf16), two per
+  // v_dot2_f32_bf16 against (1, 1).
+  // Two buffers: tile t's weights are read by the P V MFMAs of iteration t
+  // while tile t+1's are packed (buffer = tile parity).
+  u32x4_t pf[2][2][kNCC];
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  auto pack = [&](int buf, const f32x16_t (&s)[kMB][2], int cc, int nb) {
+    const int j0 = 8 * cc;
+    u32x4_t& w4 = pf[buf][nb][cc];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) w4[w] = pack_bf16x2(s[0][nb][j0 + 2 * w], s[0][nb][j0 + 2 * w + 1]);
+    pin(w4);
+    // (pairs taken with shufflevector: bit-casting single 32-bit elements of
+    // w4 to bf16x2 was miscompiled into reads of element 0 only)
+    const bf16x8_t p8 = as_bf16x8(w4);
+    float a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 0, 1), ones, 0.f, false);
+    float a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 2, 3), ones, 0.f, false);
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 4, 5), ones, a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 6, 7), ones, a1, false);
+    lpart[nb][cc] = a0 + a1;
+  };
+  auto row_sums = [&]() {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
+      float t = lpart[nb][0];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) pf[nb][cc][w] = pack_bf16x2(s[mb][nb][j0 + 2 * w], s[mb][nb][j0 + 2 * w + 1]);
-      pin(pf[nb][cc]);
+      for (int cc = 1; cc < kNCC; ++cc) t += lpart[nb][cc];
+      l_run[nb] = fmaf(l_run[nb], alpha[nb], t);
+      pin(l_run[nb]);
     }
   };
   // O *= alpha when the running max moved (rare).  O lives in accumulation
@@ -480,16 +487,16 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     const i16x4_t up = lds_tr16(a + 8 * C::ROWB);
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  auto mfma_pv = [&](bf16x8_t vf, int cc, int md) {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-      oacc[md][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pf[nb][cc]), oacc[md][nb], 0, 0, 0);
-  };
-  auto pv = [&](auto stage) {
+  auto pv = [&](int buf, auto stage) {
 #pragma unroll
     for (int cc = 0; cc < kNCC; ++cc)
 #pragma unroll
-      for (int md = 0; md < C::MD; ++md) mfma_pv(vfrag(cc, md, stage), cc, md);
+      for (int md = 0; md < C::MD; ++md) {
+        const bf16x8_t vf = vfrag(cc, md, stage);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          oacc[md][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pf[buf][nb][cc]), oacc[md][nb], 0, 0, 0);
+      }
   };
 
   // ---- main loop -----------------------------------------------------------------
@@ -503,6 +510,24 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   const int ntl_full = (p.n_k + kBN - 1) / kBN;
   const int T = ntl0 == 0 ? 0 : ntl0 + (p.nseg - 1) * ntl_full;
   TileWalk walk{0, -1, ntl0, (int)lim0, ntl_full, p.n_k, p.nseg};
+
+  // One loop iteration issues 2*NS MFMAs in slots: even slot 2m is score MFMA
+  // m (contraction step kc = m/2, query block m%2), odd slot 2m+1 is P V MFMA
+  // m (columns cc = m/(2*MD), d-block md = (m/2)%MD, query block m%2).  K
+  // fragment f = kc is first needed at slot 4f, V fragment v = cc*MD + md at
+  // slot 4v + 1; both are read kLead slots earlier (the first ones at the end
+  // of the previous iteration, after its barrier).
+  constexpr int kNS = 2 * C::KC;       // score MFMAs per tile (= P V MFMAs)
+  constexpr int kSlots = 2 * kNS;
+  constexpr int kLead = 6;
+  constexpr int kPre = (kLead + 3) / 4;   // fragments of each kind read ahead
+  // softmax group g goes to slot kSlotOf(g); the packs (columns cc, block nb)
+  // follow the exponentials they read
+  constexpr auto kSlotOfGroup = [](int g) { return (g * kSlots) / (kGroups + 2 * kNCC + 2); };
+  constexpr auto kSlotOfPack = [](int cc, int nb) {
+    return ((10 + 4 * cc + 2 * nb + 2 + 2 * cc + nb) * kSlots) / (kGroups + 2 * kNCC + 2);
+  };
+
   if (T > 0) {
     f32x16_t sa[kMB][2], sb[kMB][2];
     const Tile t0 = walk.next(), t1 = walk.next(), t2 = walk.next(), t3 = walk.next();
@@ -519,79 +544,80 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     mask(sa, t0);
     mask(sb, t1);
 #pragma unroll
-    for (int k = 0; k < kSlices; ++k) softmax_slice(sa, k);   // O is still zero: no rescale
+    for (int g = 0; g < kGroups; ++g) sm_group(sa, g);   // O is still zero: no rescale
 #pragma unroll
-    for (int cc = 0; cc < kNCC; ++cc) pack(sa, cc);
+    for (int cc = 0; cc < kNCC; ++cc)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) pack(0, sa, cc, nb);
+    row_sums();
     lds_reads_done_sync();               // K stage 0 is free
     issue_k(t4, 0);
     issue_v(t2, 2);
     // tiles t+2 .. t+5 at the top of iteration t
     Tile d2 = t2, d3 = t3, d4 = t4, d5 = walk.next();
 
+    u32x4_t kfr[C::KC];
+    bf16x8_t vfr[kNCC * C::MD];
+    auto read_k = [&](int f, auto stage) { kfr[f] = kfrag(f, 0, stage); };
+    auto read_v = [&](int v, auto stage) { vfr[v] = vfrag(v / C::MD, v % C::MD, stage); };
+    // first fragments of iteration 0 (K(2) in stage 2, V(0) in stage 0)
+    wait_dma_and_sync<4 * C::NL>();
+#pragma unroll
+    for (int f = 0; f < kPre; ++f) {
+      read_k(f, Step<2>{});
+      read_v(f, Step<0>{});
+    }
+
     // Iteration t = 4k + R: K(t+5) and V(t+3) are fetched; S(t+2) computed
     // into `nx`; O += V(t) P(t); S(t+1) in `cu` goes through the softmax into
-    // P(t+1).  Steps alternate between an S step (two MFMAs: contraction step
-    // kc of M-block mb) and a PV step (two MFMAs: columns cc, d-block md); the
-    // LDS fragments of a step are read kPF steps ahead; slice g of the softmax
-    // follows step 2g.  Columns cc of P(t+1) are packed once the PV MFMAs
-    // reading those of P(t) are issued and their exponentials exist.
-    constexpr int kHalf = C::KC * kMB;   // S steps = PV steps = kHalf
-    constexpr int kPF = SQKV_PF;
+    // P(t+1).  It ends by waiting for K(t+3), V(t+1) and reading their first
+    // fragments.
     auto body = [&](auto R, f32x16_t (&nx)[kMB][2], f32x16_t (&cu)[kMB][2]) {
       constexpr int r = decltype(R)::value;
       constexpr int ks = (r + 2) % kStages, vs = r;
-      wait_dma_and_sync<4 * C::NL>();    // K(t+2), V(t) landed
-#ifdef SQKV_PINQ
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int kc = 0; kc < C::KC; ++kc) pin(qf[nb][kc]);
-#endif
       issue_k(d5, (r + 5) % kStages);
       issue_v(d3, (r + 3) % kStages);
       resc = false;
-      u32x4_t kfr[kHalf];
-      bf16x8_t vfr[kHalf];
-      // S step i: kc = i / kMB, mb = i % kMB.  PV step i: cc = i / MD, md = i % MD.
-      auto read = [&](int g) {
-        if (g >= 2 * kHalf) return;
-        const int i = g >> 1;
-        if ((g & 1) == 0) kfr[i] = kfrag(i / kMB, i % kMB, Step<ks>{});
-        else vfr[i] = vfrag(i / C::MD, i % C::MD, Step<vs>{});
-      };
-      int packed = 0;
-#pragma unroll
-      for (int g = 0; g < kPF; ++g) read(g);
-#pragma unroll
-      for (int g = 0; g < 2 * kHalf; ++g) {
-        read(g + kPF);
-        const int i = g >> 1;
-        if ((g & 1) == 0) {
-          mfma_s(nx, kfr[i], i / kMB, i % kMB);
+      static_for<kSlots>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        // fragments needed kLead slots from now
+        constexpr int ahead = i + kLead;
+        if constexpr ((ahead & 3) == 0 && ahead / 4 < C::KC && ahead / 4 >= kPre) read_k(ahead / 4, Step<ks>{});
+        if constexpr ((ahead & 3) == 1 && ahead / 4 < kNCC * C::MD && ahead / 4 >= kPre)
+          read_v(ahead / 4, Step<vs>{});
+        constexpr int m = i >> 1, nb = m & 1;
+        if constexpr ((i & 1) == 0) {
+          constexpr int kc = m >> 1;
+          const f32x16_t z = {};
+          nx[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kfr[kc]), as_bf16x8(qf[nb][kc]),
+                                                              kc == 0 ? z : nx[0][nb], 0, 0, 0);
         } else {
-          mfma_pv(vfr[i], i / C::MD, i % C::MD);
-          // columns cc are free once PV step (cc+1)*MD - 1 is issued; their
-          // exponentials come from slice 3 + 2*cc + 1 (run after step 2*slice)
-          while (packed < kNCC && (packed + 1) * C::MD <= i + 1 && 3 + 2 * packed + 1 < (g >> 1)) {
-            pack(cu, packed);
-            ++packed;
-          }
+          constexpr int v = m >> 1, cc = v / C::MD, md = v % C::MD;
+          oacc[md][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[v], as_bf16x8(pf[r & 1][nb][cc]),
+                                                                 oacc[md][nb], 0, 0, 0);
         }
-        if ((g & 1) == 0 && (g >> 1) < kSlices) softmax_slice(cu, g >> 1);
+        static_for<kGroups>([&](auto G) {
+          if constexpr (kSlotOfGroup(decltype(G)::value) == i) sm_group(cu, decltype(G)::value);
+        });
+        static_for<2 * kNCC>([&](auto Q) {
+          constexpr int cc = decltype(Q)::value >> 1, q = decltype(Q)::value & 1;
+          if constexpr (kSlotOfPack(cc, q) == i) pack((r + 1) & 1, cu, cc, q);
+        });
         __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int k = kHalf; k < kSlices; ++k) softmax_slice(cu, k);
-      while (packed < kNCC) {
-        pack(cu, packed);
-        ++packed;
-      }
+      });
+      row_sums();
       if (resc) rescale();
       mask(nx, d2);
       d2 = d3;
       d3 = d4;
       d4 = d5;
       d5 = walk.next();
+      wait_dma_and_sync<4 * C::NL>();    // K(t+3), V(t+1) landed
+#pragma unroll
+      for (int f = 0; f < kPre; ++f) {
+        read_k(f, Step<(r + 3) % kStages>{});
+        read_v(f, Step<(r + 1) % kStages>{});
+      }
     };
     // T - 1 iterations, padded to a multiple of 4 with empty tiles
     const int iters = (T - 1 + 3) & ~3;
@@ -601,8 +627,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
       body(Step<2>{}, sa, sb);
       body(Step<3>{}, sb, sa);
     }
-    wait_dma_and_sync<4 * C::NL>();      // V of the last (padded) tile landed
-    pv(Step<0>{});
+    pv(0, Step<0>{});                    // V of the last (padded) tile landed above
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no DMA may outlive the workgroup's LDS
 
