@@ -9,20 +9,22 @@
 // (max, sum, output) state stays in registers across chunk boundaries.
 //
 // Design (gfx950, wave64, v_mfma_f32_32x32x16_bf16):
-// * A workgroup of 4 wavefronts owns 256 query rows of one (batch, head); each
-//   wavefront owns 64 rows and keeps their Q fragments in registers.  Keys
-//   are processed in tiles of 64 (two 32-key MFMA blocks); a tile's scores
-//   take 64 registers per lane and two tiles are in flight at once.
-// * Scores are computed transposed, S^T = K Q^T (keys on the MFMA M axis,
-//   queries on N).  In the 32x32 accumulator layout a lane then holds 16 keys
-//   of ONE query, so the row max and row sum are in-lane reductions plus one
-//   v_permlane32_swap with the lane 32 apart.
+// * A workgroup of 8 wavefronts (two per SIMD) owns 256 query rows of one
+//   (batch, head); each wavefront owns 32 rows and keeps their Q fragments in
+//   registers.  Two waves per SIMD let the hardware overlap one wave's LDS
+//   reads and softmax arithmetic with the other wave's MFMAs; a wave fits in
+//   256 registers.
+// * Keys are processed in tiles of 32.  Scores are computed transposed,
+//   S^T = K Q^T (keys on the MFMA M axis, queries on N): in the 32x32
+//   accumulator layout a lane holds 16 keys of ONE query, so the row max and
+//   row sum are in-lane reductions plus one v_permlane32_swap with the lane 32
+//   apart.
 // * Those accumulators, rounded to bf16, are directly the B operand of
 //   O^T = V^T P^T; the key order inside a 16-key contraction step follows the
 //   accumulator layout and the V^T operand is read in that order with
 //   ds_read_b64_tr_b16 (a 4x16 block of V rows transposed across 16 lanes),
 //   so V is stored in LDS exactly as it sits in memory.
-// * K and V tiles (64 keys x d) are copied global -> LDS by buffer_load ...
+// * K and V tiles (32 keys x d) are copied global -> LDS by buffer_load ...
 //   lds (16 bytes per lane, no register staging); rows past the end of a
 //   chunk fall outside the buffer's range and arrive as zeros.  16-byte chunks
 //   of a row are XOR-swizzled so that the K fragment reads (ds_read_b128) and
@@ -30,21 +32,23 @@
 // * Software pipeline, per wavefront and iteration t:
 //       S(t+2) = K(t+2) Q^T      (MFMA)
 //       O     += V(t)^T P(t)^T   (MFMA)
-//       softmax of S(t+1)        (VALU / transcendental, overlaps the MFMAs)
-//   The three streams are interleaved by hand: S steps and PV steps
-//   alternate, two MFMAs each, with a slice of the softmax after each, fenced
-//   with sched_barrier so the compiler keeps that order.  K and V tiles go through four LDS stages each
-//   and are fetched three iterations before use.  The loop is unrolled by four
-//   so that every stage address is an instruction immediate.  The DMA loads are inline assembly,
-//   their completion counted with explicit s_waitcnt vmcnt, because the
-//   compiler would otherwise wait for every in-flight LDS DMA before each LDS
-//   read.  The tile count is padded to 4k+1 with empty tiles (fully masked,
+//       softmax of S(t+1)        (VALU / transcendental)
+//   Score and P V MFMAs alternate one at a time with small groups of softmax
+//   work between them, fenced with sched_barrier so the compiler keeps that
+//   order; LDS fragments are read a few MFMAs ahead.  K and V tiles go
+//   through four LDS stages each and are fetched three iterations before use;
+//   the loop is unrolled by four so that every stage address is an
+//   instruction immediate.  The DMA loads are inline assembly, their
+//   completion counted with explicit s_waitcnt vmcnt, because the compiler
+//   would otherwise wait for every in-flight LDS DMA before each LDS read.
+//   The tile count is padded to 4k+1 with empty tiles (fully masked,
 //   zero-filled), which contribute nothing.
 // * Softmax runs in base 2 with scale*log2(e) folded into one FMA.  The
 //   running maximum is only moved (and O rescaled) when a tile raises it by
 //   more than kRescaleLog2; weights are taken against the slightly stale
 //   maximum in between, which leaves the normalised result unchanged and
-//   bounds weights by 2^kRescaleLog2.
+//   bounds weights by 2^kRescaleLog2.  The row sum is taken over the weights
+//   as they enter the P V product (rounded to bf16).
 // * Masks (causal diagonal, ragged chunk end) are applied only to tiles that
 //   need them; tiles entirely in the future of the whole block are never
 //   fetched.
@@ -65,21 +69,14 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 #define SQKV_LDS __attribute__((address_space(3)))
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kQW = 64;              // query rows per wavefront
+constexpr int kQW = 32;              // query rows per wavefront
 constexpr int kBM = kQW * kWaves;    // query rows per workgroup
-#ifndef SQKV_MB
-#define SQKV_MB 1
-#endif
-constexpr int kMB = SQKV_MB;         // 32-key MFMA blocks per tile
-constexpr int kBN = 32 * kMB;        // keys per tile
-constexpr int kNCC = 2 * kMB;        // 16-key contraction steps of P V per tile
+constexpr int kBN = 32;              // keys per tile
+constexpr int kNCC = kBN / 16;       // 16-key contraction steps of P V per tile
 constexpr int kStages = 4;           // LDS stages per tensor (= loop unroll)
 constexpr float kRescaleLog2 = 8.0f;
-#ifndef SQKV_PF
-#define SQKV_PF 2
-#endif
 
 template <int D>
 struct Cfg {
@@ -89,10 +86,16 @@ struct Cfg {
   static constexpr int ROWB = D * 2;                     // bytes per row
   static constexpr int TILE = kBN * ROWB;                // bytes per K or V tile
   static constexpr int RPW = 1024 / ROWB;                // rows per wave-wide 1 KiB load
-  static constexpr int NL = TILE / (1024 * kWaves);      // loads per thread per tile
+  static constexpr int NLT = TILE / 1024;                // wave-wide loads per tile
+  // Every wave issues the same number of loads per tile (its vmcnt
+  // bookkeeping is then uniform); with fewer loads than waves the spare
+  // waves issue an empty load into a dummy 1 KiB of LDS.
+  static constexpr int NL = NLT >= kWaves ? NLT / kWaves : 1;
   static constexpr int K_LDS = 0;                        // kStages K tiles
   static constexpr int V_LDS = kStages * TILE;           // kStages V tiles
-  static constexpr int LDS_BYTES = 2 * kStages * TILE;
+  static constexpr int DUMMY = 2 * kStages * TILE;       // sink of the empty loads
+  static constexpr int LDS_BYTES = DUMMY + (NLT < kWaves ? 1024 : 0);
+  static_assert(NLT % kWaves == 0 || NLT < kWaves, "tile loads must spread evenly over the waves");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -224,7 +227,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 template <int D>
 __global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bf16_kernel(AttnParams p, int n_qtiles) {
   using C = Cfg<D>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -260,23 +263,22 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   const int64_t k_csb = p.k_cs * 2, v_csb = p.v_cs * 2;             // chunk strides in bytes
 
   // ---- Q fragments (B operand of S^T = K Q^T) -------------------------------
-  // lane holds Q[row = qw0 + 32*nb + l32][16*kc + 8*hi .. +7]
-  u32x4_t qf[2][C::KC];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int row = qw0 + 32 * nb + l32;
+  // lane holds Q[row = qw0 + l32][16*kc + 8*hi .. +7]
+  u32x4_t qf[C::KC];
+  {
+    const int row = qw0 + l32;
     const bool ok = row < p.n_q;
     const uint16_t* src = qg + (int64_t)(ok ? row : 0) * p.q_sn + 8 * hi;
 #pragma unroll
     for (int kc = 0; kc < C::KC; ++kc) {
       const u32x4_t z = {0u, 0u, 0u, 0u};
-      qf[nb][kc] = ok ? *reinterpret_cast<const u32x4_t*>(src + 16 * kc) : z;
+      qf[kc] = ok ? *reinterpret_cast<const u32x4_t*>(src + 16 * kc) : z;
     }
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);   // Q is in registers before any DMA is counted
 
   // ---- per-lane LDS offsets ---------------------------------------------------
-  // K fragment (A operand of S^T): row 32*mb + l32, 16-byte chunk 2*kc + hi
+  // K fragment (A operand of S^T): row l32, 16-byte chunk 2*kc + hi
   uint32_t kofs[C::KC];
 #pragma unroll
   for (int kc = 0; kc < C::KC; ++kc)
@@ -291,8 +293,9 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     const int c = 4 * md + 2 * ((lane >> 4) & 1) + ((a16 & 3) >> 1);
     vofs[md] = lds0 + C::V_LDS + r * C::ROWB + ((c ^ swz_v<D>(r)) * 16) + (a16 & 1) * 8;
   }
-  // DMA source offsets: lane fills LDS row r0 + lane/NCH, chunk position
-  // lane%NCH, so it reads source chunk (lane%NCH) ^ swizzle(row)
+  // DMA: wave-wide load i of a tile fills rows (i*kWaves + wave)*RPW ..; lane
+  // fills row r0 + lane/NCH, chunk position lane%NCH, so it reads source chunk
+  // (lane%NCH) ^ swizzle(row).  (r0 is a multiple of the swizzle periods.)
   const int lrow = lane / C::NCH;
   const uint32_t dk = (uint32_t)(lrow * k_snb) + (((lane % C::NCH) ^ swz_k<D>(wave * C::RPW + lrow)) * 16);
   const uint32_t dv = (uint32_t)(lrow * v_snb) + (((lane % C::NCH) ^ swz_v<D>(lrow)) * 16);
@@ -307,35 +310,28 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     const unsigned char* tb = hbase + (chunk_of(t.s) * csb + (int64_t)(t.tt * kBN) * snb);
 #pragma unroll
     for (int i = 0; i < C::NL; ++i) {
-      const int r0 = (i * kWaves + wave) * C::RPW;
+      const int blk = i * kWaves + wave;
+      const int r0 = blk * C::RPW;
       const int rows = t.nvalid - r0;
-      const uint32_t bytes = rows > 0 ? (uint32_t)(rows * snb) : 0u;
-      dma16(voff, buffer_rsrc(tb + r0 * snb, bytes), stage + r0 * C::ROWB);
+      const bool real = blk < C::NLT;
+      const uint32_t bytes = (real && rows > 0) ? (uint32_t)(rows * snb) : 0u;
+      dma16(voff, buffer_rsrc(tb + (real ? r0 * snb : 0), bytes), real ? stage + r0 * C::ROWB : lds0 + C::DUMMY);
     }
   };
   auto issue_k = [&](const Tile& t, int stage) { issue(kg, k_csb, k_snb, t, lds0 + C::K_LDS + stage * C::TILE, dk); };
   auto issue_v = [&](const Tile& t, int stage) { issue(vg, v_csb, v_snb, t, lds0 + C::V_LDS + stage * C::TILE, dv); };
 
   // ---- scores and masks --------------------------------------------------------
-  // S^T tile: kBN keys (kMB M-blocks of 32) x 64 queries (2 N-blocks of 32);
-  // accumulator element j of block (mb, nb) holds key 32*mb + 8*(j/4) + 4*hi +
-  // j%4 of query qw0 + 32*nb + l32
-  auto kfrag = [&](int kc, int mb, auto stage) {
-    return lds_b128(kofs[kc] + decltype(stage)::value * C::TILE + mb * 32 * C::ROWB);
+  // S^T tile: 32 keys (M) x the wave's 32 queries (N); accumulator element j
+  // holds key 8*(j/4) + 4*hi + j%4 of query qw0 + l32
+  auto kfrag = [&](int kc, auto stage) { return lds_b128(kofs[kc] + decltype(stage)::value * C::TILE); };
+  auto mfma_s = [&](f32x16_t& s, u32x4_t kf, int kc) {
+    const f32x16_t z = {};
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[kc]), kc == 0 ? z : s, 0, 0, 0);
   };
-  auto mfma_s = [&](f32x16_t (&s)[kMB][2], u32x4_t kf, int kc, int mb) {
+  auto scores = [&](f32x16_t& s, auto stage) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const f32x16_t z = {};
-      s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[nb][kc]),
-                                                          kc == 0 ? z : s[mb][nb], 0, 0, 0);
-    }
-  };
-  auto scores = [&](f32x16_t (&s)[kMB][2], auto stage) {
-#pragma unroll
-    for (int kc = 0; kc < C::KC; ++kc)
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) mfma_s(s, kfrag(kc, mb, stage), kc, mb);
+    for (int kc = 0; kc < C::KC; ++kc) mfma_s(s, kfrag(kc, stage), kc);
   };
 
   // Causal masks only touch tiles of the first chunk of the visit (the rank's
@@ -344,95 +340,74 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   const int64_t qpos_w = p.q_pos0 + qw0;
   const int64_t kpos_own = p.k_pos0 + (int64_t)p.rank * p.k_posstride;
   const int tt_mask = (int)max((int64_t)0, (qpos_w - kpos_own - kBN + 1 + kBN) / kBN);
-  auto mask = [&](f32x16_t (&s)[kMB][2], const Tile& t) {
+  auto mask = [&](f32x16_t& s, const Tile& t) {
     const bool diag = p.causal && t.s == 0 && t.tt >= tt_mask;
     if (!(t.nvalid < kBN || diag)) return;
     const int64_t kpos = kpos_own + (int64_t)t.tt * kBN;   // only read for the own chunk
+    int64_t rel = qpos_w + l32 - kpos;                     // last visible key of the tile
+    if (!diag || rel > kBN) rel = kBN;
+    const int lastk = (int)min(rel, (int64_t)t.nvalid - 1);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      int64_t rel = qpos_w + 32 * nb + l32 - kpos;   // last visible key of the tile
-      if (!diag || rel > kBN) rel = kBN;
-      const int lastk = (int)min(rel, (int64_t)t.nvalid - 1);
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int u = 32 * mb + 8 * (j >> 2) + 4 * hi + (j & 3);
-          if (u > lastk) s[mb][nb][j] = kNegInf;
-        }
+    for (int j = 0; j < 16; ++j) {
+      const int u = 8 * (j >> 2) + 4 * hi + (j & 3);
+      if (u > lastk) s[j] = kNegInf;
     }
   };
 
-  // ---- online softmax, in slices that interleave with the MFMAs ----------------
-  f32x16_t oacc[C::MD][2];
+  // ---- online softmax state --------------------------------------------------
+  f32x16_t oacc[C::MD];
 #pragma unroll
-  for (int md = 0; md < C::MD; ++md)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) oacc[md][nb] = (f32x16_t){};
-  float m_run[2] = {kNegInf, kNegInf};  // running max, base-2 units
-  float l_run[2] = {0.f, 0.f};          // this lane's half of the row sum
-  float alpha[2] = {1.f, 1.f};
-  float pmax[2], mneg[2];
-  bool resc = false;
+  for (int md = 0; md < C::MD; ++md) oacc[md] = (f32x16_t){};
+  float m_run = kNegInf;   // running max, base-2 units
+  float l_run = 0.f;       // this lane's half of the row sum
+  float alpha = 1.f;
+  float mpart[3], pmax = kNegInf, mxs = kNegInf, mneg = 0.f, lpart[kNCC];
+  bool upd = false, resc = false;
   const float c = p.scale_log2;
 
   // ---- the softmax of one tile in small work groups ------------------------------
   // P columns cc (16 keys of the P V contraction step cc) are accumulator
-  // elements 8*cc .. 8*cc+7 (one 32-key block per tile).  The groups are
-  // spread one or two per MFMA so that the VALU work of a tile hides under
-  // the MFMAs of the next two; none of them is a long dependency chain (the
-  // wave issues in order, so a chain would hold back the MFMAs too).
-  static_assert(kMB == 1, "the group schedule assumes one 32-key block per tile");
-  float mpart[2][3], mxs[2], lpart[2][kNCC];
-  bool upd[2];
-  auto sm_group = [&](f32x16_t (&s)[kMB][2], int g) {
-    if (g < 6) {                       // partial maxima, query block g % 2
-      const int nb = g & 1, part = g >> 1;
-      const f32x16_t& v = s[0][nb];
-      if (part == 0) {
-        mpart[nb][0] = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
-        mpart[nb][1] = __builtin_fmaxf(__builtin_fmaxf(v[3], v[4]), v[5]);
-      } else if (part == 1) {
-        mpart[nb][2] = __builtin_fmaxf(__builtin_fmaxf(v[6], v[7]), v[8]);
-        mpart[nb][0] = __builtin_fmaxf(__builtin_fmaxf(v[9], v[10]), mpart[nb][0]);
-      } else {
-        mpart[nb][1] = __builtin_fmaxf(__builtin_fmaxf(v[11], v[12]), mpart[nb][1]);
-        mpart[nb][2] = __builtin_fmaxf(__builtin_fmaxf(v[13], v[14]), mpart[nb][2]);
-        pmax[nb] = __builtin_fmaxf(__builtin_fmaxf(v[15], mpart[nb][0]),
-                                   __builtin_fmaxf(mpart[nb][1], mpart[nb][2]));
-      }
-    } else if (g < 8) {                // the other half of the keys; compare
-      const int nb = g - 6;
-      mxs[nb] = max_half(pmax[nb]) * c;
-      upd[nb] = mxs[nb] > m_run[nb] + kRescaleLog2;
-    } else if (g < 10) {               // move the running max if any lane needs it
-      const int nb = g - 8;
-      const bool u = __any(upd[nb]);
-      const float mn = u ? __builtin_fmaxf(m_run[nb], mxs[nb]) : m_run[nb];
-      alpha[nb] = (mn == m_run[nb]) ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - mn);
+  // elements 8*cc .. 8*cc+7.  The groups are spread over the MFMAs of the
+  // next tiles; none is a long dependency chain (the wave issues in order).
+  auto sm_group = [&](f32x16_t& v, int g) {
+    if (g == 0) {                      // partial maxima
+      mpart[0] = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
+      mpart[1] = __builtin_fmaxf(__builtin_fmaxf(v[3], v[4]), v[5]);
+      mpart[2] = __builtin_fmaxf(__builtin_fmaxf(v[6], v[7]), v[8]);
+    } else if (g == 1) {
+      mpart[0] = __builtin_fmaxf(__builtin_fmaxf(v[9], v[10]), mpart[0]);
+      mpart[1] = __builtin_fmaxf(__builtin_fmaxf(v[11], v[12]), mpart[1]);
+      mpart[2] = __builtin_fmaxf(__builtin_fmaxf(v[13], v[14]), mpart[2]);
+      pmax = __builtin_fmaxf(__builtin_fmaxf(v[15], mpart[0]), __builtin_fmaxf(mpart[1], mpart[2]));
+    } else if (g == 2) {               // the other half of the keys; compare
+      mxs = max_half(pmax) * c;
+      upd = mxs > m_run + kRescaleLog2;
+    } else if (g == 3) {               // move the running max if any lane needs it
+      const bool u = __any(upd);
+      const float mn = u ? __builtin_fmaxf(m_run, mxs) : m_run;
+      alpha = (mn == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
       resc = resc || u;
-      m_run[nb] = mn;
-      mneg[nb] = (mn == kNegInf) ? 0.f : -mn;
-    } else if (g < 10 + 4 * kNCC) {    // 4 exponentials: columns cc, block nb, half
-      const int e = g - 10, cc = e >> 2, nb = (e >> 1) & 1, j0 = 8 * cc + 4 * (e & 1);
+      m_run = mn;
+      mneg = (mn == kNegInf) ? 0.f : -mn;
+    } else {                           // 4 exponentials
+      const int j0 = 4 * (g - 4);
 #pragma unroll
-      for (int j = j0; j < j0 + 4; ++j) s[0][nb][j] = __builtin_amdgcn_exp2f(fmaf(s[0][nb][j], c, mneg[nb]));
+      for (int j = j0; j < j0 + 4; ++j) v[j] = __builtin_amdgcn_exp2f(fmaf(v[j], c, mneg));
     }
   };
-  constexpr int kGroups = 10 + 4 * kNCC;
+  constexpr int kGroups = 4 + 4;
 
-  // bf16 weights: B operand of O^T = V^T P^T, [nb][cc]; the row sum is taken
-  // over the weights as they enter that product (rounded to bf16), two per
+  // bf16 weights (B operand of O^T = V^T P^T), two buffers: tile t's are read
+  // by the P V MFMAs of iteration t while tile t+1's are packed (buffer = tile
+  // parity).  The row sum is taken over the packed weights, two per
   // v_dot2_f32_bf16 against (1, 1).
-  // Two buffers: tile t's weights are read by the P V MFMAs of iteration t
-  // while tile t+1's are packed (buffer = tile parity).
-  u32x4_t pf[2][2][kNCC];
+  u32x4_t pf[2][kNCC];
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-  auto pack = [&](int buf, const f32x16_t (&s)[kMB][2], int cc, int nb) {
+  auto pack = [&](int buf, const f32x16_t& v, int cc) {
     const int j0 = 8 * cc;
-    u32x4_t& w4 = pf[buf][nb][cc];
+    u32x4_t& w4 = pf[buf][cc];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) w4[w] = pack_bf16x2(s[0][nb][j0 + 2 * w], s[0][nb][j0 + 2 * w + 1]);
+    for (int w = 0; w < 4; ++w) w4[w] = pack_bf16x2(v[j0 + 2 * w], v[j0 + 2 * w + 1]);
     pin(w4);
     // (pairs taken with shufflevector: bit-casting single 32-bit elements of
     // w4 to bf16x2 was miscompiled into reads of element 0 only)
@@ -441,42 +416,19 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     float a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 2, 3), ones, 0.f, false);
     a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 4, 5), ones, a0, false);
     a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 6, 7), ones, a1, false);
-    lpart[nb][cc] = a0 + a1;
+    lpart[cc] = a0 + a1;
   };
   auto row_sums = [&]() {
+    float t = lpart[0];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float t = lpart[nb][0];
-#pragma unroll
-      for (int cc = 1; cc < kNCC; ++cc) t += lpart[nb][cc];
-      l_run[nb] = fmaf(l_run[nb], alpha[nb], t);
-      pin(l_run[nb]);
-    }
+    for (int cc = 1; cc < kNCC; ++cc) t += lpart[cc];
+    l_run = fmaf(l_run, alpha, t);
+    pin(l_run);
   };
-  // O *= alpha when the running max moved (rare).  O lives in accumulation
-  // registers; each element goes through a VGPR, four at a time.  Stating the
-  // registers as "a" operands keeps the compiler from moving all of O to VGPRs.
+  // O *= alpha when the running max moved (rare).
   auto rescale = [&]() {
 #pragma unroll
-    for (int md = 0; md < C::MD; ++md)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; i += 4) {
-          float x0 = oacc[md][nb][i], x1 = oacc[md][nb][i + 1], x2 = oacc[md][nb][i + 2], x3 = oacc[md][nb][i + 3];
-          float tmp;
-          asm volatile(
-              "v_accvgpr_read_b32 %4, %0\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %0, %4\n\t"
-              "v_accvgpr_read_b32 %4, %1\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %1, %4\n\t"
-              "v_accvgpr_read_b32 %4, %2\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %2, %4\n\t"
-              "v_accvgpr_read_b32 %4, %3\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %3, %4"
-              : "+a"(x0), "+a"(x1), "+a"(x2), "+a"(x3), "=&v"(tmp)
-              : "v"(alpha[nb]));
-          oacc[md][nb][i] = x0;
-          oacc[md][nb][i + 1] = x1;
-          oacc[md][nb][i + 2] = x2;
-          oacc[md][nb][i + 3] = x3;
-        }
+    for (int md = 0; md < C::MD; ++md) oacc[md] *= alpha;
   };
 
   // O^T[d][query] += V^T[d][key] P^T[key][query]; contraction step cc covers
@@ -487,16 +439,14 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     const i16x4_t up = lds_tr16(a + 8 * C::ROWB);
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
   };
+  auto mfma_pv = [&](bf16x8_t vf, int buf, int cc, int md) {
+    oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pf[buf][cc]), oacc[md], 0, 0, 0);
+  };
   auto pv = [&](int buf, auto stage) {
 #pragma unroll
     for (int cc = 0; cc < kNCC; ++cc)
 #pragma unroll
-      for (int md = 0; md < C::MD; ++md) {
-        const bf16x8_t vf = vfrag(cc, md, stage);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          oacc[md][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pf[buf][nb][cc]), oacc[md][nb], 0, 0, 0);
-      }
+      for (int md = 0; md < C::MD; ++md) mfma_pv(vfrag(cc, md, stage), buf, cc, md);
   };
 
   // ---- main loop -----------------------------------------------------------------
@@ -511,25 +461,21 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   const int T = ntl0 == 0 ? 0 : ntl0 + (p.nseg - 1) * ntl_full;
   TileWalk walk{0, -1, ntl0, (int)lim0, ntl_full, p.n_k, p.nseg};
 
-  // One loop iteration issues 2*NS MFMAs in slots: even slot 2m is score MFMA
-  // m (contraction step kc = m/2, query block m%2), odd slot 2m+1 is P V MFMA
-  // m (columns cc = m/(2*MD), d-block md = (m/2)%MD, query block m%2).  K
-  // fragment f = kc is first needed at slot 4f, V fragment v = cc*MD + md at
-  // slot 4v + 1; both are read kLead slots earlier (the first ones at the end
-  // of the previous iteration, after its barrier).
-  constexpr int kNS = 2 * C::KC;       // score MFMAs per tile (= P V MFMAs)
-  constexpr int kSlots = 2 * kNS;
-  constexpr int kLead = 6;
-  constexpr int kPre = (kLead + 3) / 4;   // fragments of each kind read ahead
-  // softmax group g goes to slot kSlotOf(g); the packs (columns cc, block nb)
-  // follow the exponentials they read
-  constexpr auto kSlotOfGroup = [](int g) { return (g * kSlots) / (kGroups + 2 * kNCC + 2); };
-  constexpr auto kSlotOfPack = [](int cc, int nb) {
-    return ((10 + 4 * cc + 2 * nb + 2 + 2 * cc + nb) * kSlots) / (kGroups + 2 * kNCC + 2);
-  };
+  // One loop iteration issues 2*KC MFMAs in slots: even slot 2m is score MFMA
+  // m (contraction step kc = m), odd slot 2m+1 is P V MFMA m (columns
+  // cc = m / MD, d-block md = m % MD).  K fragment m is first needed at slot
+  // 2m, V fragment m at slot 2m + 1; both are read kLead slots earlier (the
+  // first ones at the end of the previous iteration, after its barrier).
+  constexpr int kSlots = 2 * C::KC;
+  constexpr int kLead = 4;
+  constexpr int kPre = (kLead + 1) / 2;   // fragments of each kind read ahead
+  // softmax group g at slot kSlotOfGroup(g); pack cc after the exponentials
+  // of its columns (groups 4 + 2*cc, 5 + 2*cc)
+  constexpr auto kSlotOfGroup = [](int g) { return (g * kSlots) / (kGroups + kNCC + 1); };
+  constexpr auto kSlotOfPack = [](int cc) { return ((6 + 3 * cc + 1) * kSlots) / (kGroups + kNCC + 1); };
 
   if (T > 0) {
-    f32x16_t sa[kMB][2], sb[kMB][2];
+    f32x16_t sa, sb;
     const Tile t0 = walk.next(), t1 = walk.next(), t2 = walk.next(), t3 = walk.next();
     const Tile t4 = walk.next();
     issue_k(t0, 0);
@@ -546,9 +492,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) sm_group(sa, g);   // O is still zero: no rescale
 #pragma unroll
-    for (int cc = 0; cc < kNCC; ++cc)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) pack(0, sa, cc, nb);
+    for (int cc = 0; cc < kNCC; ++cc) pack(0, sa, cc);
     row_sums();
     lds_reads_done_sync();               // K stage 0 is free
     issue_k(t4, 0);
@@ -558,7 +502,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
 
     u32x4_t kfr[C::KC];
     bf16x8_t vfr[kNCC * C::MD];
-    auto read_k = [&](int f, auto stage) { kfr[f] = kfrag(f, 0, stage); };
+    auto read_k = [&](int f, auto stage) { kfr[f] = kfrag(f, stage); };
     auto read_v = [&](int v, auto stage) { vfr[v] = vfrag(v / C::MD, v % C::MD, stage); };
     // first fragments of iteration 0 (K(2) in stage 2, V(0) in stage 0)
     wait_dma_and_sync<4 * C::NL>();
@@ -572,7 +516,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     // into `nx`; O += V(t) P(t); S(t+1) in `cu` goes through the softmax into
     // P(t+1).  It ends by waiting for K(t+3), V(t+1) and reading their first
     // fragments.
-    auto body = [&](auto R, f32x16_t (&nx)[kMB][2], f32x16_t (&cu)[kMB][2]) {
+    auto body = [&](auto R, f32x16_t& nx, f32x16_t& cu) {
       constexpr int r = decltype(R)::value;
       constexpr int ks = (r + 2) % kStages, vs = r;
       issue_k(d5, (r + 5) % kStages);
@@ -580,28 +524,17 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
       resc = false;
       static_for<kSlots>([&](auto I) {
         constexpr int i = decltype(I)::value;
-        // fragments needed kLead slots from now
-        constexpr int ahead = i + kLead;
-        if constexpr ((ahead & 3) == 0 && ahead / 4 < C::KC && ahead / 4 >= kPre) read_k(ahead / 4, Step<ks>{});
-        if constexpr ((ahead & 3) == 1 && ahead / 4 < kNCC * C::MD && ahead / 4 >= kPre)
-          read_v(ahead / 4, Step<vs>{});
-        constexpr int m = i >> 1, nb = m & 1;
-        if constexpr ((i & 1) == 0) {
-          constexpr int kc = m >> 1;
-          const f32x16_t z = {};
-          nx[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kfr[kc]), as_bf16x8(qf[nb][kc]),
-                                                              kc == 0 ? z : nx[0][nb], 0, 0, 0);
-        } else {
-          constexpr int v = m >> 1, cc = v / C::MD, md = v % C::MD;
-          oacc[md][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[v], as_bf16x8(pf[r & 1][nb][cc]),
-                                                                 oacc[md][nb], 0, 0, 0);
-        }
+        constexpr int ahead = i + kLead, fa = ahead >> 1;   // fragment needed kLead slots from now
+        if constexpr ((ahead & 1) == 0 && fa < C::KC && fa >= kPre) read_k(fa, Step<ks>{});
+        if constexpr ((ahead & 1) == 1 && fa < kNCC * C::MD && fa >= kPre) read_v(fa, Step<vs>{});
+        constexpr int m = i >> 1;
+        if constexpr ((i & 1) == 0) mfma_s(nx, kfr[m], m);
+        else mfma_pv(vfr[m], r & 1, m / C::MD, m % C::MD);
         static_for<kGroups>([&](auto G) {
           if constexpr (kSlotOfGroup(decltype(G)::value) == i) sm_group(cu, decltype(G)::value);
         });
-        static_for<2 * kNCC>([&](auto Q) {
-          constexpr int cc = decltype(Q)::value >> 1, q = decltype(Q)::value & 1;
-          if constexpr (kSlotOfPack(cc, q) == i) pack((r + 1) & 1, cu, cc, q);
+        static_for<kNCC>([&](auto Q) {
+          if constexpr (kSlotOfPack(decltype(Q)::value) == i) pack((r + 1) & 1, cu, decltype(Q)::value);
         });
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -632,36 +565,36 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no DMA may outlive the workgroup's LDS
 
   // ---- epilogue: normalise, merge into the running (O, lse), store ------------
+  {
+    const int row = qw0 + l32;
+    const float lt = sum_half(l_run);
+    if (row < p.n_q) {
+      const float lse_j = (lt > 0.f) ? (m_run + log2f(lt)) * kLn2 : kNegInf;
+      const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+      const int64_t srow = ((int64_t)b * p.Hq + h) * p.n_q + row;
+      float wi = 0.f, wj = 1.f, lse = lse_j;
+      if (p.o_in != nullptr) lse = lse_merge_weights(p.lse_in[srow], lse_j, wi, wj);
+      const float f = wj * inv;
+      const int64_t ooff = b * p.oo_sb + h * p.oo_sh + (int64_t)row * p.oo_sn;
+      const int64_t ioff = b * p.oi_sb + h * p.oi_sh + (int64_t)row * p.oi_sn;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int row = qw0 + 32 * nb + l32;
-    const float lt = sum_half(l_run[nb]);
-    if (row >= p.n_q) continue;
-    const float lse_j = (lt > 0.f) ? (m_run[nb] + log2f(lt)) * kLn2 : kNegInf;
-    const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
-    const int64_t srow = ((int64_t)b * p.Hq + h) * p.n_q + row;
-    float wi = 0.f, wj = 1.f, lse = lse_j;
-    if (p.o_in != nullptr) lse = lse_merge_weights(p.lse_in[srow], lse_j, wi, wj);
-    const float f = wj * inv;
-    const int64_t ooff = b * p.oo_sb + h * p.oo_sh + (int64_t)row * p.oo_sn;
-    const int64_t ioff = b * p.oi_sb + h * p.oi_sh + (int64_t)row * p.oi_sn;
+      for (int md = 0; md < C::MD; ++md)
 #pragma unroll
-    for (int md = 0; md < C::MD; ++md)
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * md + 8 * g + 4 * hi;
+          float y[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * md + 8 * g + 4 * hi;
-        float y[4];
+          for (int r = 0; r < 4; ++r) y[r] = oacc[md][4 * g + r] * f;
+          if (p.o_in != nullptr && wi != 0.f) {
+            float x[4];
+            load4(p.o_in, ioff + d0, p.acc_dtype, x);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = oacc[md][nb][4 * g + r] * f;
-        if (p.o_in != nullptr && wi != 0.f) {
-          float x[4];
-          load4(p.o_in, ioff + d0, p.acc_dtype, x);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) y[r] = fmaf(wi, x[r], y[r]);
+            for (int r = 0; r < 4; ++r) y[r] = fmaf(wi, x[r], y[r]);
+          }
+          store4(p.o_out, ooff + d0, p.out_dtype, y);
         }
-        store4(p.o_out, ooff + d0, p.out_dtype, y);
-      }
-    if (hi == 0) p.lse_out[srow] = lse;
+      if (hi == 0) p.lse_out[srow] = lse;
+    }
   }
 }
 
