@@ -73,7 +73,8 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQW = 32;              // query rows per wavefront
 constexpr int kBM = kQW * kWaves;    // query rows per workgroup
-constexpr int kBN = 32;              // keys per tile
+constexpr int kBN = 64;              // keys per tile
+constexpr int kNB = kBN / 32;        // 32-key blocks of the score tile
 constexpr int kNCC = kBN / 16;       // 16-key contraction steps of P V per tile
 constexpr int kStages = 4;           // LDS stages per tensor (= loop unroll)
 constexpr float kRescaleLog2 = 8.0f;
@@ -87,15 +88,13 @@ struct Cfg {
   static constexpr int TILE = kBN * ROWB;                // bytes per K or V tile
   static constexpr int RPW = 1024 / ROWB;                // rows per wave-wide 1 KiB load
   static constexpr int NLT = TILE / 1024;                // wave-wide loads per tile
-  // Every wave issues the same number of loads per tile (its vmcnt
-  // bookkeeping is then uniform); with fewer loads than waves the spare
-  // waves issue an empty load into a dummy 1 KiB of LDS.
-  static constexpr int NL = NLT >= kWaves ? NLT / kWaves : 1;
+  static constexpr int NL = NLT / kWaves;                // loads per wave per tile
   static constexpr int K_LDS = 0;                        // kStages K tiles
   static constexpr int V_LDS = kStages * TILE;           // kStages V tiles
-  static constexpr int DUMMY = 2 * kStages * TILE;       // sink of the empty loads
-  static constexpr int LDS_BYTES = DUMMY + (NLT < kWaves ? 1024 : 0);
-  static_assert(NLT % kWaves == 0 || NLT < kWaves, "tile loads must spread evenly over the waves");
+  static constexpr int LDS_BYTES = 2 * kStages * TILE;
+  // every wave issues the same number of loads per tile, so that its vmcnt
+  // bookkeeping is uniform
+  static_assert(NL >= 1 && NLT % kWaves == 0, "tile loads must spread evenly over the waves");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -176,11 +175,13 @@ __device__ __forceinline__ void lds_reads_done_sync() {
 
 // As above, and first wait until at most N of this wave's vector-memory
 // operations are in flight: every DMA issued before the last N has landed,
-// so after the barrier it is visible in LDS to the whole workgroup.
-template <int N>
+// so after the barrier it is visible in LDS to the whole workgroup.  The
+// last L LDS reads of the wave (reads of stages nobody overwrites next) may
+// still be in flight.
+template <int N, int L = 0>
 __device__ __forceinline__ void wait_dma_and_sync() {
-  static_assert(N >= 0 && N < 64, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(N, 0));
+  static_assert(N >= 0 && N < 64 && L >= 0 && L < 16, "waitcnt immediate");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(N, L));
   asm volatile("s_barrier" ::: "memory");
 }
 
@@ -293,65 +294,77 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     const int c = 4 * md + 2 * ((lane >> 4) & 1) + ((a16 & 3) >> 1);
     vofs[md] = lds0 + C::V_LDS + r * C::ROWB + ((c ^ swz_v<D>(r)) * 16) + (a16 & 1) * 8;
   }
-  // DMA: wave-wide load i of a tile fills rows (i*kWaves + wave)*RPW ..; lane
-  // fills row r0 + lane/NCH, chunk position lane%NCH, so it reads source chunk
-  // (lane%NCH) ^ swizzle(row).  (r0 is a multiple of the swizzle periods.)
-  const int lrow = lane / C::NCH;
-  const uint32_t dk = (uint32_t)(lrow * k_snb) + (((lane % C::NCH) ^ swz_k<D>(wave * C::RPW + lrow)) * 16);
-  const uint32_t dv = (uint32_t)(lrow * v_snb) + (((lane % C::NCH) ^ swz_v<D>(lrow)) * 16);
+  // DMA: wave-wide load i of a tile fills rows r0 = (i*kWaves + wave)*RPW ..
+  // r0 + RPW - 1; the lane fills row r0 + lane/NCH at chunk position lane%NCH,
+  // so it reads source chunk (lane%NCH) ^ swizzle(row).  dko/dvo are the
+  // lanes' byte offsets inside a tile.
+  uint32_t dko[C::NL], dvo[C::NL];
+#pragma unroll
+  for (int i = 0; i < C::NL; ++i) {
+    const int r = (i * kWaves + wave) * C::RPW + lane / C::NCH;
+    dko[i] = (uint32_t)(r * k_snb) + (((lane % C::NCH) ^ swz_k<D>(r)) * 16);
+    dvo[i] = (uint32_t)(r * v_snb) + (((lane % C::NCH) ^ swz_v<D>(r)) * 16);
+  }
 
   // chunk of visit position s
   auto chunk_of = [&](int s) {
     const int j = p.rank - s;
     return j < 0 ? j + p.P : j;
   };
+  // One buffer resource spans the tile's valid rows: rows past the end of the
+  // chunk (and every row of an empty tile) read as zeros.
   auto issue = [&](const unsigned char* hbase, int64_t csb, int snb, const Tile& t, uint32_t stage,
-                   uint32_t voff) {
+                   const uint32_t* voff) {
     const unsigned char* tb = hbase + (chunk_of(t.s) * csb + (int64_t)(t.tt * kBN) * snb);
+    const i32x4_t rs = buffer_rsrc(tb, (uint32_t)t.nvalid * (uint32_t)snb);
 #pragma unroll
-    for (int i = 0; i < C::NL; ++i) {
-      const int blk = i * kWaves + wave;
-      const int r0 = blk * C::RPW;
-      const int rows = t.nvalid - r0;
-      const bool real = blk < C::NLT;
-      const uint32_t bytes = (real && rows > 0) ? (uint32_t)(rows * snb) : 0u;
-      dma16(voff, buffer_rsrc(tb + (real ? r0 * snb : 0), bytes), real ? stage + r0 * C::ROWB : lds0 + C::DUMMY);
-    }
+    for (int i = 0; i < C::NL; ++i) dma16(voff[i], rs, stage + (i * kWaves + wave) * C::RPW * C::ROWB);
   };
-  auto issue_k = [&](const Tile& t, int stage) { issue(kg, k_csb, k_snb, t, lds0 + C::K_LDS + stage * C::TILE, dk); };
-  auto issue_v = [&](const Tile& t, int stage) { issue(vg, v_csb, v_snb, t, lds0 + C::V_LDS + stage * C::TILE, dv); };
+  auto issue_k = [&](const Tile& t, int stage) { issue(kg, k_csb, k_snb, t, lds0 + C::K_LDS + stage * C::TILE, dko); };
+  auto issue_v = [&](const Tile& t, int stage) { issue(vg, v_csb, v_snb, t, lds0 + C::V_LDS + stage * C::TILE, dvo); };
 
   // ---- scores and masks --------------------------------------------------------
-  // S^T tile: 32 keys (M) x the wave's 32 queries (N); accumulator element j
-  // holds key 8*(j/4) + 4*hi + j%4 of query qw0 + l32
-  auto kfrag = [&](int kc, auto stage) { return lds_b128(kofs[kc] + decltype(stage)::value * C::TILE); };
-  auto mfma_s = [&](f32x16_t& s, u32x4_t kf, int kc) {
-    const f32x16_t z = {};
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[kc]), kc == 0 ? z : s, 0, 0, 0);
+  // S^T tile: 64 keys (M, two 32-key blocks nb) x the wave's 32 queries (N);
+  // element j of block nb holds key 32*nb + 8*(j/4) + 4*hi + j%4 of query
+  // qw0 + l32.  Score MFMA m covers block nb = m % 2, contraction step
+  // kc = m / 2 (the two blocks' accumulation chains alternate).
+  struct STile {
+    f32x16_t b[kNB];
   };
-  auto scores = [&](f32x16_t& s, auto stage) {
+  auto kfrag = [&](int m, auto stage) {
+    return lds_b128(kofs[m / kNB] + decltype(stage)::value * C::TILE + (m % kNB) * 32 * C::ROWB);
+  };
+  auto mfma_s = [&](STile& s, u32x4_t kf, int m) {
+    const f32x16_t z = {};
+    const int nb = m % kNB, kc = m / kNB;
+    s.b[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[kc]), kc == 0 ? z : s.b[nb], 0, 0, 0);
+  };
+  auto scores = [&](STile& s, auto stage) {
 #pragma unroll
-    for (int kc = 0; kc < C::KC; ++kc) mfma_s(s, kfrag(kc, stage), kc);
+    for (int m = 0; m < kNB * C::KC; ++m) mfma_s(s, kfrag(m, stage), m);
   };
 
   // Causal masks only touch tiles of the first chunk of the visit (the rank's
   // own): those at or after tile tt_mask can hold a key after this wave's
   // first query.
-  const int64_t qpos_w = p.q_pos0 + qw0;
+  // qrel: position of this wave's first query relative to the own chunk's
+  // first key (clamped: beyond +-2^30 no own tile is on the diagonal)
   const int64_t kpos_own = p.k_pos0 + (int64_t)p.rank * p.k_posstride;
-  const int tt_mask = (int)max((int64_t)0, (qpos_w - kpos_own - kBN + 1 + kBN) / kBN);
-  auto mask = [&](f32x16_t& s, const Tile& t) {
+  const int qrel = (int)min((int64_t)(1 << 30), max((int64_t)-(1 << 30), p.q_pos0 + qw0 - kpos_own));
+  const int tt_mask = max(0, (qrel + 1) / kBN);
+  auto mask = [&](STile& s, const Tile& t) {
     const bool diag = p.causal && t.s == 0 && t.tt >= tt_mask;
     if (!(t.nvalid < kBN || diag)) return;
-    const int64_t kpos = kpos_own + (int64_t)t.tt * kBN;   // only read for the own chunk
-    int64_t rel = qpos_w + l32 - kpos;                     // last visible key of the tile
+    int64_t rel = (int64_t)qrel + l32 - (int64_t)t.tt * kBN;   // last visible key of the tile
     if (!diag || rel > kBN) rel = kBN;
-    const int lastk = (int)min(rel, (int64_t)t.nvalid - 1);
+    // key u = (32*nb + 8*(j/4) + j%4) + 4*hi is masked when u > lastk; the
+    // lane term moves to the right so that the left side is an immediate
+    const int lk = (int)min(rel, (int64_t)t.nvalid - 1) - 4 * hi;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int u = 8 * (j >> 2) + 4 * hi + (j & 3);
-      if (u > lastk) s[j] = kNegInf;
-    }
+    for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (32 * nb + 8 * (j >> 2) + (j & 3) > lk) s.b[nb][j] = kNegInf;
   };
 
   // ---- online softmax state --------------------------------------------------
@@ -361,28 +374,33 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   float m_run = kNegInf;   // running max, base-2 units
   float l_run = 0.f;       // this lane's half of the row sum
   float alpha = 1.f;
-  float mpart[3], pmax = kNegInf, mxs = kNegInf, mneg = 0.f, lpart[kNCC];
+  float mpart[4], pmax = kNegInf, mxs = kNegInf, mneg = 0.f, lpart[kNCC];
   bool upd = false, resc = false;
   const float c = p.scale_log2;
 
   // ---- the softmax of one tile in small work groups ------------------------------
-  // P columns cc (16 keys of the P V contraction step cc) are accumulator
-  // elements 8*cc .. 8*cc+7.  The groups are spread over the MFMAs of the
-  // next tiles; none is a long dependency chain (the wave issues in order).
-  auto sm_group = [&](f32x16_t& v, int g) {
-    if (g == 0) {                      // partial maxima
-      mpart[0] = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
-      mpart[1] = __builtin_fmaxf(__builtin_fmaxf(v[3], v[4]), v[5]);
-      mpart[2] = __builtin_fmaxf(__builtin_fmaxf(v[6], v[7]), v[8]);
-    } else if (g == 1) {
-      mpart[0] = __builtin_fmaxf(__builtin_fmaxf(v[9], v[10]), mpart[0]);
-      mpart[1] = __builtin_fmaxf(__builtin_fmaxf(v[11], v[12]), mpart[1]);
-      mpart[2] = __builtin_fmaxf(__builtin_fmaxf(v[13], v[14]), mpart[2]);
-      pmax = __builtin_fmaxf(__builtin_fmaxf(v[15], mpart[0]), __builtin_fmaxf(mpart[1], mpart[2]));
-    } else if (g == 2) {               // the other half of the keys; compare
+  // A lane holds 32 scores of its query: x(e) = block e / 16, element e % 16.
+  // P columns cc (16 keys of the P V contraction step cc) are x(8*cc) ..
+  // x(8*cc + 7).  The groups are spread over the MFMAs of the next tiles;
+  // none is a long dependency chain (the wave issues in order).
+  auto sm_group = [&](STile& v, int g) {
+    auto x = [&](int e) { return v.b[e >> 4][e & 15]; };
+    if (g == 0) {                      // partial maxima over x(0..11)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) mpart[k] = __builtin_fmaxf(__builtin_fmaxf(x(3 * k), x(3 * k + 1)), x(3 * k + 2));
+    } else if (g == 1 || g == 2) {     // x(12..19), x(20..27)
+      const int e0 = 12 + 8 * (g - 1);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        mpart[k] = __builtin_fmaxf(__builtin_fmaxf(x(e0 + 2 * k), x(e0 + 2 * k + 1)), mpart[k]);
+    } else if (g == 3) {               // x(28..31) and the tree's root
+      mpart[0] = __builtin_fmaxf(__builtin_fmaxf(x(28), x(29)), mpart[0]);
+      mpart[1] = __builtin_fmaxf(__builtin_fmaxf(x(30), x(31)), mpart[1]);
+      pmax = __builtin_fmaxf(__builtin_fmaxf(mpart[0], mpart[1]), __builtin_fmaxf(mpart[2], mpart[3]));
+    } else if (g == 4) {               // the other half of the keys; compare
       mxs = max_half(pmax) * c;
       upd = mxs > m_run + kRescaleLog2;
-    } else if (g == 3) {               // move the running max if any lane needs it
+    } else if (g == 5) {               // move the running max if any lane needs it
       const bool u = __any(upd);
       const float mn = u ? __builtin_fmaxf(m_run, mxs) : m_run;
       alpha = (mn == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
@@ -390,24 +408,25 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
       m_run = mn;
       mneg = (mn == kNegInf) ? 0.f : -mn;
     } else {                           // 4 exponentials
-      const int j0 = 4 * (g - 4);
+      const int e0 = 4 * (g - 6);
 #pragma unroll
-      for (int j = j0; j < j0 + 4; ++j) v[j] = __builtin_amdgcn_exp2f(fmaf(v[j], c, mneg));
+      for (int e = e0; e < e0 + 4; ++e) v.b[e >> 4][e & 15] = __builtin_amdgcn_exp2f(fmaf(x(e), c, mneg));
     }
   };
-  constexpr int kGroups = 4 + 4;
+  constexpr int kGroups = 6 + 8;
 
-  // bf16 weights (B operand of O^T = V^T P^T), two buffers: tile t's are read
-  // by the P V MFMAs of iteration t while tile t+1's are packed (buffer = tile
-  // parity).  The row sum is taken over the packed weights, two per
-  // v_dot2_f32_bf16 against (1, 1).
-  u32x4_t pf[2][kNCC];
+  // bf16 weights (B operand of O^T = V^T P^T) of one tile: the P V MFMAs of
+  // iteration t read tile t's columns while tile t+1's are packed behind them.
+  // The row sum is taken over the packed weights, two per v_dot2_f32_bf16
+  // against (1, 1).
+  u32x4_t pf[kNCC];
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-  auto pack = [&](int buf, const f32x16_t& v, int cc) {
-    const int j0 = 8 * cc;
-    u32x4_t& w4 = pf[buf][cc];
+  auto pack = [&](const STile& v, int cc) {
+    const int j0 = 8 * (cc & 1);
+    const f32x16_t& vb = v.b[cc >> 1];
+    u32x4_t& w4 = pf[cc];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) w4[w] = pack_bf16x2(v[j0 + 2 * w], v[j0 + 2 * w + 1]);
+    for (int w = 0; w < 4; ++w) w4[w] = pack_bf16x2(vb[j0 + 2 * w], vb[j0 + 2 * w + 1]);
     pin(w4);
     // (pairs taken with shufflevector: bit-casting single 32-bit elements of
     // w4 to bf16x2 was miscompiled into reads of element 0 only)
@@ -439,14 +458,14 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     const i16x4_t up = lds_tr16(a + 8 * C::ROWB);
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  auto mfma_pv = [&](bf16x8_t vf, int buf, int cc, int md) {
-    oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pf[buf][cc]), oacc[md], 0, 0, 0);
+  auto mfma_pv = [&](bf16x8_t vf, int cc, int md) {
+    oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pf[cc]), oacc[md], 0, 0, 0);
   };
-  auto pv = [&](int buf, auto stage) {
+  auto pv = [&](auto stage) {
 #pragma unroll
     for (int cc = 0; cc < kNCC; ++cc)
 #pragma unroll
-      for (int md = 0; md < C::MD; ++md) mfma_pv(vfrag(cc, md, stage), buf, cc, md);
+      for (int md = 0; md < C::MD; ++md) mfma_pv(vfrag(cc, md, stage), cc, md);
   };
 
   // ---- main loop -----------------------------------------------------------------
@@ -461,21 +480,31 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   const int T = ntl0 == 0 ? 0 : ntl0 + (p.nseg - 1) * ntl_full;
   TileWalk walk{0, -1, ntl0, (int)lim0, ntl_full, p.n_k, p.nseg};
 
-  // One loop iteration issues 2*KC MFMAs in slots: even slot 2m is score MFMA
-  // m (contraction step kc = m), odd slot 2m+1 is P V MFMA m (columns
-  // cc = m / MD, d-block md = m % MD).  K fragment m is first needed at slot
-  // 2m, V fragment m at slot 2m + 1; both are read kLead slots earlier (the
-  // first ones at the end of the previous iteration, after its barrier).
-  constexpr int kSlots = 2 * C::KC;
+  // One loop iteration issues 2*NB*KC MFMAs in slots: even slot 2m is score
+  // MFMA m, odd slot 2m+1 is P V MFMA m (columns cc = m / MD, d-block
+  // md = m % MD).  K fragment m is first needed at slot 2m, V fragment m at
+  // slot 2m + 1; both are read kLead slots earlier (the first ones in the last
+  // slots of the previous iteration).
+  constexpr int kMF = kNB * C::KC;        // MFMAs of each kind per tile
+  static_assert(kMF == kNCC * C::MD, "score and P V MFMA counts");
+  constexpr int kSlots = 2 * kMF;
   constexpr int kLead = 4;
   constexpr int kPre = (kLead + 1) / 2;   // fragments of each kind read ahead
-  // softmax group g at slot kSlotOfGroup(g); pack cc after the exponentials
-  // of its columns (groups 4 + 2*cc, 5 + 2*cc)
-  constexpr auto kSlotOfGroup = [](int g) { return (g * kSlots) / (kGroups + kNCC + 1); };
-  constexpr auto kSlotOfPack = [](int cc) { return ((6 + 3 * cc + 1) * kSlots) / (kGroups + kNCC + 1); };
+  constexpr int kPreLds = 3 * kPre;       // their LDS instructions (K: 1, V: 2)
+  // softmax group g at slot kSlotOfGroup(g).  Pack cc overwrites the weights
+  // of columns cc, so it comes after the exponentials of those columns (groups
+  // 6 + 2*cc, 7 + 2*cc) and after the last P V MFMA of this iteration that
+  // reads them (slot 2*MD*(cc+1) - 1); a pack that falls past the last slot
+  // runs after the slot loop.
+  constexpr auto kSlotOfGroup = [](int g) { return (g * kSlots) / (kGroups + kNCC); };
+  constexpr auto kSlotOfPack = [](int cc) {
+    const int after_exp = ((7 + 2 * cc) * kSlots) / (kGroups + kNCC) + 1;
+    const int after_pv = 2 * C::MD * (cc + 1);
+    return after_exp > after_pv ? after_exp : after_pv;
+  };
 
   if (T > 0) {
-    f32x16_t sa, sb;
+    STile sa, sb;
     const Tile t0 = walk.next(), t1 = walk.next(), t2 = walk.next(), t3 = walk.next();
     const Tile t4 = walk.next();
     issue_k(t0, 0);
@@ -492,7 +521,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) sm_group(sa, g);   // O is still zero: no rescale
 #pragma unroll
-    for (int cc = 0; cc < kNCC; ++cc) pack(0, sa, cc);
+    for (int cc = 0; cc < kNCC; ++cc) pack(sa, cc);
     row_sums();
     lds_reads_done_sync();               // K stage 0 is free
     issue_k(t4, 0);
@@ -500,12 +529,13 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     // tiles t+2 .. t+5 at the top of iteration t
     Tile d2 = t2, d3 = t3, d4 = t4, d5 = walk.next();
 
-    u32x4_t kfr[C::KC];
-    bf16x8_t vfr[kNCC * C::MD];
+    u32x4_t kfr[kMF];
+    bf16x8_t vfr[kMF];
     auto read_k = [&](int f, auto stage) { kfr[f] = kfrag(f, stage); };
     auto read_v = [&](int v, auto stage) { vfr[v] = vfrag(v / C::MD, v % C::MD, stage); };
-    // first fragments of iteration 0 (K(2) in stage 2, V(0) in stage 0)
-    wait_dma_and_sync<4 * C::NL>();
+    // first fragments of iteration 0 (K(2) in stage 2, V(0) in stage 0); K(3)
+    // and V(1), which iteration 0 reads ahead, have landed as well
+    wait_dma_and_sync<2 * C::NL>();
 #pragma unroll
     for (int f = 0; f < kPre; ++f) {
       read_k(f, Step<2>{});
@@ -514,9 +544,10 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
 
     // Iteration t = 4k + R: K(t+5) and V(t+3) are fetched; S(t+2) computed
     // into `nx`; O += V(t) P(t); S(t+1) in `cu` goes through the softmax into
-    // P(t+1).  It ends by waiting for K(t+3), V(t+1) and reading their first
-    // fragments.
-    auto body = [&](auto R, f32x16_t& nx, f32x16_t& cu) {
+    // P(t+1).  Its last slots read the first fragments of K(t+3) and V(t+1)
+    // (made visible by the previous iteration's barrier); it ends by waiting
+    // for K(t+4), V(t+2), which iteration t+1 reads ahead.
+    auto body = [&](auto R, STile& nx, STile& cu) {
       constexpr int r = decltype(R)::value;
       constexpr int ks = (r + 2) % kStages, vs = r;
       issue_k(d5, (r + 5) % kStages);
@@ -525,18 +556,26 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
       static_for<kSlots>([&](auto I) {
         constexpr int i = decltype(I)::value;
         constexpr int ahead = i + kLead, fa = ahead >> 1;   // fragment needed kLead slots from now
-        if constexpr ((ahead & 1) == 0 && fa < C::KC && fa >= kPre) read_k(fa, Step<ks>{});
-        if constexpr ((ahead & 1) == 1 && fa < kNCC * C::MD && fa >= kPre) read_v(fa, Step<vs>{});
+        if constexpr ((ahead & 1) == 0) {
+          if constexpr (fa >= kMF) read_k(fa - kMF, Step<(r + 3) % kStages>{});
+          else if constexpr (fa >= kPre) read_k(fa, Step<ks>{});
+        } else {
+          if constexpr (fa >= kMF) read_v(fa - kMF, Step<(r + 1) % kStages>{});
+          else if constexpr (fa >= kPre) read_v(fa, Step<vs>{});
+        }
         constexpr int m = i >> 1;
         if constexpr ((i & 1) == 0) mfma_s(nx, kfr[m], m);
-        else mfma_pv(vfr[m], r & 1, m / C::MD, m % C::MD);
+        else mfma_pv(vfr[m], m / C::MD, m % C::MD);
         static_for<kGroups>([&](auto G) {
           if constexpr (kSlotOfGroup(decltype(G)::value) == i) sm_group(cu, decltype(G)::value);
         });
         static_for<kNCC>([&](auto Q) {
-          if constexpr (kSlotOfPack(decltype(Q)::value) == i) pack((r + 1) & 1, cu, decltype(Q)::value);
+          if constexpr (kSlotOfPack(decltype(Q)::value) == i) pack(cu, decltype(Q)::value);
         });
         __builtin_amdgcn_sched_barrier(0);
+      });
+      static_for<kNCC>([&](auto Q) {
+        if constexpr (kSlotOfPack(decltype(Q)::value) >= kSlots) pack(cu, decltype(Q)::value);
       });
       row_sums();
       if (resc) rescale();
@@ -545,12 +584,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
       d3 = d4;
       d4 = d5;
       d5 = walk.next();
-      wait_dma_and_sync<4 * C::NL>();    // K(t+3), V(t+1) landed
-#pragma unroll
-      for (int f = 0; f < kPre; ++f) {
-        read_k(f, Step<(r + 3) % kStages>{});
-        read_v(f, Step<(r + 1) % kStages>{});
-      }
+      wait_dma_and_sync<2 * C::NL, kPreLds>();   // K(t+4), V(t+2) landed
     };
     // T - 1 iterations, padded to a multiple of 4 with empty tiles
     const int iters = (T - 1 + 3) & ~3;
@@ -560,7 +594,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
       body(Step<2>{}, sa, sb);
       body(Step<3>{}, sb, sa);
     }
-    pv(0, Step<0>{});                    // V of the last (padded) tile landed above
+    pv(Step<0>{});                       // V of the last (padded) tile landed above
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no DMA may outlive the workgroup's LDS
 
