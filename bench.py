@@ -147,7 +147,7 @@ def bench_attention_extra(api, torch, name, steps=3):
             "flops": w.flops()}
 
 
-def cpu_baseline(x_dev, w, torch, budget_rows=4096, heads=4):
+def cpu_baseline(x_dev, w, torch, budget_rows=4096, heads=16):
     """The fp64 oracle on a bounded sample of the workload: query chunk 0
     (4096 rows) of the first `heads` heads against all 32768 keys."""
     import oracle

@@ -241,13 +241,27 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   const int hi = lane >> 5;
   const int a16 = lane & 15;
 
-  // Workgroup -> (b, h, q-tile).  Heads vary fastest so that consecutive
-  // workgroups (spread round-robin over the XCDs) cover all heads; with a
-  // causal mask the q-tiles are issued heaviest (last) first.
+  // Workgroup -> (b, h, q-tile).  Workgroups are dealt round-robin to the 8
+  // XCDs, each with its own L2.  Without a mask every workgroup has the same
+  // work: the linear id is remapped so that each XCD walks a contiguous range
+  // of (b, h, q-tile) with the q-tiles of one head adjacent, and the
+  // workgroups streaming one head's K/V run together on one XCD and share its
+  // L2.  With a causal mask the work grows with the q-tile: heads vary
+  // fastest (every XCD gets a mix) and the q-tiles are issued heaviest first.
   const int BH = p.B * p.Hq;
-  const int qt_rank = blockIdx.x / BH;
-  const int bh = blockIdx.x - qt_rank * BH;
-  const int qt = p.causal ? (n_qtiles - 1 - qt_rank) : qt_rank;
+  int bh, qt;
+  if (p.causal) {
+    const int qt_rank = blockIdx.x / BH;
+    bh = blockIdx.x - qt_rank * BH;
+    qt = n_qtiles - 1 - qt_rank;
+  } else {
+    constexpr int kXcds = 8;
+    const int per = gridDim.x / kXcds, rem = gridDim.x % kXcds;
+    const int xcd = blockIdx.x % kXcds;
+    const int logical = xcd * per + min(xcd, rem) + blockIdx.x / kXcds;
+    bh = logical / n_qtiles;
+    qt = logical - bh * n_qtiles;
+  }
   const int b = bh / p.Hq;
   const int h = bh - b * p.Hq;
   const int hk = h / p.group;
