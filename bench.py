@@ -13,7 +13,8 @@ Printed: ONE JSON line on stdout with the metric, the roofline of the
 chunk-attention kernel (MFMA-bound) and the CPU oracle timed on a bounded
 sample of the same workload.  Extra figures on the other workloads (Ulysses
 permute GB/s on 8 x [16384, 32, 128] bf16, the causal 128k rank-7 ring share,
-the causal 128k GQA Ulysses share) go in "extras".  Logs go to stderr.
+the causal 128k GQA Ulysses share, the whole causal 128k ring under the
+contiguous and the zigzag split) go in "extras".  Logs go to stderr.
 """
 from __future__ import annotations
 
@@ -147,6 +148,49 @@ def bench_attention_extra(api, torch, name, steps=3):
             "flops": w.flops()}
 
 
+def bench_causal_split(api, torch, steps=2):
+    """The whole causal 128k ring (8 ranks x chunks of 16384, 32 heads) under the
+    contiguous split and under the zigzag split: per-rank launch time, the sum
+    (the ring on one GPU) and the slowest rank (what bounds a step when every
+    rank has its own GPU)."""
+    from sequence_kv_chunk_amd.synth import WORKLOADS, device_attention_inputs
+    res = {}
+    for split, name in (("contiguous", "ring_bf16_128k_causal"), ("zigzag", "zigzag_bf16_128k_causal")):
+        w = WORKLOADS[name]
+        x = device_attention_inputs(w)
+        B, H, n, d = x["q"].shape[1:]
+        o = torch.empty((B, H, n, d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(B * H * n, dtype=torch.float32, device="cuda")
+        work = (torch.empty((B, H, n // 2, d), dtype=torch.float32, device="cuda"),
+                torch.empty(B * H * (n // 2), dtype=torch.float32, device="cuda"))
+        rank_ms = []
+        for r in range(w.P):
+            if split == "zigzag":
+                fn = lambda: api.ra_zigzag_attention(x["q"][r], x["k"], x["v"], o, lse, rank=r, work=work)
+            else:
+                fn = lambda: api.ra_ring_attention(x["q"][r], x["k"], x["v"], o, lse, rank=r, causal=True)
+            fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            rank_ms.append(e0.elapsed_time(e1) / steps)
+        tot = sum(rank_ms)
+        res[split] = {"rank_ms": [round(t, 3) for t in rank_ms], "ring_ms_one_gpu": round(tot, 3),
+                      "slowest_rank_ms": round(max(rank_ms), 3),
+                      "max_over_min": round(max(rank_ms) / min(rank_ms), 2),
+                      "TFLOP/s": round(w.flops() / (tot * 1e-3) / 1e12, 1), "flops": w.flops()}
+        del x, o, lse, work
+        torch.cuda.empty_cache()
+    res["slowest_rank_speedup_zigzag"] = round(res["contiguous"]["slowest_rank_ms"] /
+                                               res["zigzag"]["slowest_rank_ms"], 2)
+    res["workload"] = ("causal 131072 tokens, 8 ranks, B=1, 32 heads, d=128, bf16; contiguous chunks of 16384 "
+                       "vs zigzag pieces r and 15-r of 8192")
+    return res
+
+
 def cpu_baseline(x_dev, w, torch, budget_rows=4096, heads=16):
     """The fp64 oracle on a bounded sample of the workload: query chunk 0
     (4096 rows) of the first `heads` heads against all 32768 keys."""
@@ -250,6 +294,8 @@ def main():
             extras["ulysses_share_gqa_128k_causal"] = bench_attention_extra(api, torch,
                                                                             "ulysses_share_gqa_128k_causal")
             log(f"ulysses share: {extras['ulysses_share_gqa_128k_causal']}")
+            extras["causal_128k_ring_split"] = bench_causal_split(api, torch)
+            log(f"causal split: {extras['causal_128k_ring_split']}")
         except Exception as e:  # extras never hide the main line
             extras["error"] = repr(e)
     if not args.no_cpu:

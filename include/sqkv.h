@@ -136,6 +136,45 @@ sqkv_status ra_ring_attention(sqkv_view q, sqkv_view k, sqkv_view v,
                               float scale, int causal, void* stream);
 
 /*
+ * ra_zigzag_attention -- causal ring attention for one virtual rank under the
+ * zigzag assignment of the sequence.  [UL], opening paragraph, names
+ * Ring/ZigZag among the context-parallel methods without defining it; the
+ * reading taken here is the usual one: the sequence of length L is cut into
+ * 2P equal pieces of c = L/(2P) tokens and rank r holds pieces r and
+ * 2P-1-r, so that under a causal mask every rank has the same work ((2P-1)
+ * fully visible piece pairs and 2 diagonal ones) instead of rank P-1 doing
+ * 2P-1 times the work of rank 0.  A rank's local shard is its two pieces one
+ * after the other: n = 2c rows, rows 0..c-1 at positions r*c .. r*c+c-1 and
+ * rows c..2c-1 at positions (2P-1-r)*c .. .
+ *
+ *   q        [B, Hq, n, d]  in_dtype      the rank's local shard
+ *   k, v     [B, Hkv, n, d] in_dtype      shard 0 of the pool (same zigzag
+ *                                         layout); shard j starts
+ *                                         j*k_chunk_stride (v_chunk_stride)
+ *                                         elements after it
+ *   o        [B, Hq, n, d]  out_dtype     result
+ *   lse      [B, Hq, n]     float32       result (natural log)
+ *   work_o   [B, Hq, n/2, d] float32, dense (element (b,h,t,e) at
+ *            ((b*Hq + h)*(n/2) + t)*d + e), and
+ *   work_lse [B, Hq, n/2]   float32, dense: caller-owned scratch, 16- and
+ *            4-byte aligned, overlapping no other argument; contents on entry
+ *            are ignored and on return unspecified.
+ *
+ * Enqueues three launches on `stream`: the early piece against the early
+ * pieces of ranks r, r-1, .., 0; the late piece against all early pieces
+ * (into the scratch); the late piece against the late pieces of ranks r, r+1,
+ * .., P-1, merged with the scratch.  Same support and status codes as
+ * ra_ring_attention; additionally EINVAL for odd n and null or overlapping
+ * scratch.
+ */
+sqkv_status ra_zigzag_attention(sqkv_view q, sqkv_view k, sqkv_view v,
+                                int64_t k_chunk_stride, int64_t v_chunk_stride,
+                                sqkv_view o, float* lse, float* work_o, float* work_lse,
+                                int B, int Hq, int Hkv, int n, int d, int P, int rank,
+                                sqkv_dtype in_dtype, sqkv_dtype out_dtype,
+                                float scale, void* stream);
+
+/*
  * ra_lse_merge -- the online-softmax merge of two partial attentions over
  * disjoint key sets ([RA] section 5, the rescale of the running output and
  * normaliser by the exponent of the change in the running maximum), in the

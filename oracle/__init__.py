@@ -18,6 +18,8 @@ the pages by eye:
   definition;
 * ``ulysses``    -- the sequence<->head all-to-all as an explicit index copy,
   including GQA key/value head replication;
+* ``zigzag``     -- the zigzag split of the sequence over ring ranks and the
+  causal attention of one rank's shard under it;
 * ``closed_form``-- the materialised attention-matrix memory formula.
 
 Sources (the pages):
@@ -32,16 +34,18 @@ facts other than itself (brute-force loops, closed forms, library routines,
 the pages' printed figure); ``tests/test_oracle_mutants.py`` shows that
 plausible mistakes fail those pins.  No function is left "parity unpinned".
 """
-from .attention import attention_fp64, unmasked_pairs
+from .attention import attention_fp64, attention_at_positions_fp64, unmasked_pairs
 from .ring import lse_merge_fp64, ring_attention_fp64, ring_visit_order
 from .ulysses import (seq_to_head_naive, head_to_seq_naive, replicated_head_source,
                       check_ulysses_shapes)
 from .closed_form import attn_matrix_bytes
+from .zigzag import zigzag_positions, zigzag_shard, zigzag_attention_fp64, zigzag_block_classes
 
 __all__ = [
-    "attention_fp64", "unmasked_pairs",
+    "attention_fp64", "attention_at_positions_fp64", "unmasked_pairs",
     "lse_merge_fp64", "ring_attention_fp64", "ring_visit_order",
     "seq_to_head_naive", "head_to_seq_naive", "replicated_head_source",
     "check_ulysses_shapes",
     "attn_matrix_bytes",
+    "zigzag_positions", "zigzag_shard", "zigzag_attention_fp64", "zigzag_block_classes",
 ]

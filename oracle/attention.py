@@ -77,3 +77,44 @@ def unmasked_pairs(n_q: int, n_k: int, causal: bool, q_pos0: int = 0, k_pos0: in
         # keys u with k_pos0 + u <= q_pos0 + t
         tot += max(0, min(n_k, q_pos0 + t - k_pos0 + 1))
     return tot
+
+
+def attention_at_positions_fp64(q, k, v, q_pos, k_pos, scale: float = 1.0, row_block: int = 256):
+    """Causal softmax attention with explicit global positions.
+
+    Same definition as ``attention_fp64`` with ``causal=True``, for tokens whose
+    positions are not one contiguous run: query row t sits at ``q_pos[t]``, key
+    u at ``k_pos[u]``, and u is visible to t iff ``k_pos[u] <= q_pos[t]``.
+    q: [B, Hq, n_q, d], k and v: [B, Hkv, n_k, d]; q_pos [n_q], k_pos [n_k].
+    Returns (O [B, Hq, n_q, d], lse [B, Hq, n_q]) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    k_pos = np.asarray(k_pos, dtype=np.int64)
+    B, Hq, n_q, d = q.shape
+    Hkv, n_k = k.shape[1], k.shape[2]
+    if q_pos.shape != (n_q,) or k_pos.shape != (n_k,):
+        raise ValueError("one position per query row and per key")
+    if Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = Hq // Hkv
+    O = np.zeros((B, Hq, n_q, d), dtype=np.float64)
+    lse = np.full((B, Hq, n_q), -np.inf, dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            for r0 in range(0, n_q, row_block):
+                r1 = min(n_q, r0 + row_block)
+                s = scale * (q[b, h, r0:r1] @ k[b, g].T)
+                visible = k_pos[None, :] <= q_pos[r0:r1, None]
+                s = np.where(visible, s, -np.inf)
+                any_vis = visible.any(axis=1)
+                m = np.where(any_vis, s.max(axis=1, initial=-np.inf), 0.0)
+                w = np.where(visible, np.exp(s - m[:, None]), 0.0)
+                l = w.sum(axis=1)
+                safe_l = np.where(any_vis, l, 1.0)
+                O[b, h, r0:r1] = np.where(any_vis[:, None], (w @ v[b, g]) / safe_l[:, None], 0.0)
+                lse[b, h, r0:r1] = np.where(any_vis, m + np.log(safe_l), -np.inf)
+    return O, lse

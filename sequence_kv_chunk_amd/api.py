@@ -50,6 +50,9 @@ _lib.ra_chunk_attention.argtypes = [_V, _V, _V, _V, _vp, _V, _vp, _c_int, _c_int
 _lib.ra_ring_attention.restype = _c_int
 _lib.ra_ring_attention.argtypes = [_V, _V, _V, _c_i64, _c_i64, _V, _vp, _c_int, _c_int, _c_int, _c_int,
                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _vp]
+_lib.ra_zigzag_attention.restype = _c_int
+_lib.ra_zigzag_attention.argtypes = [_V, _V, _V, _c_i64, _c_i64, _V, _vp, _vp, _vp, _c_int, _c_int, _c_int,
+                                     _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_f, _vp]
 _lib.ra_lse_merge.restype = _c_int
 _lib.ra_lse_merge.argtypes = [_V, _vp, _c_int, _V, _vp, _c_int, _V, _vp, _c_int, _c_int, _c_int, _c_int,
                               _c_int, _vp]
@@ -58,8 +61,8 @@ _lib.ulysses_seq_to_head.argtypes = [_vp, _vp, _c_int, _c_i64, _c_int, _c_int, _
 _lib.ulysses_head_to_seq.restype = _c_int
 _lib.ulysses_head_to_seq.argtypes = [_vp, _vp, _c_int, _c_i64, _c_int, _c_int, _c_int, _vp]
 
-EXPORTED = ("ra_chunk_attention", "ra_ring_attention", "ra_lse_merge", "ulysses_seq_to_head",
-            "ulysses_head_to_seq", "sqkv_last_error")
+EXPORTED = ("ra_chunk_attention", "ra_ring_attention", "ra_zigzag_attention", "ra_lse_merge",
+            "ulysses_seq_to_head", "ulysses_head_to_seq", "sqkv_last_error")
 
 
 def _check(status: int):
@@ -152,6 +155,35 @@ def ra_ring_attention(q, k_pool, v_pool, o, lse, *, rank: int, scale: float = 1.
                                     v_pool.stride(0), _view(o), _lse_ptr(lse, B * Hq * n),
                                     B, Hq, k_pool.shape[2], n, d, P, int(rank), _dtype_code(q),
                                     _dtype_code(o), float(scale), int(bool(causal)), _stream(q))
+    _check(st)
+
+
+def ra_zigzag_attention(q, k_pool, v_pool, o, lse, *, rank: int, scale: float = 1.0, work=None):
+    """Causal ring attention of virtual rank ``rank`` under the zigzag split:
+    ``q`` ([B, Hq, n, d]) holds the rank's pieces ``rank`` and ``2P-1-rank``
+    of the 2P-piece sequence, ``k_pool``/``v_pool`` ([P, B, Hkv, n, d]) every
+    rank's shard in the same layout.  ``work`` = (work_o fp32 [B, Hq, n/2, d],
+    work_lse fp32 [B*Hq*n/2]) scratch; allocated here when not given."""
+    if k_pool.dim() != 5 or v_pool.shape != k_pool.shape:
+        raise SqkvError(SQKV_EINVAL, "k_pool, v_pool must be [P, B, Hkv, n, d]")
+    _same_device(q, k_pool, v_pool, o, lse)
+    P = k_pool.shape[0]
+    B, Hq, n, d = q.shape
+    if tuple(o.shape) != (B, Hq, n, d) or k_pool.shape[3] != n or k_pool.shape[1] != B:
+        raise SqkvError(SQKV_EINVAL, "shapes disagree")
+    if work is None:
+        work = (torch.empty((B, Hq, n // 2, d), dtype=torch.float32, device=q.device),
+                torch.empty(B * Hq * (n // 2), dtype=torch.float32, device=q.device))
+    wo, wl = work
+    _same_device(q, wo, wl)
+    if wo.dtype != torch.float32 or wl.dtype != torch.float32 or not wo.is_contiguous() or not wl.is_contiguous() \
+            or wo.numel() != B * Hq * (n // 2) * d or wl.numel() != B * Hq * (n // 2):
+        raise SqkvError(SQKV_EINVAL, "work must be contiguous fp32 [B, Hq, n/2, d] and [B*Hq*n/2]")
+    with torch.cuda.device(q.device):
+        st = _lib.ra_zigzag_attention(_view(q), _view(k_pool[0]), _view(v_pool[0]), k_pool.stride(0),
+                                      v_pool.stride(0), _view(o), _lse_ptr(lse, B * Hq * n), wo.data_ptr(),
+                                      wl.data_ptr(), B, Hq, k_pool.shape[2], n, d, P, int(rank), _dtype_code(q),
+                                      _dtype_code(o), float(scale), _stream(q))
     _check(st)
 
 

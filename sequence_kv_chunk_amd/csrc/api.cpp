@@ -170,6 +170,7 @@ sqkv::AttnParams make_params(const sqkv_view& q, const sqkv_view& k, const sqkv_
   p.causal = causal ? 1 : 0;
   p.q_pos0 = q_pos0;
   p.k_pos0 = k_pos0;
+  p.lse_in_hs = p.lse_out_hs = n_q;   // dense [B, Hq, n_q]
   // a single chunk; ra_ring_attention widens this to the ring visit
   p.k_cs = p.v_cs = 0;
   p.k_posstride = 0;
@@ -228,6 +229,99 @@ SQKV_EXPORT sqkv_status ra_ring_attention(sqkv_view q, sqkv_view k, sqkv_view v,
   p.rank = rank;
   p.nseg = causal ? rank + 1 : P;
   return hip_status(launch_attention(p, d, in_dtype, (hipStream_t)stream), "ra_ring_attention launch");
+}
+
+SQKV_EXPORT sqkv_status ra_zigzag_attention(sqkv_view q, sqkv_view k, sqkv_view v, int64_t k_chunk_stride,
+                                            int64_t v_chunk_stride, sqkv_view o, float* lse, float* work_o,
+                                            float* work_lse, int B, int Hq, int Hkv, int n, int d, int P,
+                                            int rank, sqkv_dtype in_dtype, sqkv_dtype out_dtype, float scale,
+                                            void* stream) {
+  if (P < 1 || rank < 0 || rank >= P) return fail(SQKV_EINVAL, "need P >= 1 and 0 <= rank < P (P=%d rank=%d)", P, rank);
+  if (n % 2) return fail(SQKV_EINVAL, "the local shard length n=%d must be even (two pieces)", n);
+  if (k_chunk_stride < 0 || v_chunk_stride < 0) return fail(SQKV_EINVAL, "negative chunk stride");
+  const int ieb = dtype_bytes(in_dtype);
+  if ((k_chunk_stride * ieb) % 16 || (v_chunk_stride * ieb) % 16)
+    return fail(SQKV_EUNSUPPORTED, "chunk strides must be multiples of 16 bytes");
+  AttnCheck a{q, k, v, sqkv_view{nullptr, 0, 0, 0}, o, nullptr, lse, B, Hq, Hkv, n, n,
+              (int64_t)(P - 1) * std::max(k_chunk_stride, v_chunk_stride) * ieb, d,
+              in_dtype, SQKV_F32, out_dtype, scale};
+  sqkv_status st = check_attention(a);
+  if (st != SQKV_OK || n == 0) return st;
+  const int c = n / 2;
+  if (!work_o || !work_lse) return fail(SQKV_EINVAL, "null work_o or work_lse");
+  if (((uintptr_t)work_o) % 16 || ((uintptr_t)work_lse) % 4)
+    return fail(SQKV_EUNSUPPORTED, "work_o must be 16-byte and work_lse 4-byte aligned");
+  {
+    const int64_t rows = (int64_t)B * Hq * c;
+    Range rw = dense_range(work_o, rows * d, 4), rwl = dense_range(work_lse, rows, 4);
+    Range rq = view_range(q, B, Hq, n, d, ieb), ro = view_range(o, B, Hq, n, d, dtype_bytes(out_dtype));
+    Range rl = dense_range(lse, (int64_t)B * Hq * n, 4);
+    Range rk = view_range(k, B, Hkv, n, d, ieb), rv = view_range(v, B, Hkv, n, d, ieb);
+    rk.hi += a.kv_extent_extra_bytes;
+    rv.hi += a.kv_extent_extra_bytes;
+    for (const Range* r : {&rq, &ro, &rl, &rk, &rv})
+      if (overlap(rw, *r) || overlap(rwl, *r)) return fail(SQKV_EINVAL, "work buffers overlap q, k, v, o or lse");
+    if (overlap(rw, rwl)) return fail(SQKV_EINVAL, "work_o overlaps work_lse");
+  }
+  auto rows_from = [](sqkv_view x, int64_t t0, int eb) {
+    x.ptr = static_cast<char*>(x.ptr) + t0 * x.sn * eb;
+    return x;
+  };
+  const int oeb = dtype_bytes(out_dtype);
+  const sqkv_view q_early = q, q_late = rows_from(q, c, ieb);
+  const sqkv_view o_early = o, o_late = rows_from(o, c, oeb);
+  const sqkv_view w{work_o, (int64_t)Hq * c * d, (int64_t)c * d, d};
+  const sqkv_view none{nullptr, 0, 0, 0};
+  hipStream_t hs = (hipStream_t)stream;
+
+  // 1. early piece (positions rank*c ..) against the early pieces of ranks
+  //    rank, rank-1, .., 0: the own piece on its diagonal, the rest in the past
+  sqkv::AttnParams p1 = make_params(q_early, k, v, none, nullptr, o_early, lse, B, Hq, Hkv, c, c, SQKV_F32,
+                                    out_dtype, scale, 1, (int64_t)rank * c, 0);
+  p1.k_cs = k_chunk_stride;
+  p1.v_cs = v_chunk_stride;
+  p1.k_posstride = c;
+  p1.P = P;
+  p1.rank = rank;
+  p1.nseg = rank + 1;
+  p1.lse_out_hs = n;
+  hipError_t e = launch_attention(p1, d, in_dtype, hs);
+  if (e != hipSuccess) return hip_status(e, "ra_zigzag_attention launch 1");
+
+  // 2. late piece (positions (2P-1-rank)*c ..) against every early piece, all
+  //    in its past: an unmasked ring visit, partial into the work buffers
+  sqkv::AttnParams p2 = make_params(q_late, k, v, none, nullptr, w, work_lse, B, Hq, Hkv, c, c, SQKV_F32,
+                                    SQKV_F32, scale, 0, 0, 0);
+  p2.k_cs = k_chunk_stride;
+  p2.v_cs = v_chunk_stride;
+  p2.k_posstride = c;
+  p2.P = P;
+  p2.rank = rank;
+  p2.nseg = P;
+  e = launch_attention(p2, d, in_dtype, hs);
+  if (e != hipSuccess) return hip_status(e, "ra_zigzag_attention launch 2");
+
+  // 3. late piece against the late pieces of ranks rank, rank+1, .., P-1
+  //    (positions (2P-1-j)*c: the own piece on its diagonal, the rest in the
+  //    past), merged with the partial of step 2.  Numbered j' = P-1-j the late
+  //    pieces sit at positions (P + j')*c and the visit is the causal ring of
+  //    rank P-1-rank over a pool that starts at rank P-1's late piece and
+  //    steps backwards through the shards.
+  const sqkv_view k3 = rows_from(sqkv_view{static_cast<char*>(k.ptr) + (int64_t)(P - 1) * k_chunk_stride * ieb,
+                                           k.sb, k.sh, k.sn}, c, ieb);
+  const sqkv_view v3 = rows_from(sqkv_view{static_cast<char*>(v.ptr) + (int64_t)(P - 1) * v_chunk_stride * ieb,
+                                           v.sb, v.sh, v.sn}, c, ieb);
+  sqkv::AttnParams p3 = make_params(q_late, k3, v3, w, work_lse, o_late, lse + c, B, Hq, Hkv, c, c, SQKV_F32,
+                                    out_dtype, scale, 1, (int64_t)(2 * P - 1 - rank) * c, (int64_t)P * c);
+  p3.k_cs = -k_chunk_stride;
+  p3.v_cs = -v_chunk_stride;
+  p3.k_posstride = c;
+  p3.P = P;
+  p3.rank = P - 1 - rank;
+  p3.nseg = P - rank;
+  p3.lse_in_hs = c;
+  p3.lse_out_hs = n;
+  return hip_status(launch_attention(p3, d, in_dtype, hs), "ra_zigzag_attention launch 3");
 }
 
 SQKV_EXPORT sqkv_status ra_lse_merge(sqkv_view o_a, const float* lse_a, sqkv_dtype a_dtype, sqkv_view o_b,

@@ -619,9 +619,9 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     if (row < p.n_q) {
       const float lse_j = (lt > 0.f) ? (m_run + log2f(lt)) * kLn2 : kNegInf;
       const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
-      const int64_t srow = ((int64_t)b * p.Hq + h) * p.n_q + row;
+      const int64_t bh_row = (int64_t)b * p.Hq + h;
       float wi = 0.f, wj = 1.f, lse = lse_j;
-      if (p.o_in != nullptr) lse = lse_merge_weights(p.lse_in[srow], lse_j, wi, wj);
+      if (p.o_in != nullptr) lse = lse_merge_weights(p.lse_in[bh_row * p.lse_in_hs + row], lse_j, wi, wj);
       const float f = wj * inv;
       const int64_t ooff = b * p.oo_sb + h * p.oo_sh + (int64_t)row * p.oo_sn;
       const int64_t ioff = b * p.oi_sb + h * p.oi_sh + (int64_t)row * p.oi_sn;
@@ -641,7 +641,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
           }
           store4(p.o_out, ooff + d0, p.out_dtype, y);
         }
-      if (hi == 0) p.lse_out[srow] = lse;
+      if (hi == 0) p.lse_out[bh_row * p.lse_out_hs + row] = lse;
     }
   }
 }

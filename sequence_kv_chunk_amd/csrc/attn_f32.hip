@@ -102,9 +102,9 @@ __global__ void __launch_bounds__(kRows) attn_f32_kernel(AttnParams p) {
   // chunk partial: normalised output and natural-log lse
   float lse_j = (l > 0.f) ? (m + log2f(l)) * kLn2 : kNegInf;
   float inv = (l > 0.f) ? 1.f / l : 0.f;
-  const int64_t row = ((int64_t)b * p.Hq + h) * p.n_q + t;
+  const int64_t bh_row = (int64_t)b * p.Hq + h;
   float wi = 0.f, wj = 1.f, lse = lse_j;
-  if (p.o_in != nullptr) lse = lse_merge_weights(p.lse_in[row], lse_j, wi, wj);
+  if (p.o_in != nullptr) lse = lse_merge_weights(p.lse_in[bh_row * p.lse_in_hs + t], lse_j, wi, wj);
   const int64_t ooff = b * p.oo_sb + h * p.oo_sh + (int64_t)t * p.oo_sn;
   const int64_t ioff = b * p.oi_sb + h * p.oi_sh + (int64_t)t * p.oi_sn;
 #pragma unroll
@@ -120,7 +120,7 @@ __global__ void __launch_bounds__(kRows) attn_f32_kernel(AttnParams p) {
     }
     store4(p.o_out, ooff + e, p.out_dtype, y);
   }
-  p.lse_out[row] = lse;
+  p.lse_out[bh_row * p.lse_out_hs + t] = lse;
 }
 
 }  // namespace

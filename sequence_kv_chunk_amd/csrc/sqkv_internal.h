@@ -12,8 +12,10 @@ enum DType : int { kF32 = 0, kBF16 = 1 };
 // One attention launch: a query chunk against `nseg` key/value chunks visited
 // in ring order.  Views are [B, H, n, d] with element strides.  Visit s reads
 // chunk j = (rank - s) mod P, which starts j*k_cs (j*v_cs) elements after k
-// (v) and whose key 0 sits at global position k_pos0 + j*k_posstride.  A
-// single chunk is nseg = P = 1, rank = 0.
+// (v; the chunk strides may be negative) and whose key 0 sits at global
+// position k_pos0 + j*k_posstride.  With a causal mask only the first chunk
+// visited (the rank's own) may hold keys after a query; later ones must lie
+// entirely in its past.  A single chunk is nseg = P = 1, rank = 0.
 struct AttnParams {
   const void* q;
   const void* k;
@@ -30,6 +32,8 @@ struct AttnParams {
   void* o_out;
   int64_t oo_sb, oo_sh, oo_sn;
   float* lse_out;
+  // lse of query row t of (b, h) is lse_*[(b*Hq + h)*lse_*_hs + t]
+  int64_t lse_in_hs, lse_out_hs;
   int B, Hq, Hkv, n_q, n_k;
   int group;          // Hq / Hkv
   int acc_dtype;      // dtype of o_in

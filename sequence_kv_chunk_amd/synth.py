@@ -90,6 +90,8 @@ class AttnWorkload:
     layout "bhnd": Q is one query chunk [B, Hq, n_q, d]; K and V are a pool of
     P resident chunks [P][B, Hkv, n, d] (shard-major), as the ring sees them.
     layout "shd": one Ulysses head share, Q [S, Hq, d], K/V [S, Hkv, d].
+    layout "zigzag": as "bhnd", but every shard of n tokens holds the two
+    sequence pieces r and 2P-1-r of n/2 tokens each (the zigzag split).
     """
     name: str
     seed: int
@@ -121,6 +123,11 @@ class AttnWorkload:
             if self.layout == "shd":
                 # a single share: one "chunk" of the full length
                 tot += self.L * (self.L + 1) // 2 if self.causal else self.L * self.L
+                continue
+            if self.layout == "zigzag":
+                # 2P-1 fully visible piece pairs and 2 diagonal ones per rank
+                c = n // 2
+                tot += (2 * self.P - 1) * c * c + c * (c + 1) if self.causal else n * self.L
                 continue
             for j in range(self.P):
                 if not self.causal or j < i:
@@ -164,6 +171,14 @@ WORKLOADS = {
     "ring_bf16_128k_rank7_causal": AttnWorkload(
         "ring_bf16_128k_rank7_causal", 4, "bf16", 1, 32, 32, 128, 131072, 8,
         True, True, "bhnd", (7,)),
+    # the whole causal 128k ring (all 8 ranks), contiguous chunks of 16384
+    "ring_bf16_128k_causal": AttnWorkload(
+        "ring_bf16_128k_causal", 4, "bf16", 1, 32, 32, 128, 131072, 8,
+        True, True, "bhnd"),
+    # the same ring with the zigzag split: rank r holds pieces r and 15-r of 8192
+    "zigzag_bf16_128k_causal": AttnWorkload(
+        "zigzag_bf16_128k_causal", 6, "bf16", 1, 32, 32, 128, 131072, 8,
+        True, True, "zigzag"),
     # one GPU's Ulysses share: full 128k sequence, 4 query heads, 1 KV head
     "ulysses_share_gqa_128k_causal": AttnWorkload(
         "ulysses_share_gqa_128k_causal", 5, "bf16", 1, 4, 1, 128, 131072, 1,

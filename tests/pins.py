@@ -350,6 +350,111 @@ def pin_ulysses_limits(orc):
         raise AssertionError("limit not enforced")
 
 
+# ----------------------------------------------------------------------------
+# attention at explicit positions, zigzag split
+# ----------------------------------------------------------------------------
+def _bruteforce_pos(q, k, v, q_pos, k_pos, scale):
+    """Pure-Python loops: key u visible to query t iff k_pos[u] <= q_pos[t]."""
+    B, Hq, nq, d = q.shape
+    Hkv, nk = k.shape[1], k.shape[2]
+    grp = Hq // Hkv
+    O = np.zeros((B, Hq, nq, d))
+    lse = np.full((B, Hq, nq), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // grp
+            for t in range(nq):
+                keys = [u for u in range(nk) if int(k_pos[u]) <= int(q_pos[t])]
+                if not keys:
+                    continue
+                s = {u: scale * sum(float(q[b, h, t, e]) * float(k[b, g, u, e]) for e in range(d)) for u in keys}
+                mx = max(s.values())
+                w = {u: math.exp(s[u] - mx) for u in keys}
+                tot = sum(w.values())
+                for e in range(d):
+                    O[b, h, t, e] = sum(w[u] * float(v[b, g, u, e]) for u in keys) / tot
+                lse[b, h, t] = mx + math.log(tot)
+    return O, lse
+
+
+def pin_attention_at_positions(orc):
+    rng = np.random.default_rng(31)
+    for B, Hq, Hkv, nq, nk, d in [(1, 2, 1, 5, 7, 3), (2, 4, 2, 4, 6, 2)]:
+        q = rng.standard_normal((B, Hq, nq, d))
+        k = rng.standard_normal((B, Hkv, nk, d))
+        v = rng.standard_normal((B, Hkv, nk, d))
+        q_pos = rng.permutation(12)[:nq]
+        k_pos = rng.permutation(12)[:nk]
+        q_pos[0] = -1                                  # a query that sees no key
+        O, lse = orc.attention_at_positions_fp64(q, k, v, q_pos, k_pos, scale=0.8)
+        Ob, lb = _bruteforce_pos(q, k, v, q_pos, k_pos, 0.8)
+        _close(O, Ob, 1e-12, "O at positions vs brute force")
+        _close(lse, lb, 1e-12, "lse at positions vs brute force")
+        # reordering the keys together with their positions changes nothing
+        perm = rng.permutation(nk)
+        O2, l2 = orc.attention_at_positions_fp64(q, k[:, :, perm], v[:, :, perm], q_pos, k_pos[perm], scale=0.8)
+        _close(O2, O, 1e-12, "key order")
+        _close(l2, lse, 1e-12, "key order lse")
+
+
+def pin_zigzag_positions(orc):
+    for P in range(1, 7):
+        for c in (1, 3, 4):
+            L = 2 * P * c
+            allpos = np.concatenate([orc.zigzag_positions(r, P, c) for r in range(P)])
+            assert sorted(allpos.tolist()) == list(range(L)), "every token on exactly one rank"
+            for r in range(P):
+                pos = orc.zigzag_positions(r, P, c)
+                assert pos.shape == (2 * c,)
+                # piece r then piece 2P-1-r, each a contiguous run of c tokens
+                assert pos.tolist() == list(range(r * c, r * c + c)) + \
+                    list(range((2 * P - 1 - r) * c, (2 * P - r) * c))
+    # P = 1: the shard is the whole sequence in natural order
+    assert orc.zigzag_positions(0, 1, 5).tolist() == list(range(10))
+    x = np.arange(2 * 3 * 2 * 4).reshape(1, 2 * 3 * 2, 4)            # [1, L=12, 4], P=3, c=2
+    sh = orc.zigzag_shard(x, 3, axis=1)
+    assert sh.shape == (3, 1, 4, 4)
+    assert sh[1, 0, :, 0].tolist() == [8, 12, 32, 36], "rank 1 holds tokens 2,3 and 8,9"
+
+
+def pin_zigzag_equals_full(orc):
+    """Every rank's zigzag shard result, put back in natural order, equals one
+    causal softmax over the whole sequence (the contiguous definition)."""
+    rng = np.random.default_rng(33)
+    for P, c, B, Hq, Hkv, d, scale in [(1, 3, 1, 2, 1, 4, 1.0), (2, 2, 1, 2, 2, 3, 0.7),
+                                       (3, 2, 2, 4, 2, 2, 1.2), (4, 1, 1, 2, 1, 3, 1.0)]:
+        L = 2 * P * c
+        q = rng.standard_normal((B, Hq, L, d))
+        k = rng.standard_normal((B, Hkv, L, d)) * 1.5
+        v = rng.standard_normal((B, Hkv, L, d))
+        Of, lf = orc.attention_fp64(q, k, v, scale=scale, causal=True)
+        kp = np.stack([k[:, :, [t for t in range(L) if (t // c) in (j, 2 * P - 1 - j)]] for j in range(P)])
+        vp = np.stack([v[:, :, [t for t in range(L) if (t // c) in (j, 2 * P - 1 - j)]] for j in range(P)])
+        for r in range(P):
+            rows = [t for t in range(L) if (t // c) in (r, 2 * P - 1 - r)]
+            O, lse = orc.zigzag_attention_fp64(q[:, :, rows], kp, vp, r, scale=scale)
+            _close(O, Of[:, :, rows], 1e-12, f"zigzag O P={P} rank {r}")
+            _close(lse, lf[:, :, rows], 1e-12, f"zigzag lse P={P} rank {r}")
+
+
+def pin_zigzag_balance(orc):
+    """Equal causal work on every rank: (2P-1) full piece pairs and 2 diagonal
+    ones, i.e. 2P*c^2 + c visible pairs, counted directly from positions."""
+    for P in range(1, 9):
+        for c in (1, 2, 5):
+            for r in range(P):
+                cls = [x[3] for x in orc.zigzag_block_classes(r, P)]
+                assert cls.count("full") == 2 * P - 1 and cls.count("diagonal") == 2
+                assert cls.count("skip") == 4 * P - (2 * P - 1) - 2
+                qp = orc.zigzag_positions(r, P, c)
+                kp = np.concatenate([orc.zigzag_positions(j, P, c) for j in range(P)])
+                pairs = int(np.sum(kp[None, :] <= qp[:, None]))
+                assert pairs == 2 * P * c * c + c, (P, c, r, pairs)
+                for qa, j, kb, cl in orc.zigzag_block_classes(r, P):
+                    assert cl == ("full" if kb < qa else "diagonal" if kb == qa else "skip")
+                    assert kb in (j, 2 * P - 1 - j) and qa in (r, 2 * P - 1 - r)
+
+
 def pin_closed_form(orc):
     g = _load("attn_matrix_memory.json")
     b = orc.attn_matrix_bytes(g["L"], g["heads"], g["elem_bytes"])
@@ -373,4 +478,8 @@ ALL_PINS = [
     pin_ulysses_replication,
     pin_ulysses_limits,
     pin_closed_form,
+    pin_attention_at_positions,
+    pin_zigzag_positions,
+    pin_zigzag_equals_full,
+    pin_zigzag_balance,
 ]

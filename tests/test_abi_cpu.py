@@ -34,8 +34,8 @@ def lib():
 
 def test_header_declares_the_api():
     names = declared_functions()
-    for n in ("ra_chunk_attention", "ra_ring_attention", "ra_lse_merge", "ulysses_seq_to_head",
-              "ulysses_head_to_seq", "sqkv_last_error"):
+    for n in ("ra_chunk_attention", "ra_ring_attention", "ra_zigzag_attention", "ra_lse_merge",
+              "ulysses_seq_to_head", "ulysses_head_to_seq", "sqkv_last_error"):
         assert n in names
 
 
@@ -70,6 +70,7 @@ def _setup(lib):
     i, i64, f, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
     lib.ra_chunk_attention.argtypes = [V, V, V, V, vp, V, vp, i, i, i, i, i, i, i, i, i, f, i, i64, i64, vp]
     lib.ra_ring_attention.argtypes = [V, V, V, i64, i64, V, vp, i, i, i, i, i, i, i, i, i, f, i, vp]
+    lib.ra_zigzag_attention.argtypes = [V, V, V, i64, i64, V, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, vp]
     lib.ra_lse_merge.argtypes = [V, vp, i, V, vp, i, V, vp, i, i, i, i, i, vp]
     lib.ulysses_seq_to_head.argtypes = [vp, vp, i, i64, i, i, i, i, vp]
     lib.ulysses_head_to_seq.argtypes = [vp, vp, i, i64, i, i, i, vp]
@@ -151,6 +152,28 @@ def test_ring_rejects(lib):
     # the pool of 4 chunks reaches into o when o sits right after chunk 0
     assert lib.ra_ring_attention(q, k, v, cs, cs, _dense(2 * GB + 2 * cs, 4, 64, 128), lse, 1, 4, 4, 64,
                                  128, 4, 1, BF16, F32, 1.0, 0, None) == EINVAL
+
+
+@no_gpu
+def test_zigzag_rejects(lib):
+    _setup(lib)
+    q, k, v = _dense(1 * GB, 4, 64, 128), _dense(2 * GB, 4, 64, 128), _dense(3 * GB, 4, 64, 128)
+    o, lse = _dense(4 * GB, 4, 64, 128), 5 * GB
+    cs = 4 * 64 * 128
+
+    def call(P=4, rank=0, n=64, wo=6 * GB, wl=7 * GB, kcs=cs):
+        return lib.ra_zigzag_attention(q, k, v, kcs, cs, o, lse, wo, wl, 1, 4, 4, n, 128, P, rank, BF16, BF16,
+                                       1.0, None)
+
+    assert call(rank=4) == EINVAL
+    assert call(P=0) == EINVAL
+    assert call(n=63) == EINVAL                  # two pieces of equal length
+    assert call(wo=None) == EINVAL
+    assert call(wl=None) == EINVAL
+    assert call(wo=6 * GB + 4) == EUNSUP         # work_o not 16-byte aligned
+    assert call(wo=4 * GB + 64) == EINVAL        # scratch inside o
+    assert call(wl=5 * GB + 16) == EINVAL        # scratch inside lse
+    assert call(kcs=cs + 3) == EUNSUP
 
 
 @no_gpu

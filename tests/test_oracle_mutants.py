@@ -42,6 +42,14 @@ MUTANTS = [
     ("ulysses.py", "src[r, p * n:(p + 1) * n, hl, :]", "src[p, r * n:(r + 1) * n, hl, :]"),
     ("ulysses.py", "dst[p, :, r * Hl + hl, :]", "dst[p, :, hl * P + r, :]"),
     ("closed_form.py", "L * L * elem_bytes * heads", "L * elem_bytes * heads * 1024"),
+    ("attention.py", "visible = k_pos[None, :] <= q_pos[r0:r1, None]", "visible = k_pos[None, :] < q_pos[r0:r1, None]"),
+    ("attention.py", "(w @ v[b, g]) / safe_l[:, None]", "(w @ v[b, h // Hkv]) / safe_l[:, None]"),
+    ("zigzag.py", "late = (2 * P - 1 - rank) * c", "late = (2 * P - rank) * c"),
+    ("zigzag.py", "late = (2 * P - 1 - rank) * c", "late = (P + rank) * c"),
+    ("zigzag.py", "np.concatenate([early, late])", "np.concatenate([late, early])"),
+    ("zigzag.py", "cls = \"full\" if kb < qa else", "cls = \"full\" if kb <= qa else"),
+    ("zigzag.py", "for kb in (j, 2 * P - 1 - j):", "for kb in (j, P + j):"),
+    ("zigzag.py", "zigzag_positions(rank, P, c), k_pos, scale=scale)", "zigzag_positions(rank, P, c), k_pos, scale=1.0)"),
 ]
 
 
