@@ -185,34 +185,6 @@ __device__ __forceinline__ void wait_dma_and_sync() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// One tile of the visit: visit position s (chunk j = (rank - s) mod P), tile
-// tt inside that chunk, nvalid keys (0 for "past the end").
-struct Tile {
-  int s, tt, nvalid;
-};
-
-// Walks the tiles a workgroup visits: chunks in ring order, and in each chunk
-// the tiles holding keys visible to at least one of its query rows.  Only the
-// first chunk (the rank's own, or the single chunk of one ring step) can be
-// cut short by the causal mask; every later chunk of a ring lies entirely in
-// the past of the rank's queries and is visited whole.  next() is branch-free
-// scalar code so that it can sit inside the pipelined loop.
-struct TileWalk {
-  int s, tt, ntl, lim;       // current visit position, tile in it, its tiles / keys
-  int ntl_full, n_k, nseg;
-
-  __device__ Tile next() {
-    tt += 1;
-    const bool wrap = tt >= ntl;
-    s += wrap ? 1 : 0;
-    tt = wrap ? 0 : tt;
-    ntl = wrap ? ntl_full : ntl;
-    lim = wrap ? n_k : lim;
-    const int nv = s < nseg ? min(kBN, lim - tt * kBN) : 0;
-    return Tile{s, tt, nv};
-  }
-};
-
 template <int R>
 using Step = std::integral_constant<int, R>;
 
@@ -320,23 +292,6 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     dvo[i] = (uint32_t)(r * v_snb) + (((lane % C::NCH) ^ swz_v<D>(r)) * 16);
   }
 
-  // chunk of visit position s
-  auto chunk_of = [&](int s) {
-    const int j = p.rank - s;
-    return j < 0 ? j + p.P : j;
-  };
-  // One buffer resource spans the tile's valid rows: rows past the end of the
-  // chunk (and every row of an empty tile) read as zeros.
-  auto issue = [&](const unsigned char* hbase, int64_t csb, int snb, const Tile& t, uint32_t stage,
-                   const uint32_t* voff) {
-    const unsigned char* tb = hbase + (chunk_of(t.s) * csb + (int64_t)(t.tt * kBN) * snb);
-    const i32x4_t rs = buffer_rsrc(tb, (uint32_t)t.nvalid * (uint32_t)snb);
-#pragma unroll
-    for (int i = 0; i < C::NL; ++i) dma16(voff[i], rs, stage + (i * kWaves + wave) * C::RPW * C::ROWB);
-  };
-  auto issue_k = [&](const Tile& t, int stage) { issue(kg, k_csb, k_snb, t, lds0 + C::K_LDS + stage * C::TILE, dko); };
-  auto issue_v = [&](const Tile& t, int stage) { issue(vg, v_csb, v_snb, t, lds0 + C::V_LDS + stage * C::TILE, dvo); };
-
   // ---- scores and masks --------------------------------------------------------
   // S^T tile: 64 keys (M, two 32-key blocks nb) x the wave's 32 queries (N);
   // element j of block nb holds key 32*nb + 8*(j/4) + 4*hi + j%4 of query
@@ -366,14 +321,32 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   const int64_t kpos_own = p.k_pos0 + (int64_t)p.rank * p.k_posstride;
   const int qrel = (int)min((int64_t)(1 << 30), max((int64_t)-(1 << 30), p.q_pos0 + qw0 - kpos_own));
   const int tt_mask = max(0, (qrel + 1) / kBN);
-  auto mask = [&](STile& s, const Tile& t) {
-    const bool diag = p.causal && t.s == 0 && t.tt >= tt_mask;
-    if (!(t.nvalid < kBN || diag)) return;
-    int64_t rel = (int64_t)qrel + l32 - (int64_t)t.tt * kBN;   // last visible key of the tile
+
+  // The visit: chunks in ring order, and in each chunk the tiles holding keys
+  // visible to at least one of the block's query rows.  Only the first chunk
+  // (the rank's own, or the single chunk of one ring step) can be cut short
+  // by the causal mask; every later chunk of a ring lies entirely in the past
+  // of the rank's queries and is visited whole.  Tile g < ntl0 is tile g of
+  // the own chunk.
+  int64_t lim0 = p.n_k;   // visible keys of the own chunk for this block
+  if (p.causal) {
+    const int64_t qpos_last = p.q_pos0 + min(q0 + kBM, p.n_q) - 1;
+    lim0 = max((int64_t)0, min(lim0, qpos_last - kpos_own + 1));
+  }
+  const int ntl0 = (int)((lim0 + kBN - 1) / kBN);
+  const int ntl_full = (p.n_k + kBN - 1) / kBN;
+  const int T = ntl0 == 0 ? 0 : ntl0 + (p.nseg - 1) * ntl_full;
+
+  // Tile g of the visit with nv valid keys: own-chunk tiles from tt_mask on
+  // are masked on the causal diagonal, short tiles past their last key.
+  auto mask = [&](STile& s, int g, int nv) {
+    const bool diag = p.causal && g >= tt_mask && g < ntl0;
+    if (!(nv < kBN || diag)) return;
+    int64_t rel = (int64_t)qrel + l32 - (int64_t)g * kBN;   // last visible key of the tile
     if (!diag || rel > kBN) rel = kBN;
     // key u = (32*nb + 8*(j/4) + j%4) + 4*hi is masked when u > lastk; the
     // lane term moves to the right so that the left side is an immediate
-    const int lk = (int)min(rel, (int64_t)t.nvalid - 1) - 4 * hi;
+    const int lk = (int)min(rel, (int64_t)nv - 1) - 4 * hi;
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
@@ -482,17 +455,65 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
       for (int md = 0; md < C::MD; ++md) mfma_pv(vfrag(cc, md, stage), cc, md);
   };
 
+  // ---- K/V tile DMA -----------------------------------------------------------
+  // One walker per tensor, in scalar registers, steps through the tiles of the
+  // visit; crossing into the next chunk (rare) reloads the chunk base, and
+  // past the last chunk the tiles are empty.  Chunk j of the pool starts
+  // j*csb bytes after chunk 0; visit s reads chunk (rank - s) mod P.
+  struct DmaWalk {
+    const unsigned char* ptr;   // first row of the current tile
+    int rows;                   // rows of the current chunk from this tile on
+    int tl;                     // tiles of the current chunk from this tile on
+    int j;                      // current chunk
+    int left;                   // chunks of the visit after the current one
+  };
+  auto walk_start = [&](const unsigned char* hbase, int64_t csb) {
+    return DmaWalk{hbase + (int64_t)p.rank * csb, (int)lim0, ntl0, p.rank, p.nseg - 1};
+  };
+  auto walk_step = [&](DmaWalk& w, const unsigned char* hbase, int64_t csb, int snb) {
+    w.ptr += kBN * snb;
+    w.rows -= kBN;
+    if (--w.tl == 0) {
+      if (w.left > 0) {
+        w.left -= 1;
+        w.j = (w.j == 0 ? p.P : w.j) - 1;
+        w.ptr = hbase + (int64_t)w.j * csb;
+        w.rows = p.n_k;
+        w.tl = ntl_full;
+      } else {
+        w.rows = -(1 << 30);   // the visit is over
+      }
+    }
+  };
+  // One buffer resource spans the tile's valid rows: rows past the end of the
+  // chunk (and every row of an empty tile) read as zeros.  Returns the tile's
+  // valid rows.
+  const uint32_t m0_wave = (uint32_t)(wave * C::RPW * C::ROWB);   // this wave's rows of a tile
+  auto issue = [&](const DmaWalk& w, int snb, uint32_t stage, const uint32_t* voff) {
+    // (readfirstlane: the value is uniform; it keeps the clamp on the scalar
+    // unit, where the buffer resource has to live)
+    const int nv = __builtin_amdgcn_readfirstlane(min(max(w.rows, 0), kBN));
+    const i32x4_t rs = buffer_rsrc(w.ptr, (uint32_t)nv * (uint32_t)snb);
+    // (the laundering keeps the compiler from precomputing every stage's
+    // destination and holding them all in scalar registers)
+    uint32_t mw = m0_wave;
+    asm volatile("" : "+s"(mw));
+#pragma unroll
+    for (int i = 0; i < C::NL; ++i) dma16(voff[i], rs, stage + mw + i * kWaves * C::RPW * C::ROWB);
+    return nv;
+  };
+  DmaWalk wk = walk_start(kg, k_csb), wv = walk_start(vg, v_csb);
+  auto issue_k = [&](int stage) {
+    issue(wk, k_snb, lds0 + C::K_LDS + stage * C::TILE, dko);
+    walk_step(wk, kg, k_csb, k_snb);
+  };
+  auto issue_v = [&](int stage) {
+    const int nv = issue(wv, v_snb, lds0 + C::V_LDS + stage * C::TILE, dvo);
+    walk_step(wv, vg, v_csb, v_snb);
+    return nv;
+  };
+
   // ---- main loop -----------------------------------------------------------------
-  // first chunk of the visit: the rank's own; its visible keys for this block
-  int64_t lim0 = p.n_k;
-  if (p.causal) {
-    const int64_t qpos_last = p.q_pos0 + min(q0 + kBM, p.n_q) - 1;
-    lim0 = max((int64_t)0, min(lim0, qpos_last - kpos_own + 1));
-  }
-  const int ntl0 = (int)((lim0 + kBN - 1) / kBN);
-  const int ntl_full = (p.n_k + kBN - 1) / kBN;
-  const int T = ntl0 == 0 ? 0 : ntl0 + (p.nseg - 1) * ntl_full;
-  TileWalk walk{0, -1, ntl0, (int)lim0, ntl_full, p.n_k, p.nseg};
 
   // One loop iteration issues 2*NB*KC MFMAs in slots: even slot 2m is score
   // MFMA m, odd slot 2m+1 is P V MFMA m (columns cc = m / MD, d-block
@@ -519,29 +540,26 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
 
   if (T > 0) {
     STile sa, sb;
-    const Tile t0 = walk.next(), t1 = walk.next(), t2 = walk.next(), t3 = walk.next();
-    const Tile t4 = walk.next();
-    issue_k(t0, 0);
-    issue_k(t1, 1);
-    issue_k(t2, 2);
-    issue_v(t0, 0);
-    issue_k(t3, 3);
-    issue_v(t1, 1);
+    issue_k(0);                          // K(0) .. K(3) into stages 0..3
+    issue_k(1);
+    issue_k(2);
+    const int nv0 = issue_v(0);          // V(0), V(1)
+    issue_k(3);
+    const int nv1 = issue_v(1);
     wait_dma_and_sync<4 * C::NL>();      // K(0), K(1) landed
     scores(sa, Step<0>{});
     scores(sb, Step<1>{});
-    mask(sa, t0);
-    mask(sb, t1);
+    mask(sa, 0, nv0);
+    mask(sb, 1, nv1);
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) sm_group(sa, g);   // O is still zero: no rescale
 #pragma unroll
     for (int cc = 0; cc < kNCC; ++cc) pack(sa, cc);
     row_sums();
     lds_reads_done_sync();               // K stage 0 is free
-    issue_k(t4, 0);
-    issue_v(t2, 2);
-    // tiles t+2 .. t+5 at the top of iteration t
-    Tile d2 = t2, d3 = t3, d4 = t4, d5 = walk.next();
+    issue_k(0);                          // K(4)
+    int nv_next = issue_v(2);            // V(2); valid keys of the tile masked next
+    int g = 2;                           // tile masked at the end of the current iteration
 
     u32x4_t kfr[kMF];
     bf16x8_t vfr[kMF];
@@ -564,8 +582,9 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     auto body = [&](auto R, STile& nx, STile& cu) {
       constexpr int r = decltype(R)::value;
       constexpr int ks = (r + 2) % kStages, vs = r;
-      issue_k(d5, (r + 5) % kStages);
-      issue_v(d3, (r + 3) % kStages);
+      issue_k((r + 5) % kStages);          // K(t+5)
+      const int nv_mask = nv_next;         // tile t+2
+      nv_next = issue_v((r + 3) % kStages);   // V(t+3)
       resc = false;
       static_for<kSlots>([&](auto I) {
         constexpr int i = decltype(I)::value;
@@ -593,11 +612,8 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
       });
       row_sums();
       if (resc) rescale();
-      mask(nx, d2);
-      d2 = d3;
-      d3 = d4;
-      d4 = d5;
-      d5 = walk.next();
+      mask(nx, g, nv_mask);
+      g += 1;
       wait_dma_and_sync<2 * C::NL, kPreLds>();   // K(t+4), V(t+2) landed
     };
     // T - 1 iterations, padded to a multiple of 4 with empty tiles
@@ -613,18 +629,24 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no DMA may outlive the workgroup's LDS
 
   // ---- epilogue: normalise, merge into the running (O, lse), store ------------
+  // The output parameters are read from the kernel argument segment here,
+  // through a pointer the compiler cannot see through: otherwise it loads
+  // them at kernel entry and keeps ~20 scalar registers live across the loop.
   {
+    const AttnParams* pk = (const AttnParams*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(pk));
+    const AttnParams& pe = *pk;
     const int row = qw0 + l32;
     const float lt = sum_half(l_run);
-    if (row < p.n_q) {
+    if (row < pe.n_q) {
       const float lse_j = (lt > 0.f) ? (m_run + log2f(lt)) * kLn2 : kNegInf;
       const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
-      const int64_t bh_row = (int64_t)b * p.Hq + h;
+      const int64_t bh_row = (int64_t)b * pe.Hq + h;
       float wi = 0.f, wj = 1.f, lse = lse_j;
-      if (p.o_in != nullptr) lse = lse_merge_weights(p.lse_in[bh_row * p.lse_in_hs + row], lse_j, wi, wj);
+      if (pe.o_in != nullptr) lse = lse_merge_weights(pe.lse_in[bh_row * pe.lse_in_hs + row], lse_j, wi, wj);
       const float f = wj * inv;
-      const int64_t ooff = b * p.oo_sb + h * p.oo_sh + (int64_t)row * p.oo_sn;
-      const int64_t ioff = b * p.oi_sb + h * p.oi_sh + (int64_t)row * p.oi_sn;
+      const int64_t ooff = b * pe.oo_sb + h * pe.oo_sh + (int64_t)row * pe.oo_sn;
+      const int64_t ioff = b * pe.oi_sb + h * pe.oi_sh + (int64_t)row * pe.oi_sn;
 #pragma unroll
       for (int md = 0; md < C::MD; ++md)
 #pragma unroll
@@ -633,15 +655,15 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
           float y[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) y[r] = oacc[md][4 * g + r] * f;
-          if (p.o_in != nullptr && wi != 0.f) {
+          if (pe.o_in != nullptr && wi != 0.f) {
             float x[4];
-            load4(p.o_in, ioff + d0, p.acc_dtype, x);
+            load4(pe.o_in, ioff + d0, pe.acc_dtype, x);
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[r] = fmaf(wi, x[r], y[r]);
           }
-          store4(p.o_out, ooff + d0, p.out_dtype, y);
+          store4(pe.o_out, ooff + d0, pe.out_dtype, y);
         }
-      if (hi == 0) p.lse_out[bh_row * p.lse_out_hs + row] = lse;
+      if (hi == 0) pe.lse_out[bh_row * pe.lse_out_hs + row] = lse;
     }
   }
 }
