@@ -520,7 +520,8 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   static_assert(kMF == kNCC * C::MD, "score and P V MFMA counts");
   constexpr int kSlots = 2 * kMF;
   constexpr int kLead = 4;
-  constexpr int kPre = (kLead + 1) / 2;   // fragments of each kind read ahead
+  constexpr int kPre = kLead / 2;         // fragments of each kind read ahead
+  static_assert(kLead % 2 == 0, "reads alternate K, V: an even lead keeps both kinds kPre ahead");
   constexpr int kPreLds = 3 * kPre;       // their LDS instructions (K: 1, V: 2)
   // The iteration's K and V DMA go out a few slots into it rather than all
   // right after the barrier, where the eight waves would issue them at once
