@@ -18,6 +18,8 @@ the pages by eye:
   definition;
 * ``ulysses``    -- the sequence<->head all-to-all as an explicit index copy,
   including GQA key/value head replication;
+* ``backward``   -- the gradients of softmax attention (dQ, dK, dV) and one
+  chunk pair's share of them given the rows' full log-sum-exp;
 * ``zigzag``     -- the zigzag split of the sequence over ring ranks and the
   causal attention of one rank's shard under it;
 * ``closed_form``-- the materialised attention-matrix memory formula.
@@ -39,6 +41,7 @@ from .ring import lse_merge_fp64, ring_attention_fp64, ring_visit_order
 from .ulysses import (seq_to_head_naive, head_to_seq_naive, replicated_head_source,
                       check_ulysses_shapes)
 from .closed_form import attn_matrix_bytes
+from .backward import attention_bwd_fp64, chunk_attention_bwd_fp64, rowsum_do_o_fp64
 from .zigzag import zigzag_positions, zigzag_shard, zigzag_attention_fp64, zigzag_block_classes
 
 __all__ = [
@@ -47,5 +50,6 @@ __all__ = [
     "seq_to_head_naive", "head_to_seq_naive", "replicated_head_source",
     "check_ulysses_shapes",
     "attn_matrix_bytes",
+    "attention_bwd_fp64", "chunk_attention_bwd_fp64", "rowsum_do_o_fp64",
     "zigzag_positions", "zigzag_shard", "zigzag_attention_fp64", "zigzag_block_classes",
 ]

@@ -455,6 +455,119 @@ def pin_zigzag_balance(orc):
                     assert kb in (j, 2 * P - 1 - j) and qa in (r, 2 * P - 1 - r)
 
 
+# ----------------------------------------------------------------------------
+# backward
+# ----------------------------------------------------------------------------
+_BWD_CASES = [
+    # B, Hq, Hkv, nq, nk, d, scale, causal, q_pos0, k_pos0, seed
+    (1, 2, 1, 4, 5, 3, 0.8, False, 0, 0, 41),
+    (1, 2, 2, 5, 5, 2, 1.1, True, 0, 0, 42),
+    (2, 4, 2, 3, 6, 2, 1.0, True, 4, 2, 43),     # GQA, offset positions
+    (1, 2, 1, 3, 4, 2, 1.0, True, 0, 2, 44),     # first row sees no key
+]
+
+
+def pin_backward_finite_differences(orc):
+    """Central differences of L = sum(dO * O) through the (pinned) forward."""
+    for c in _BWD_CASES:
+        B, Hq, Hkv, nq, nk, d, scale, causal, qp, kp, seed = c
+        rng = np.random.default_rng(seed)
+        q = rng.standard_normal((B, Hq, nq, d))
+        k = rng.standard_normal((B, Hkv, nk, d))
+        v = rng.standard_normal((B, Hkv, nk, d))
+        do = rng.standard_normal((B, Hq, nq, d))
+        dq, dk, dv = orc.attention_bwd_fp64(q, k, v, do, scale=scale, causal=causal, q_pos0=qp, k_pos0=kp)
+
+        def loss(q_, k_, v_):
+            O, _ = orc.attention_fp64(q_, k_, v_, scale=scale, causal=causal, q_pos0=qp, k_pos0=kp)
+            return float((O * do).sum())
+        eps = 1e-6
+        for name, x, g in (("dq", q, dq), ("dk", k, dk), ("dv", v, dv)):
+            num = np.zeros_like(x)
+            it = np.nditer(x, flags=["multi_index"])
+            for _ in it:
+                i = it.multi_index
+                xp, xm = x.copy(), x.copy()
+                xp[i] += eps
+                xm[i] -= eps
+                args_p = [q, k, v]
+                args_m = [q, k, v]
+                idx = {"dq": 0, "dk": 1, "dv": 2}[name]
+                args_p[idx], args_m[idx] = xp, xm
+                num[i] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            _close(g, num, 1e-6, f"{name} vs finite differences {c}")
+
+
+def pin_backward_autograd(orc):
+    """torch autograd in float64 on the CPU through its own attention."""
+    import torch
+    for c in _BWD_CASES + [(1, 4, 2, 17, 23, 8, 0.3, True, 10, 0, 45), (2, 2, 1, 9, 9, 4, 1.0, False, 0, 0, 46)]:
+        B, Hq, Hkv, nq, nk, d, scale, causal, qp, kp, seed = c
+        rng = np.random.default_rng(seed)
+        q = rng.standard_normal((B, Hq, nq, d))
+        k = rng.standard_normal((B, Hkv, nk, d))
+        v = rng.standard_normal((B, Hkv, nk, d))
+        do = rng.standard_normal((B, Hq, nq, d))
+        dq, dk, dv = orc.attention_bwd_fp64(q, k, v, do, scale=scale, causal=causal, q_pos0=qp, k_pos0=kp)
+        qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        grp = Hq // Hkv
+        s = scale * torch.matmul(qt, kt.repeat_interleave(grp, dim=1).transpose(-1, -2))
+        if causal:
+            mask = (kp + torch.arange(nk))[None, :] <= (qp + torch.arange(nq))[:, None]
+            s = s.masked_fill(~mask, float("-inf"))
+            rows = mask.any(dim=1)
+        else:
+            rows = torch.ones(nq, dtype=torch.bool)
+        p = torch.softmax(s, dim=-1)
+        p = torch.where(rows[None, None, :, None], p, torch.zeros_like(p))     # empty rows: 0, not NaN
+        o = torch.matmul(p, vt.repeat_interleave(grp, dim=1))
+        (o * torch.tensor(do)).sum().backward()
+        _close(dq, qt.grad.numpy(), 1e-12, f"dq vs autograd {c}")
+        _close(dk, kt.grad.numpy(), 1e-12, f"dk vs autograd {c}")
+        _close(dv, vt.grad.numpy(), 1e-12, f"dv vs autograd {c}")
+
+
+def pin_backward_chunks_sum_to_full(orc):
+    """Per-chunk-pair contributions with the full-row lse sum to the full gradients."""
+    for P, n, B, Hq, Hkv, d, causal, scale, seed in [(3, 4, 1, 2, 1, 3, True, 0.9, 51), (2, 5, 1, 4, 2, 2, False, 1.2, 52),
+                                                     (4, 2, 2, 2, 2, 2, True, 1.0, 53)]:
+        rng = np.random.default_rng(seed)
+        L = P * n
+        q = rng.standard_normal((B, Hq, L, d))
+        k = rng.standard_normal((B, Hkv, L, d)) * 1.5
+        v = rng.standard_normal((B, Hkv, L, d))
+        do = rng.standard_normal((B, Hq, L, d))
+        dq, dk, dv = orc.attention_bwd_fp64(q, k, v, do, scale=scale, causal=causal)
+        O, lse = orc.attention_fp64(q, k, v, scale=scale, causal=causal)
+        D = orc.rowsum_do_o_fp64(do, O)
+        cq, ck, cv = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
+        for i in range(P):
+            qs = slice(i * n, (i + 1) * n)
+            for j in range(P):
+                ks = slice(j * n, (j + 1) * n)
+                a, b_, c_ = orc.chunk_attention_bwd_fp64(q[:, :, qs], k[:, :, ks], v[:, :, ks], do[:, :, qs],
+                                                          lse[:, :, qs], D[:, :, qs], scale=scale, causal=causal,
+                                                          q_pos0=i * n, k_pos0=j * n)
+                cq[:, :, qs] += a
+                ck[:, :, ks] += b_
+                cv[:, :, ks] += c_
+        _close(cq, dq, 1e-12, f"chunked dq P={P}")
+        _close(ck, dk, 1e-12, f"chunked dk P={P}")
+        _close(cv, dv, 1e-12, f"chunked dv P={P}")
+        # D is rowsum(P * dP) as well (a property of the softmax Jacobian)
+        Ddirect = np.zeros_like(D)
+        grp = Hq // Hkv
+        for b in range(B):
+            for h in range(Hq):
+                g = h // grp
+                s = scale * (q[b, h] @ k[b, g].T)
+                if causal:
+                    s = np.where(np.arange(L)[None, :] <= np.arange(L)[:, None], s, -np.inf)
+                p = np.exp(s - lse[b, h][:, None])
+                Ddirect[b, h] = (p * (do[b, h] @ v[b, g].T)).sum(axis=1)
+        _close(D, Ddirect, 1e-12, "D = rowsum(P * dP)")
+
+
 def pin_closed_form(orc):
     g = _load("attn_matrix_memory.json")
     b = orc.attn_matrix_bytes(g["L"], g["heads"], g["elem_bytes"])
@@ -482,4 +595,7 @@ ALL_PINS = [
     pin_zigzag_positions,
     pin_zigzag_equals_full,
     pin_zigzag_balance,
+    pin_backward_finite_differences,
+    pin_backward_autograd,
+    pin_backward_chunks_sum_to_full,
 ]

@@ -50,6 +50,18 @@ MUTANTS = [
     ("zigzag.py", "cls = \"full\" if kb < qa else", "cls = \"full\" if kb <= qa else"),
     ("zigzag.py", "for kb in (j, 2 * P - 1 - j):", "for kb in (j, P + j):"),
     ("zigzag.py", "zigzag_positions(rank, P, c), k_pos, scale=scale)", "zigzag_positions(rank, P, c), k_pos, scale=1.0)"),
+    ("backward.py", "            dv[b, g] += p.T @ do[b, h]\n            dp = do[b, h] @ v[b, g].T\n            D = ",
+     "            dv[b, g] += p @ do[b, h]\n            dp = do[b, h] @ v[b, g].T\n            D = "),
+    ("backward.py", "            ds = p * (dp - D[:, None])\n            dq[b, h] = scale * (ds @ k[b, g])\n            dk[b, g] += scale * (ds.T @ q[b, h])\n    return dq, dk, dv\n\n\ndef rowsum",
+     "            ds = p * dp\n            dq[b, h] = scale * (ds @ k[b, g])\n            dk[b, g] += scale * (ds.T @ q[b, h])\n    return dq, dk, dv\n\n\ndef rowsum"),
+    ("backward.py", "            dq[b, h] = scale * (ds @ k[b, g])\n            dk[b, g] += scale * (ds.T @ q[b, h])\n    return dq, dk, dv\n\n\ndef rowsum",
+     "            dq[b, h] = (ds @ k[b, g])\n            dk[b, g] += scale * (ds.T @ q[b, h])\n    return dq, dk, dv\n\n\ndef rowsum"),
+    ("backward.py", "            dk[b, g] += scale * (ds.T @ q[b, h])\n    return dq, dk, dv\n\n\ndef rowsum",
+     "            dk[b, g] = scale * (ds.T @ q[b, h])\n    return dq, dk, dv\n\n\ndef rowsum"),
+    ("backward.py", "np.exp(s - np.where(fin, lse[b, h], 0.0)[:, None])", "np.exp(s - np.where(fin, lse[b, h], 0.0)[None, :])"),
+    ("backward.py", "            ds = p * (dp - D[b, h][:, None])", "            ds = p * (dp - D[b, h][None, :])"),
+    ("backward.py", "return (np.asarray(do, dtype=np.float64) * np.asarray(o, dtype=np.float64)).sum(axis=-1)",
+     "return (np.asarray(do, dtype=np.float64) * np.asarray(o, dtype=np.float64)).sum(axis=-2)"),
 ]
 
 
