@@ -136,6 +136,72 @@ sqkv_status ra_ring_attention(sqkv_view q, sqkv_view k, sqkv_view v,
                               float scale, int causal, void* stream);
 
 /*
+ * Backward of chunked attention.  [RA], "pet project" steps 5-7: after the
+ * ring forward a loss is computed and backpropagated, and the result must
+ * match full attention.  The pages give no formulas; the gradients are the
+ * plain calculus of O = softmax(scale * Q K^T) V, row by row:
+ *   P = exp(scale * q.k - lse),  dV = P^T dO,  dP = dO V^T,
+ *   D = rowsum(dO * O),  dS = P * (dP - D),
+ *   dQ = scale * dS K,  dK = scale * dS^T Q
+ * (GQA: a key/value head's gradients sum over the query heads that read it).
+ * With lse the rows' log-sum-exp over ALL keys -- what the forward returned --
+ * P of one (query chunk, key chunk) pair is the full softmax restricted to
+ * that pair, so the ring backward is a sum of per-pair contributions.
+ *
+ * ra_attention_bwd_preprocess: D[b,h,t] = sum_e dout[b,h,t,e] * o[b,h,t,e]
+ * (o, dout [B, H, n, d] views of `dtype`, D dense float32 [B, H, n]).  Run it
+ * once per query chunk on the final output before the backward calls.
+ */
+sqkv_status ra_attention_bwd_preprocess(sqkv_view o, sqkv_view dout, float* D,
+                                        int B, int H, int n, int d, sqkv_dtype dtype, void* stream);
+
+/*
+ * ra_chunk_attention_bwd -- one chunk pair: ADDS its share into the float32
+ * gradients (the caller zeroes them before the first pair).
+ *
+ *   q, dout  [B, Hq, n_q, d]  bf16        query chunk and upstream gradient
+ *   k, v     [B, Hkv, n_k, d] bf16        key/value chunk
+ *   lse, D   [B, Hq, n_q]     float32     dense: the forward's lse over all
+ *                                         keys (natural log) and the
+ *                                         preprocess output
+ *   dq       [B, Hq, n_q, d]  float32     += scale * dS K
+ *   dk, dv   [B, Hkv, n_k, d] float32     += scale * dS^T Q, P^T dO
+ *
+ * Positions and the causal mask as in ra_chunk_attention.  Rows with
+ * lse = -inf (no visible key anywhere) contribute nothing.  Supported: d in
+ * {64, 128}, in_dtype BF16 (bf16 MFMA products, fp32 accumulation; P and dS
+ * rounded to bf16 for the products that take them), pointers and strides
+ * 16-byte aligned, row strides below 16 MiB.  Returns SQKV_OK, SQKV_EINVAL
+ * (null pointer, sizes, Hq % Hkv, scale, a gradient buffer overlapping an
+ * input or another gradient), SQKV_EUNSUPPORTED (d, dtype, alignment) or
+ * SQKV_EHIP.
+ */
+sqkv_status ra_chunk_attention_bwd(sqkv_view q, sqkv_view k, sqkv_view v, sqkv_view dout,
+                                   const float* lse, const float* D,
+                                   sqkv_view dq, sqkv_view dk, sqkv_view dv,
+                                   int B, int Hq, int Hkv, int n_q, int n_k, int d,
+                                   sqkv_dtype in_dtype, float scale, int causal,
+                                   int64_t q_pos0, int64_t k_pos0, void* stream);
+
+/*
+ * ra_ring_attention_bwd -- the backward of ra_ring_attention for one virtual
+ * rank: the rank's query chunk against the P resident chunks in ring order
+ * (own first; with causal != 0 the chunks after the rank's own are skipped).
+ * dq [B, Hq, n, d] float32 receives the rank's dQ; the pool gradients dk, dv
+ * (chunk 0 at dk/dv, chunk j dkv_chunk_stride elements further, float32)
+ * receive the rank's share of every chunk's dK, dV -- calling it for every
+ * rank accumulates the full pool gradients.  Same support and status codes
+ * as ra_chunk_attention_bwd; additionally EINVAL for rank outside [0, P) and
+ * EUNSUPPORTED for chunk strides that are not multiples of 16 bytes.
+ */
+sqkv_status ra_ring_attention_bwd(sqkv_view q, sqkv_view k, sqkv_view v,
+                                  int64_t k_chunk_stride, int64_t v_chunk_stride,
+                                  sqkv_view dout, const float* lse, const float* D,
+                                  sqkv_view dq, sqkv_view dk, sqkv_view dv, int64_t dkv_chunk_stride,
+                                  int B, int Hq, int Hkv, int n, int d, int P, int rank,
+                                  sqkv_dtype in_dtype, float scale, int causal, void* stream);
+
+/*
  * ra_zigzag_attention -- causal ring attention for one virtual rank under the
  * zigzag assignment of the sequence.  [UL], opening paragraph, names
  * Ring/ZigZag among the context-parallel methods without defining it; the

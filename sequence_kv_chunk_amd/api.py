@@ -53,6 +53,14 @@ _lib.ra_ring_attention.argtypes = [_V, _V, _V, _c_i64, _c_i64, _V, _vp, _c_int, 
 _lib.ra_zigzag_attention.restype = _c_int
 _lib.ra_zigzag_attention.argtypes = [_V, _V, _V, _c_i64, _c_i64, _V, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                      _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_f, _vp]
+_lib.ra_attention_bwd_preprocess.restype = _c_int
+_lib.ra_attention_bwd_preprocess.argtypes = [_V, _V, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]
+_lib.ra_chunk_attention_bwd.restype = _c_int
+_lib.ra_chunk_attention_bwd.argtypes = [_V, _V, _V, _V, _vp, _vp, _V, _V, _V, _c_int, _c_int, _c_int, _c_int,
+                                        _c_int, _c_int, _c_int, _c_f, _c_int, _c_i64, _c_i64, _vp]
+_lib.ra_ring_attention_bwd.restype = _c_int
+_lib.ra_ring_attention_bwd.argtypes = [_V, _V, _V, _c_i64, _c_i64, _V, _vp, _vp, _V, _V, _V, _c_i64, _c_int,
+                                       _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _vp]
 _lib.ra_lse_merge.restype = _c_int
 _lib.ra_lse_merge.argtypes = [_V, _vp, _c_int, _V, _vp, _c_int, _V, _vp, _c_int, _c_int, _c_int, _c_int,
                               _c_int, _vp]
@@ -62,6 +70,7 @@ _lib.ulysses_head_to_seq.restype = _c_int
 _lib.ulysses_head_to_seq.argtypes = [_vp, _vp, _c_int, _c_i64, _c_int, _c_int, _c_int, _vp]
 
 EXPORTED = ("ra_chunk_attention", "ra_ring_attention", "ra_zigzag_attention", "ra_lse_merge",
+            "ra_attention_bwd_preprocess", "ra_chunk_attention_bwd", "ra_ring_attention_bwd",
             "ulysses_seq_to_head", "ulysses_head_to_seq", "sqkv_last_error")
 
 
@@ -184,6 +193,72 @@ def ra_zigzag_attention(q, k_pool, v_pool, o, lse, *, rank: int, scale: float = 
                                       v_pool.stride(0), _view(o), _lse_ptr(lse, B * Hq * n), wo.data_ptr(),
                                       wl.data_ptr(), B, Hq, k_pool.shape[2], n, d, P, int(rank), _dtype_code(q),
                                       _dtype_code(o), float(scale), _stream(q))
+    _check(st)
+
+
+def ra_attention_bwd_preprocess(o, dout, D):
+    """D = rowsum(dout * o) over [B, H, n, d] tensors (or [S, H, d] shares)."""
+    o4, d4 = _bhnd(o), _bhnd(dout)
+    _same_device(o4, d4, D)
+    B, H, n, d = o4.shape
+    if d4.shape != o4.shape or d4.dtype != o4.dtype:
+        raise SqkvError(SQKV_EINVAL, "o and dout must agree in shape and dtype")
+    with torch.cuda.device(o4.device):
+        st = _lib.ra_attention_bwd_preprocess(_view(o4), _view(d4), _lse_ptr(D, B * H * n), B, H, n, d,
+                                              _dtype_code(o4), _stream(o4))
+    _check(st)
+
+
+def _f32(*ts):
+    for t in ts:
+        if t.dtype != torch.float32:
+            raise SqkvError(SQKV_EINVAL, "gradient buffers must be float32")
+
+
+def ra_chunk_attention_bwd(q, k, v, dout, lse, D, dq, dk, dv, *, scale: float = 1.0, causal: bool = False,
+                           q_pos0: int = 0, k_pos0: int = 0):
+    """Adds one chunk pair's share of (dQ, dK, dV) into the float32 dq, dk, dv."""
+    q4, k4, v4, o4 = _bhnd(q), _bhnd(k), _bhnd(v), _bhnd(dout)
+    g4, gk4, gv4 = _bhnd(dq), _bhnd(dk), _bhnd(dv)
+    _same_device(q4, k4, v4, o4, lse, D, g4, gk4, gv4)
+    _f32(g4, gk4, gv4)
+    B, Hq, n_q, d = q4.shape
+    Hkv, n_k = k4.shape[1], k4.shape[2]
+    if o4.shape != q4.shape or g4.shape != q4.shape or v4.shape != k4.shape or gk4.shape != k4.shape \
+            or gv4.shape != k4.shape:
+        raise SqkvError(SQKV_EINVAL, "shapes disagree")
+    rows = B * Hq * n_q
+    with torch.cuda.device(q4.device):
+        st = _lib.ra_chunk_attention_bwd(_view(q4), _view(k4), _view(v4), _view(o4), _lse_ptr(lse, rows),
+                                         _lse_ptr(D, rows), _view(g4), _view(gk4), _view(gv4), B, Hq, Hkv, n_q,
+                                         n_k, d, _dtype_code(q4), float(scale), int(bool(causal)), int(q_pos0),
+                                         int(k_pos0), _stream(q4))
+    _check(st)
+
+
+def ra_ring_attention_bwd(q, k_pool, v_pool, dout, lse, D, dq, dk_pool, dv_pool, *, rank: int,
+                          scale: float = 1.0, causal: bool = False):
+    """Backward of ra_ring_attention for virtual rank ``rank``: dq [B, Hq, n, d]
+    receives the rank's dQ, dk_pool/dv_pool ([P, B, Hkv, n, d] float32) the
+    rank's share of every chunk's dK, dV (all accumulated)."""
+    if k_pool.dim() != 5 or v_pool.shape != k_pool.shape or dk_pool.shape != k_pool.shape \
+            or dv_pool.shape != k_pool.shape:
+        raise SqkvError(SQKV_EINVAL, "pools must be [P, B, Hkv, n, d]")
+    _same_device(q, k_pool, v_pool, dout, lse, D, dq, dk_pool, dv_pool)
+    _f32(dq, dk_pool, dv_pool)
+    if dk_pool.stride(0) != dv_pool.stride(0):
+        raise SqkvError(SQKV_EINVAL, "dk_pool and dv_pool must share a chunk stride")
+    P = k_pool.shape[0]
+    B, Hq, n, d = q.shape
+    if tuple(dout.shape) != (B, Hq, n, d) or tuple(dq.shape) != (B, Hq, n, d) or k_pool.shape[3] != n:
+        raise SqkvError(SQKV_EINVAL, "shapes disagree")
+    rows = B * Hq * n
+    with torch.cuda.device(q.device):
+        st = _lib.ra_ring_attention_bwd(_view(q), _view(k_pool[0]), _view(v_pool[0]), k_pool.stride(0),
+                                        v_pool.stride(0), _view(dout), _lse_ptr(lse, rows), _lse_ptr(D, rows),
+                                        _view(dq), _view(dk_pool[0]), _view(dv_pool[0]), dk_pool.stride(0), B, Hq,
+                                        k_pool.shape[2], n, d, P, int(rank), _dtype_code(q), float(scale),
+                                        int(bool(causal)), _stream(q))
     _check(st)
 
 

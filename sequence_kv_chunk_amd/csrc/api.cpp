@@ -324,6 +324,145 @@ SQKV_EXPORT sqkv_status ra_zigzag_attention(sqkv_view q, sqkv_view k, sqkv_view 
   return hip_status(launch_attention(p3, d, in_dtype, hs), "ra_zigzag_attention launch 3");
 }
 
+namespace {
+
+// Validation of one backward chunk pair (views as in the forward; dq, dk, dv
+// fp32; lse and D dense fp32 [B, Hq, n_q]).
+sqkv_status check_bwd(const sqkv_view& q, const sqkv_view& k, const sqkv_view& v, const sqkv_view& dout,
+                      const float* lse, const float* D, const sqkv_view& dq, const sqkv_view& dk,
+                      const sqkv_view& dv, int B, int Hq, int Hkv, int64_t n_q, int64_t n_k, int64_t kv_extra,
+                      int64_t dkv_extra, int d, int in_dt, float scale) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || n_q < 0 || n_k < 0)
+    return fail(SQKV_EINVAL, "sizes must be positive (B=%d Hq=%d Hkv=%d n_q=%lld n_k=%lld)", B, Hq, Hkv,
+                (long long)n_q, (long long)n_k);
+  if (Hq % Hkv != 0) return fail(SQKV_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SQKV_EINVAL, "scale must be finite and > 0");
+  if (d != 64 && d != 128) return fail(SQKV_EUNSUPPORTED, "head dim d=%d not in {64, 128}", d);
+  if (in_dt != SQKV_BF16) return fail(SQKV_EUNSUPPORTED, "the backward takes bf16 q, k, v and dout");
+  if (B > 65535 || Hq > 65535) return fail(SQKV_EUNSUPPORTED, "B and Hq must be <= 65535");
+  if (n_q > (1ll << 30) || n_k > (1ll << 30)) return fail(SQKV_EUNSUPPORTED, "chunk lengths above 2^30");
+  if (n_q == 0 || n_k == 0) return ok();
+  if (!q.ptr || !k.ptr || !v.ptr || !dout.ptr || !lse || !D || !dq.ptr || !dk.ptr || !dv.ptr)
+    return fail(SQKV_EINVAL, "null pointer");
+  for (const sqkv_view* x : {&q, &k, &v, &dout, &dq, &dk, &dv})
+    if (!strides_nonneg(*x)) return fail(SQKV_EINVAL, "negative stride");
+  if (!view_aligned(q, 2) || !view_aligned(k, 2) || !view_aligned(v, 2) || !view_aligned(dout, 2) ||
+      !view_aligned(dq, 4) || !view_aligned(dk, 4) || !view_aligned(dv, 4))
+    return fail(SQKV_EUNSUPPORTED, "pointers and strides must be 16-byte aligned");
+  if (((uintptr_t)lse | (uintptr_t)D) % 4) return fail(SQKV_EUNSUPPORTED, "lse and D must be 4-byte aligned");
+  if (k.sn * 2 >= (1ll << 24) || v.sn * 2 >= (1ll << 24) || q.sn * 2 >= (1ll << 24) || dout.sn * 2 >= (1ll << 24))
+    return fail(SQKV_EUNSUPPORTED, "row strides must be below 16 MiB");
+  const int64_t rows = (int64_t)B * Hq * n_q;
+  Range rq = view_range(q, B, Hq, n_q, d, 2), ro = view_range(dout, B, Hq, n_q, d, 2);
+  Range rk = view_range(k, B, Hkv, n_k, d, 2), rv = view_range(v, B, Hkv, n_k, d, 2);
+  rk.hi += kv_extra;
+  rv.hi += kv_extra;
+  Range rl = dense_range(lse, rows, 4), rD = dense_range(D, rows, 4);
+  Range gq = view_range(dq, B, Hq, n_q, d, 4);
+  Range gk = view_range(dk, B, Hkv, n_k, d, 4), gv = view_range(dv, B, Hkv, n_k, d, 4);
+  gk.hi += dkv_extra;
+  gv.hi += dkv_extra;
+  for (const Range* g : {&gq, &gk, &gv})
+    for (const Range* r : {&rq, &ro, &rk, &rv, &rl, &rD})
+      if (overlap(*g, *r)) return fail(SQKV_EINVAL, "a gradient buffer overlaps an input");
+  if (overlap(gq, gk) || overlap(gq, gv) || overlap(gk, gv)) return fail(SQKV_EINVAL, "gradient buffers overlap");
+  return ok();
+}
+
+sqkv::BwdParams make_bwd(const sqkv_view& q, const sqkv_view& k, const sqkv_view& v, const sqkv_view& dout,
+                         const float* lse, const float* D, const sqkv_view& dq, const sqkv_view& dk,
+                         const sqkv_view& dv, int B, int Hq, int Hkv, int n_q, int n_k, float scale, int causal,
+                         int64_t q_pos0, int64_t k_pos0) {
+  sqkv::BwdParams p;
+  p.q = q.ptr; p.q_sb = q.sb; p.q_sh = q.sh; p.q_sn = q.sn;
+  p.k = k.ptr; p.k_sb = k.sb; p.k_sh = k.sh; p.k_sn = k.sn;
+  p.v = v.ptr; p.v_sb = v.sb; p.v_sh = v.sh; p.v_sn = v.sn;
+  p.dout = dout.ptr; p.do_sb = dout.sb; p.do_sh = dout.sh; p.do_sn = dout.sn;
+  p.lse = lse;
+  p.D = D;
+  p.dq = static_cast<float*>(dq.ptr); p.dq_sb = dq.sb; p.dq_sh = dq.sh; p.dq_sn = dq.sn;
+  p.dk = static_cast<float*>(dk.ptr); p.dk_sb = dk.sb; p.dk_sh = dk.sh; p.dk_sn = dk.sn;
+  p.dv = static_cast<float*>(dv.ptr); p.dv_sb = dv.sb; p.dv_sh = dv.sh; p.dv_sn = dv.sn;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.n_q = n_q; p.n_k = n_k;
+  p.group = Hq / Hkv;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.44269504088896340736f;
+  p.causal = causal ? 1 : 0;
+  p.q_pos0 = q_pos0;
+  p.k_pos0 = k_pos0;
+  return p;
+}
+
+sqkv_view offset_view(sqkv_view x, int64_t elems, int eb) {
+  x.ptr = static_cast<char*>(x.ptr) + elems * eb;
+  return x;
+}
+
+}  // namespace
+
+SQKV_EXPORT sqkv_status ra_attention_bwd_preprocess(sqkv_view o, sqkv_view dout, float* D, int B, int H, int n,
+                                                    int d, sqkv_dtype dtype, void* stream) {
+  if (B < 1 || H < 1 || n < 0) return fail(SQKV_EINVAL, "sizes must be positive");
+  if (d != 64 && d != 128) return fail(SQKV_EUNSUPPORTED, "head dim d=%d not in {64, 128}", d);
+  if (!dtype_ok(dtype)) return fail(SQKV_EUNSUPPORTED, "dtype must be SQKV_F32 or SQKV_BF16");
+  if (n == 0) return ok();
+  if (!o.ptr || !dout.ptr || !D) return fail(SQKV_EINVAL, "null pointer");
+  if (!strides_nonneg(o) || !strides_nonneg(dout)) return fail(SQKV_EINVAL, "negative stride");
+  const int eb = dtype_bytes(dtype);
+  if (!view_aligned(o, eb) || !view_aligned(dout, eb) || ((uintptr_t)D) % 4)
+    return fail(SQKV_EUNSUPPORTED, "pointers and strides must be 16-byte aligned (D 4-byte)");
+  Range rD = dense_range(D, (int64_t)B * H * n, 4);
+  if (overlap(rD, view_range(o, B, H, n, d, eb)) || overlap(rD, view_range(dout, B, H, n, d, eb)))
+    return fail(SQKV_EINVAL, "D overlaps o or dout");
+  sqkv::RowDotParams p;
+  p.o = o.ptr; p.o_sb = o.sb; p.o_sh = o.sh; p.o_sn = o.sn;
+  p.dout = dout.ptr; p.do_sb = dout.sb; p.do_sh = dout.sh; p.do_sn = dout.sn;
+  p.D = D;
+  p.B = B; p.H = H; p.n = n;
+  p.dtype = dtype;
+  return hip_status(sqkv::launch_bwd_rowdot(p, d, (hipStream_t)stream), "ra_attention_bwd_preprocess launch");
+}
+
+SQKV_EXPORT sqkv_status ra_chunk_attention_bwd(sqkv_view q, sqkv_view k, sqkv_view v, sqkv_view dout,
+                                               const float* lse, const float* D, sqkv_view dq, sqkv_view dk,
+                                               sqkv_view dv, int B, int Hq, int Hkv, int n_q, int n_k, int d,
+                                               sqkv_dtype in_dtype, float scale, int causal, int64_t q_pos0,
+                                               int64_t k_pos0, void* stream) {
+  sqkv_status st = check_bwd(q, k, v, dout, lse, D, dq, dk, dv, B, Hq, Hkv, n_q, n_k, 0, 0, d, in_dtype, scale);
+  if (st != SQKV_OK || n_q == 0 || n_k == 0) return st;
+  sqkv::BwdParams p = make_bwd(q, k, v, dout, lse, D, dq, dk, dv, B, Hq, Hkv, n_q, n_k, scale, causal, q_pos0, k_pos0);
+  return hip_status(sqkv::launch_attn_bwd_bf16(p, d, (hipStream_t)stream), "ra_chunk_attention_bwd launch");
+}
+
+SQKV_EXPORT sqkv_status ra_ring_attention_bwd(sqkv_view q, sqkv_view k, sqkv_view v, int64_t k_chunk_stride,
+                                              int64_t v_chunk_stride, sqkv_view dout, const float* lse,
+                                              const float* D, sqkv_view dq, sqkv_view dk, sqkv_view dv,
+                                              int64_t dkv_chunk_stride, int B, int Hq, int Hkv, int n, int d,
+                                              int P, int rank, sqkv_dtype in_dtype, float scale, int causal,
+                                              void* stream) {
+  if (P < 1 || rank < 0 || rank >= P) return fail(SQKV_EINVAL, "need P >= 1 and 0 <= rank < P (P=%d rank=%d)", P, rank);
+  if (k_chunk_stride < 0 || v_chunk_stride < 0 || dkv_chunk_stride < 0) return fail(SQKV_EINVAL, "negative chunk stride");
+  if ((k_chunk_stride * 2) % 16 || (v_chunk_stride * 2) % 16 || (dkv_chunk_stride * 4) % 16)
+    return fail(SQKV_EUNSUPPORTED, "chunk strides must be multiples of 16 bytes");
+  sqkv_status st = check_bwd(q, k, v, dout, lse, D, dq, dk, dv, B, Hq, Hkv, n, n,
+                             (int64_t)(P - 1) * std::max(k_chunk_stride, v_chunk_stride) * 2,
+                             (int64_t)(P - 1) * dkv_chunk_stride * 4, d, in_dtype, scale);
+  if (st != SQKV_OK || n == 0) return st;
+  // chunks in ring order, the rank's own first: j = (rank - s) mod P; with a
+  // causal mask the chunks after the rank's own are entirely in the future
+  const int nseg = causal ? rank + 1 : P;
+  for (int s = 0; s < nseg; ++s) {
+    const int j = (rank - s + P) % P;
+    sqkv::BwdParams p = make_bwd(q, offset_view(k, j * k_chunk_stride, 2), offset_view(v, j * v_chunk_stride, 2),
+                                 dout, lse, D, dq, offset_view(dk, j * dkv_chunk_stride, 4),
+                                 offset_view(dv, j * dkv_chunk_stride, 4), B, Hq, Hkv, n, n, scale, causal,
+                                 (int64_t)rank * n, (int64_t)j * n);
+    hipError_t e = sqkv::launch_attn_bwd_bf16(p, d, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "ra_ring_attention_bwd launch");
+  }
+  return ok();
+}
+
 SQKV_EXPORT sqkv_status ra_lse_merge(sqkv_view o_a, const float* lse_a, sqkv_dtype a_dtype, sqkv_view o_b,
                                      const float* lse_b, sqkv_dtype b_dtype, sqkv_view o_out, float* lse_out,
                                      sqkv_dtype out_dtype, int B, int H, int n, int d, void* stream) {

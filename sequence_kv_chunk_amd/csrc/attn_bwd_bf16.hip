@@ -1,0 +1,570 @@
+// Backward of chunk attention with bf16 inputs on gfx950 matrix cores.
+//
+// Ring-attention Q&A (aivaro.ru answer 425), "pet project" steps 5-7: the
+// ring forward is followed by a loss and a backward pass.  The gradients of
+// O = softmax(S) V, S = scale * Q K^T, are (row by row):
+//     P = exp(S - lse),  dV = P^T dO,  dP = dO V^T,
+//     dS = P * (dP - D) with D = rowsum(dO * O),
+//     dQ = scale * dS K,  dK = scale * dS^T Q.
+// With the rows' log-sum-exp over ALL keys (what the forward returns), P for
+// one (query chunk, key chunk) pair is the full softmax restricted to that
+// pair, so a ring backward is a sum of per-pair contributions.  One launch of
+// each kernel below adds one pair's share into fp32 dq, dk, dv.
+//
+// Two kernels, as in the usual split of the attention backward:
+// * attn_bwd_dq: parallel over query rows (8 waves x 32 rows per workgroup,
+//   two waves per SIMD).  Per 64-key tile it forms S^T = K Q^T and
+//   dP^T = V dO^T (keys on the MFMA M axis: a lane holds 16 keys of ONE
+//   query, so lse and D are one scalar per lane), the weights and dS^T in
+//   registers, and dQ^T += K^T dS^T with the K^T operand read from LDS with
+//   ds_read_b64_tr_b16 and dS^T rounded to bf16 as the B operand.
+// * attn_bwd_dkdv: parallel over keys (4 waves x 32 keys per workgroup, one
+//   wave per SIMD: K and V rows of the wave's keys, dK^T and dV^T stay in
+//   registers).  Per 32-query block it forms S = Q K^T and dP = dO V^T
+//   (queries on M: a lane holds 16 queries of ONE key), P and dS, and
+//   dV^T += dO^T P, dK^T += Q^T dS with transposed reads of the dO and Q
+//   tiles.  The query heads of a GQA group are walked inside the workgroup so
+//   that a key/value head's gradients sum over them without atomics.
+// Tiles (64 rows) are copied global -> LDS by buffer_load ... lds, double
+// buffered.  Every tile is read both as rows (ds_read_b128) and transposed
+// (ds_read_b64_tr_b16); the 16-byte chunk swizzle below keeps both
+// conflict-free.
+#include <type_traits>
+#include <utility>
+
+#include "attn_common.h"
+
+namespace sqkv {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+#define SQKV_LDS __attribute__((address_space(3)))
+
+constexpr int kTR = 64;   // rows per LDS tile (keys in the dq kernel, queries in the dk/dv kernel)
+
+template <int D, int NWAVES>
+struct BCfg {
+  static constexpr int KC = D / 16;            // 16-wide contraction steps over d
+  static constexpr int MD = D / 32;            // 32-row blocks of d
+  static constexpr int NCH = D / 8;            // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;           // bytes per row
+  static constexpr int TILE = kTR * ROWB;      // bytes per tile
+  static constexpr int RPW = 1024 / ROWB;      // rows per wave-wide 1 KiB load
+  static constexpr int NL = TILE / 1024 / NWAVES;   // loads per wave per tile
+  static_assert(NL >= 1 && (TILE / 1024) % NWAVES == 0, "tile loads must spread evenly over the waves");
+};
+
+// Position of 16-byte chunk c of tile row r: c ^ swz(r).  The low part (by
+// r % 4) sends the transpose reads of four consecutive rows to distinct bank
+// groups; the high part (by (r / 4) % 4, one coset of the first pattern
+// each) makes the 16 rows of a row read distinct as well.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  const int f = (r & 3) == 0 ? 0 : (r & 3) == 1 ? 6 : (r & 3) == 2 ? 12 : 10;
+  return (f ^ ((r >> 2) & 3)) & (D / 8 - 1);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t v = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ u32x4_t lds_b128(uint32_t addr) {
+  return *reinterpret_cast<SQKV_LDS const u32x4_t*>((size_t)addr);
+}
+
+__device__ __forceinline__ i16x4_t lds_tr16(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<SQKV_LDS i16x4_t*>((size_t)addr));
+}
+
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = (int)(uint32_t)b;
+  r[1] = (int)(uint32_t)(b >> 32);
+  r[2] = (int)bytes;                 // num_records: bytes past this read as 0
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from the buffer at `voff` into LDS at m0 + 16 * lane.
+__device__ __forceinline__ void dma16(uint32_t voff, i32x4_t rsrc, uint32_t lds) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
+}
+
+// s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8).
+constexpr unsigned waitcnt_imm(int vm, int lgkm) {
+  return (unsigned)((vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8));
+}
+
+// Wait for every DMA and LDS read of this wave, then meet the other waves.
+__device__ __forceinline__ void drain_and_sync() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Copies rows [row0, row0 + kTR) of a [n, d] bf16 view (valid rows < n) into
+// an LDS tile at `lds`; wave-wide load i of the tile fills rows
+// (i * NWAVES + wave) * RPW ..; rows past n arrive as zeros.
+template <int D, int NWAVES>
+struct TileDma {
+  using C = BCfg<D, NWAVES>;
+  uint32_t voff[C::NL];
+  uint32_t m0_wave;
+
+  __device__ void init(int lane, int wave, int snb) {
+#pragma unroll
+    for (int i = 0; i < C::NL; ++i) {
+      const int r = (i * NWAVES + wave) * C::RPW + lane / C::NCH;
+      voff[i] = (uint32_t)(r * snb) + (((lane % C::NCH) ^ swz<D>(r)) * 16);
+    }
+    m0_wave = (uint32_t)(wave * C::RPW * C::ROWB);
+  }
+  __device__ void issue(const unsigned char* base, int snb, int row0, int n, uint32_t lds) const {
+    const int nv = __builtin_amdgcn_readfirstlane(min(max(n - row0, 0), kTR));
+    const i32x4_t rs = buffer_rsrc(base + (int64_t)row0 * snb, (uint32_t)nv * (uint32_t)snb);
+#pragma unroll
+    for (int i = 0; i < C::NL; ++i) dma16(voff[i], rs, lds + m0_wave + i * NWAVES * C::RPW * C::ROWB);
+  }
+};
+
+// Row read (A operand, 32 rows x 16 d): lane holds row rb + l32, d columns
+// 16 * kc + 8 * hi .. +7.  Returns the lane's LDS byte offset for kc = 0
+// relative to the tile; kc adds nothing fixed (the swizzle differs per kc),
+// so the offsets are kept per kc.
+template <int D>
+__device__ __forceinline__ uint32_t row_ofs(int row, int kc, int hi) {
+  return (uint32_t)(row * (D * 2) + (((2 * kc + hi) ^ swz<D>(row)) * 16));
+}
+
+// Transposed read (A operand, 32 d rows x 16 tile rows): the 16-lane group
+// g = lane / 16 reads tile rows 16 * cc + 4 * hi + {0..3} (part 0) and the
+// same + 8 (part 1) at d columns 32 * md + 16 * (g & 1) + {0..15}; group lane
+// a16 supplies row a16 / 4, columns 4 * (a16 % 4) .. +3.  Offset for cc = 0
+// relative to the tile; cc adds 16 rows (the swizzle repeats every 16 rows,
+// but differs between the two parts).
+template <int D>
+__device__ __forceinline__ uint32_t tr_ofs(int lane, int md, int part) {
+  const int hi = lane >> 5, a16 = lane & 15;
+  const int r = 4 * hi + (a16 >> 2) + 8 * part;
+  const int c = 4 * md + 2 * ((lane >> 4) & 1) + ((a16 & 3) >> 1);
+  return (uint32_t)(r * (D * 2) + ((c ^ swz<D>(r)) * 16) + (a16 & 1) * 8);
+}
+
+__device__ __forceinline__ bf16x8_t tr_frag(uint32_t a0, uint32_t a1) {
+  const i16x4_t lo = lds_tr16(a0);
+  const i16x4_t up = lds_tr16(a1);
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Global row loads of one lane's 8 d-values (16 bytes) of a bf16 row, zero
+// when the row is invalid.
+__device__ __forceinline__ u32x4_t load_row8(const uint16_t* rowp, bool ok, int e0) {
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  return ok ? *reinterpret_cast<const u32x4_t*>(rowp + e0) : z;
+}
+
+// ============================================================================
+// dQ: query rows in registers, K/V tiles streamed
+// ============================================================================
+constexpr int kDqWaves = 8;
+constexpr int kDqRows = 32 * kDqWaves;
+
+template <int D>
+__global__ void __launch_bounds__(64 * kDqWaves)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dq_kernel(BwdParams p, int n_qtiles) {
+  using C = BCfg<D, kDqWaves>;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const uint32_t lds0 = (uint32_t)(size_t)(SQKV_LDS unsigned char*)smem;
+  const uint32_t K_LDS = lds0, V_LDS = lds0 + 2 * C::TILE;   // two stages each
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  const int BH = p.B * p.Hq;
+  const int qt_rank = blockIdx.x / BH;
+  const int bh = blockIdx.x - qt_rank * BH;
+  const int qt = p.causal ? (n_qtiles - 1 - qt_rank) : qt_rank;
+  const int b = bh / p.Hq, h = bh - (bh / p.Hq) * p.Hq;
+  const int hk = h / p.group;
+  const int q0 = qt * kDqRows, qw0 = q0 + wave * 32;
+  const int row = qw0 + l32;
+  const bool row_ok = row < p.n_q;
+
+  // Q and dO rows of the lane's query (B operands of S^T and dP^T)
+  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)(row_ok ? row : 0) * p.q_sn;
+  const uint16_t* drow = static_cast<const uint16_t*>(p.dout) + b * p.do_sb + h * p.do_sh +
+                         (int64_t)(row_ok ? row : 0) * p.do_sn;
+  u32x4_t qf[C::KC], dof[C::KC];
+#pragma unroll
+  for (int kc = 0; kc < C::KC; ++kc) {
+    qf[kc] = load_row8(qrow, row_ok, 16 * kc + 8 * hi);
+    dof[kc] = load_row8(drow, row_ok, 16 * kc + 8 * hi);
+  }
+  const int64_t srow = ((int64_t)b * p.Hq + h) * p.n_q + (row_ok ? row : 0);
+  const float lse = row_ok ? p.lse[srow] : kNegInf;
+  // P = exp2(c * s - lse2); a row that sees no key anywhere has P = 0
+  const float lse2 = (lse == kNegInf) ? __builtin_huge_valf() : lse * kLog2e;
+  const float Dq = row_ok ? p.D[srow] : 0.f;
+  const float c = p.scale_log2;
+
+  // visible keys of the block: causal keys up to the last query's position
+  int n_vis = p.n_k;
+  if (p.causal) {
+    const int64_t qpos_last = p.q_pos0 + min(q0 + kDqRows, p.n_q) - 1;
+    n_vis = (int)max((int64_t)0, min((int64_t)p.n_k, qpos_last - p.k_pos0 + 1));
+  }
+  const int T = (n_vis + kTR - 1) / kTR;
+  const int64_t qpos = p.q_pos0 + row;   // this lane's query position
+
+  const unsigned char* kg = reinterpret_cast<const unsigned char*>(
+      static_cast<const uint16_t*>(p.k) + b * p.k_sb + hk * p.k_sh);
+  const unsigned char* vg = reinterpret_cast<const unsigned char*>(
+      static_cast<const uint16_t*>(p.v) + b * p.v_sb + hk * p.v_sh);
+  const int k_snb = (int)(p.k_sn * 2), v_snb = (int)(p.v_sn * 2);
+  TileDma<D, kDqWaves> dk_dma, dv_dma;
+  dk_dma.init(lane, wave, k_snb);
+  dv_dma.init(lane, wave, v_snb);
+
+  uint32_t kofs[C::KC], tofs[C::MD][2];
+#pragma unroll
+  for (int kc = 0; kc < C::KC; ++kc) kofs[kc] = row_ofs<D>(l32, kc, hi);
+#pragma unroll
+  for (int md = 0; md < C::MD; ++md) {
+    tofs[md][0] = tr_ofs<D>(lane, md, 0);
+    tofs[md][1] = tr_ofs<D>(lane, md, 1);
+  }
+
+  f32x16_t acc[C::MD];
+#pragma unroll
+  for (int md = 0; md < C::MD; ++md) acc[md] = (f32x16_t){};
+
+  if (T > 0) {
+    dk_dma.issue(kg, k_snb, 0, n_vis, K_LDS);
+    dv_dma.issue(vg, v_snb, 0, n_vis, V_LDS);
+  }
+  for (int t = 0; t < T; ++t) {
+    const uint32_t st = (uint32_t)(t & 1) * C::TILE;
+    drain_and_sync();                       // tile t landed; stage (t+1)&1 is free
+    if (t + 1 < T) {
+      dk_dma.issue(kg, k_snb, (t + 1) * kTR, n_vis, K_LDS + (C::TILE - st));
+      dv_dma.issue(vg, v_snb, (t + 1) * kTR, n_vis, V_LDS + (C::TILE - st));
+    }
+    // S^T and dP^T for the two 32-key blocks: element j of block nb holds key
+    // t*64 + 32*nb + 8*(j/4) + 4*hi + j%4 of query `row`
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      s[nb] = (f32x16_t){};
+      dp[nb] = (f32x16_t){};
+#pragma unroll
+      for (int kc = 0; kc < C::KC; ++kc) {
+        const uint32_t o = kofs[kc] + st + nb * 32 * C::ROWB;
+        s[nb] = mfma(as_bf16x8(lds_b128(K_LDS + o)), as_bf16x8(qf[kc]), s[nb]);
+        dp[nb] = mfma(as_bf16x8(lds_b128(V_LDS + o)), as_bf16x8(dof[kc]), dp[nb]);
+      }
+    }
+    // weights and dS^T; keys past the visible range or after the query are 0
+    const int kbase = t * kTR;
+    int64_t lastk = p.causal ? (qpos - p.k_pos0 - kbase) : (int64_t)kTR;   // last visible key of the tile
+    lastk = min(lastk, (int64_t)(n_vis - kbase - 1));
+    const int lk = (int)max((int64_t)-1, min(lastk, (int64_t)kTR)) - 4 * hi;
+    u32x4_t dsf[4];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float w[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const bool vis = 32 * nb + 8 * (j >> 2) + (j & 3) <= lk;
+        const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(s[nb][j], c, -lse2)) : 0.f;
+        w[j] = pr * (dp[nb][j] - Dq);
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) dsf[2 * nb + half][x] = pack_bf16x2(w[8 * half + 2 * x], w[8 * half + 2 * x + 1]);
+    }
+    // dQ^T[d][query] += K^T[d][key] dS^T[key][query]
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int md = 0; md < C::MD; ++md)
+        acc[md] = mfma(tr_frag(K_LDS + st + tofs[md][0] + 16 * cc * C::ROWB,
+                               K_LDS + st + tofs[md][1] + 16 * cc * C::ROWB),
+                       as_bf16x8(dsf[cc]), acc[md]);
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // no DMA may outlive the workgroup's LDS
+
+  if (row_ok) {
+    float* dqr = p.dq + b * p.dq_sb + h * p.dq_sh + (int64_t)row * p.dq_sn;
+#pragma unroll
+    for (int md = 0; md < C::MD; ++md)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * md + 8 * g + 4 * hi;
+        float4 x = *reinterpret_cast<float4*>(dqr + d0);
+        x.x = fmaf(p.scale, acc[md][4 * g + 0], x.x);
+        x.y = fmaf(p.scale, acc[md][4 * g + 1], x.y);
+        x.z = fmaf(p.scale, acc[md][4 * g + 2], x.z);
+        x.w = fmaf(p.scale, acc[md][4 * g + 3], x.w);
+        *reinterpret_cast<float4*>(dqr + d0) = x;
+      }
+  }
+}
+
+// ============================================================================
+// dK, dV: key rows in registers, Q/dO tiles streamed
+// ============================================================================
+constexpr int kKvWaves = 4;
+constexpr int kKvRows = 32 * kKvWaves;
+
+template <int D>
+__global__ void __launch_bounds__(64 * kKvWaves)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_bwd_dkdv_kernel(BwdParams p) {
+  using C = BCfg<D, kKvWaves>;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const uint32_t lds0 = (uint32_t)(size_t)(SQKV_LDS unsigned char*)smem;
+  const uint32_t Q_LDS = lds0, O_LDS = lds0 + 2 * C::TILE;   // Q and dO, two stages each
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  const int BH = p.B * p.Hkv;
+  const int kt = blockIdx.x / BH;
+  const int bh = blockIdx.x - kt * BH;
+  const int b = bh / p.Hkv, hk = bh - (bh / p.Hkv) * p.Hkv;
+  const int k0 = kt * kKvRows, kw0 = k0 + wave * 32;
+  const int key = kw0 + l32;
+  const bool key_ok = key < p.n_k;
+
+  // K and V rows of the lane's key (B operands of S and dP)
+  const uint16_t* krow = static_cast<const uint16_t*>(p.k) + b * p.k_sb + hk * p.k_sh + (int64_t)(key_ok ? key : 0) * p.k_sn;
+  const uint16_t* vrow = static_cast<const uint16_t*>(p.v) + b * p.v_sb + hk * p.v_sh + (int64_t)(key_ok ? key : 0) * p.v_sn;
+  u32x4_t kf[C::KC], vf[C::KC];
+#pragma unroll
+  for (int kc = 0; kc < C::KC; ++kc) {
+    kf[kc] = load_row8(krow, key_ok, 16 * kc + 8 * hi);
+    vf[kc] = load_row8(vrow, key_ok, 16 * kc + 8 * hi);
+  }
+  const int64_t kpos = p.k_pos0 + key;
+  const float c = p.scale_log2;
+
+  // the first query that can see the workgroup's first key
+  int qstart = 0;
+  if (p.causal) qstart = (int)min((int64_t)p.n_q, max((int64_t)0, p.k_pos0 + k0 - p.q_pos0));
+  const int t0 = qstart / kTR;
+  const int T = (p.n_q + kTR - 1) / kTR;
+
+  const int q_snb = (int)(p.q_sn * 2), o_snb = (int)(p.do_sn * 2);
+  TileDma<D, kKvWaves> q_dma, o_dma;
+  q_dma.init(lane, wave, q_snb);
+  o_dma.init(lane, wave, o_snb);
+
+  uint32_t rofs[C::KC], tofs[C::MD][2];
+#pragma unroll
+  for (int kc = 0; kc < C::KC; ++kc) rofs[kc] = row_ofs<D>(l32, kc, hi);
+#pragma unroll
+  for (int md = 0; md < C::MD; ++md) {
+    tofs[md][0] = tr_ofs<D>(lane, md, 0);
+    tofs[md][1] = tr_ofs<D>(lane, md, 1);
+  }
+
+  f32x16_t dka[C::MD], dva[C::MD];
+#pragma unroll
+  for (int md = 0; md < C::MD; ++md) {
+    dka[md] = (f32x16_t){};
+    dva[md] = (f32x16_t){};
+  }
+
+  for (int gi = 0; gi < p.group; ++gi) {
+    const int h = hk * p.group + gi;
+    const unsigned char* qg = reinterpret_cast<const unsigned char*>(
+        static_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh);
+    const unsigned char* og = reinterpret_cast<const unsigned char*>(
+        static_cast<const uint16_t*>(p.dout) + b * p.do_sb + h * p.do_sh);
+    const float* lse_h = p.lse + ((int64_t)b * p.Hq + h) * p.n_q;
+    const float* D_h = p.D + ((int64_t)b * p.Hq + h) * p.n_q;
+    if (t0 < T) {
+      drain_and_sync();                     // the previous head's tiles are no longer read
+      q_dma.issue(qg, q_snb, t0 * kTR, p.n_q, Q_LDS);
+      o_dma.issue(og, o_snb, t0 * kTR, p.n_q, O_LDS);
+    }
+    for (int t = t0; t < T; ++t) {
+      const uint32_t st = (uint32_t)((t - t0) & 1) * C::TILE;
+      drain_and_sync();
+      if (t + 1 < T) {
+        q_dma.issue(qg, q_snb, (t + 1) * kTR, p.n_q, Q_LDS + (C::TILE - st));
+        o_dma.issue(og, o_snb, (t + 1) * kTR, p.n_q, O_LDS + (C::TILE - st));
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        // S and dP for 32 queries: element j holds query
+        // t*64 + 32*qb + 8*(j/4) + 4*hi + j%4 of key `key`
+        f32x16_t s = {}, dp = {};
+#pragma unroll
+        for (int kc = 0; kc < C::KC; ++kc) {
+          const uint32_t o = rofs[kc] + st + qb * 32 * C::ROWB;
+          s = mfma(as_bf16x8(lds_b128(Q_LDS + o)), as_bf16x8(kf[kc]), s);
+          dp = mfma(as_bf16x8(lds_b128(O_LDS + o)), as_bf16x8(vf[kc]), dp);
+        }
+        const int qb0 = t * kTR + 32 * qb;
+        float pw[16], dsw[16];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int qi = qb0 + 8 * g4 + 4 * hi;    // first of 4 consecutive queries
+          float l4[4], d4[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const bool ok = qi + x < p.n_q;
+            l4[x] = ok ? lse_h[qi + x] : kNegInf;
+            d4[x] = ok ? D_h[qi + x] : 0.f;
+          }
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int j = 4 * g4 + x;
+            const int64_t qp = p.q_pos0 + qi + x;
+            const bool vis = key_ok && l4[x] != kNegInf && (!p.causal || kpos <= qp);
+            const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(s[j], c, -l4[x] * kLog2e)) : 0.f;
+            pw[j] = pr;
+            dsw[j] = pr * (dp[j] - d4[x]);
+          }
+        }
+        u32x4_t pf[2], df[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            pf[half][x] = pack_bf16x2(pw[8 * half + 2 * x], pw[8 * half + 2 * x + 1]);
+            df[half][x] = pack_bf16x2(dsw[8 * half + 2 * x], dsw[8 * half + 2 * x + 1]);
+          }
+        // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int md = 0; md < C::MD; ++md) {
+            const uint32_t o = st + (32 * qb + 16 * half) * C::ROWB;
+            dva[md] = mfma(tr_frag(O_LDS + o + tofs[md][0], O_LDS + o + tofs[md][1]), as_bf16x8(pf[half]), dva[md]);
+            dka[md] = mfma(tr_frag(Q_LDS + o + tofs[md][0], Q_LDS + o + tofs[md][1]), as_bf16x8(df[half]), dka[md]);
+          }
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // no DMA may outlive the workgroup's LDS
+
+  if (key_ok) {
+    float* dkr = p.dk + b * p.dk_sb + hk * p.dk_sh + (int64_t)key * p.dk_sn;
+    float* dvr = p.dv + b * p.dv_sb + hk * p.dv_sh + (int64_t)key * p.dv_sn;
+#pragma unroll
+    for (int md = 0; md < C::MD; ++md)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * md + 8 * g + 4 * hi;
+        float4 x = *reinterpret_cast<float4*>(dkr + d0);
+        x.x = fmaf(p.scale, dka[md][4 * g + 0], x.x);
+        x.y = fmaf(p.scale, dka[md][4 * g + 1], x.y);
+        x.z = fmaf(p.scale, dka[md][4 * g + 2], x.z);
+        x.w = fmaf(p.scale, dka[md][4 * g + 3], x.w);
+        *reinterpret_cast<float4*>(dkr + d0) = x;
+        float4 y = *reinterpret_cast<float4*>(dvr + d0);
+        y.x += dva[md][4 * g + 0];
+        y.y += dva[md][4 * g + 1];
+        y.z += dva[md][4 * g + 2];
+        y.w += dva[md][4 * g + 3];
+        *reinterpret_cast<float4*>(dvr + d0) = y;
+      }
+  }
+}
+
+// ============================================================================
+// D = rowsum(dO * O)
+// ============================================================================
+template <int D>
+__global__ void __launch_bounds__(256) bwd_rowdot_kernel(RowDotParams p) {
+  // one row per 16 lanes: each lane takes D/16 consecutive elements
+  constexpr int E = D / 16;
+  const int64_t rows = (int64_t)p.B * p.H * p.n;
+  const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 16;
+  const int sub = threadIdx.x & 15;
+  float acc = 0.f;
+  if (r < rows) {
+    const int64_t t = r % p.n, bh = r / p.n;
+    const int64_t hh = bh % p.H, bb = bh / p.H;
+    const int64_t oo = bb * p.o_sb + hh * p.o_sh + t * p.o_sn + sub * E;
+    const int64_t od = bb * p.do_sb + hh * p.do_sh + t * p.do_sn + sub * E;
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      float a[4], g[4];
+      load4(p.o, oo + e, p.dtype, a);
+      load4(p.dout, od + e, p.dtype, g);
+      acc = fmaf(a[0], g[0], acc);
+      acc = fmaf(a[1], g[1], acc);
+      acc = fmaf(a[2], g[2], acc);
+      acc = fmaf(a[3], g[3], acc);
+    }
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+  if (r < rows && sub == 0) p.D[r] = acc;
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdParams& p, hipStream_t s) {
+  using Cq = BCfg<D, kDqWaves>;
+  using Ck = BCfg<D, kKvWaves>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 4 * Cq::TILE);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 4 * Ck::TILE);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int n_qtiles = (p.n_q + kDqRows - 1) / kDqRows;
+  const int64_t bq = (int64_t)n_qtiles * p.B * p.Hq;
+  if (bq > 0)
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3((unsigned)bq), dim3(64 * kDqWaves), 4 * Cq::TILE, s, p, n_qtiles);
+  const int n_ktiles = (p.n_k + kKvRows - 1) / kKvRows;
+  const int64_t bk = (int64_t)n_ktiles * p.B * p.Hkv;
+  if (bk > 0)
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)bk), dim3(64 * kKvWaves), 4 * Ck::TILE, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const BwdParams& p, int d, hipStream_t s) {
+  if (p.n_q == 0 || p.n_k == 0) return hipSuccess;
+  return d == 128 ? launch_bwd_d<128>(p, s) : launch_bwd_d<64>(p, s);
+}
+
+hipError_t launch_bwd_rowdot(const RowDotParams& p, int d, hipStream_t s) {
+  const int64_t rows = (int64_t)p.B * p.H * p.n;
+  if (rows == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((rows * 16 + 255) / 256);
+  if (d == 128)
+    hipLaunchKernelGGL(bwd_rowdot_kernel<128>, dim3(blocks), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(bwd_rowdot_kernel<64>, dim3(blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace sqkv

@@ -43,6 +43,47 @@ struct AttnParams {
   int64_t q_pos0, k_pos0;
 };
 
+// One chunk pair of the attention backward: query chunk (q, dout, lse, D)
+// against key/value chunk (k, v); adds the pair's share into dq (fp32
+// [B, Hq, n_q, d]) and dk, dv (fp32 [B, Hkv, n_k, d]).  lse and D are dense
+// [B, Hq, n_q] fp32: the rows' natural-log log-sum-exp over ALL keys and
+// rowsum(dO * O).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t do_sb, do_sh, do_sn;
+  const float* lse;
+  const float* D;
+  float* dq;
+  float* dk;
+  float* dv;
+  int64_t dq_sb, dq_sh, dq_sn;
+  int64_t dk_sb, dk_sh, dk_sn;
+  int64_t dv_sb, dv_sh, dv_sn;
+  int B, Hq, Hkv, n_q, n_k;
+  int group;          // Hq / Hkv
+  float scale;        // logits are scale * (q . k)
+  float scale_log2;   // scale * log2(e)
+  int causal;
+  int64_t q_pos0, k_pos0;
+};
+
+// D = rowsum(dO * O) per query row.
+struct RowDotParams {
+  const void* o;
+  const void* dout;
+  int64_t o_sb, o_sh, o_sn;
+  int64_t do_sb, do_sh, do_sn;
+  float* D;            // dense [B, H, n]
+  int B, H, n;
+  int dtype;           // of o and dout
+};
+
 struct MergeParams {
   const void* oa;
   int64_t a_sb, a_sh, a_sn;
@@ -75,6 +116,8 @@ struct PermuteParams {
 hipError_t launch_attn_bf16(const AttnParams& p, int d, hipStream_t s);
 hipError_t launch_attn_f32(const AttnParams& p, int d, hipStream_t s);
 hipError_t launch_lse_merge(const MergeParams& p, int d, hipStream_t s);
+hipError_t launch_bwd_rowdot(const RowDotParams& p, int d, hipStream_t s);
+hipError_t launch_attn_bwd_bf16(const BwdParams& p, int d, hipStream_t s);
 hipError_t launch_seq_to_head(const PermuteParams& p, hipStream_t s);
 hipError_t launch_head_to_seq(const PermuteParams& p, hipStream_t s);
 

@@ -1,0 +1,133 @@
+"""Attention backward (bf16 MFMA kernels) against the fp64 oracle.
+
+One chunk pair at a time with the oracle's lse and D as inputs (so that the
+kernels are checked on their own), the D preprocess, and the whole ring
+backward end to end (GPU forward, GPU D, every rank's backward accumulated)
+against the gradients of full attention.  Tolerance for the fp32 gradients
+of bf16 inputs: max-abs error <= 2e-2 * max(1, max |reference|) per tensor
+(the attention bar, scaled to the gradient's magnitude)."""
+import numpy as np
+import pytest
+
+import oracle
+from sequence_kv_chunk_amd.synth import bf16_bits_to_f64, f32_to_bf16_bits
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from gpu_util import dev_bf16, host_f64, say  # noqa: E402
+
+GRAD_TOL = 2e-2
+
+
+def check_grad(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    bound = GRAD_TOL * max(1.0, float(np.max(np.abs(ref))) if ref.size else 1.0)
+    assert err <= bound, f"{what}: max abs err {err:.3e} > {bound:.3e}"
+    say(f"   {what}: max abs err {err:.2e} (max |ref| {float(np.max(np.abs(ref))):.2e})")
+    return err
+
+
+@pytest.fixture(scope="module")
+def api():
+    from sequence_kv_chunk_amd import api
+    return api
+
+
+def _bits(shape, rng, scale=1.0):
+    return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(scale))
+
+
+CASES = [
+    # B, Hq, Hkv, nq, nk, d, causal, q_pos0, k_pos0, scale
+    (1, 2, 2, 64, 64, 128, False, 0, 0, 1.0),
+    (1, 2, 1, 100, 70, 128, False, 0, 0, 1.0),
+    (2, 4, 2, 300, 200, 64, False, 0, 0, 0.8),
+    (1, 2, 2, 257, 257, 128, True, 0, 0, 1.0),       # diagonal block, ragged
+    (1, 4, 1, 200, 300, 128, True, 500, 300, 1.0),   # queries ahead of the keys
+    (1, 2, 2, 130, 200, 64, True, 0, 60, 1.0),       # first rows see nothing
+    (1, 8, 2, 129, 513, 128, False, 0, 0, 1.2),      # GQA 4:1, several key tiles
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in range(len(CASES))])
+def test_chunk_bwd(api, case):
+    B, Hq, Hkv, nq, nk, d, causal, qp, kp, scale = case
+    say(f"chunk bwd {case}")
+    rng = np.random.default_rng(700 + nq + nk + d)
+    qb = _bits((B, Hq, nq, d), rng, d ** -0.5)
+    kb = _bits((B, Hkv, nk, d), rng)
+    vb = _bits((B, Hkv, nk, d), rng)
+    ob = _bits((B, Hq, nq, d), rng)
+    q, k, v, do = (bf16_bits_to_f64(x) for x in (qb, kb, vb, ob))
+    # the rows' lse and D as a full forward over these keys would give them
+    O, lse = oracle.attention_fp64(q, k, v, scale=scale, causal=causal, q_pos0=qp, k_pos0=kp)
+    D = oracle.rowsum_do_o_fp64(do, O)
+    ref = oracle.chunk_attention_bwd_fp64(q, k, v, do, lse, D, scale=scale, causal=causal, q_pos0=qp, k_pos0=kp)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    dq = torch.zeros((B, Hq, nq, d), dtype=torch.float32, device="cuda")
+    dk = torch.zeros((B, Hkv, nk, d), dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+    api.ra_chunk_attention_bwd(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), dev_bf16(ob), dev(lse).reshape(-1),
+                               dev(D).reshape(-1), dq, dk, dv, scale=scale, causal=causal, q_pos0=qp, k_pos0=kp)
+    torch.cuda.synchronize()
+    for name, g, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        check_grad(host_f64(g), r, f"{name} {case}")
+
+
+def test_bwd_preprocess(api):
+    rng = np.random.default_rng(77)
+    for dt in ("bf16", "f32"):
+        for d in (64, 128):
+            x = rng.standard_normal((2, 3, 70, d), dtype=np.float32)
+            y = rng.standard_normal((2, 3, 70, d), dtype=np.float32)
+            if dt == "bf16":
+                xb, yb = f32_to_bf16_bits(x), f32_to_bf16_bits(y)
+                xd, yd = dev_bf16(xb), dev_bf16(yb)
+                ref = oracle.rowsum_do_o_fp64(bf16_bits_to_f64(yb), bf16_bits_to_f64(xb))
+            else:
+                xd, yd = torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()
+                ref = oracle.rowsum_do_o_fp64(y, x)
+            D = torch.full((2 * 3 * 70,), float("nan"), dtype=torch.float32, device="cuda")
+            api.ra_attention_bwd_preprocess(xd, yd, D)
+            torch.cuda.synchronize()
+            got = host_f64(D).reshape(2, 3, 70)
+            assert np.max(np.abs(got - ref)) <= 1e-5 * max(1.0, np.max(np.abs(ref))), (dt, d)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("P,n,Hq,Hkv,d", [(4, 128, 4, 2, 128), (3, 100, 2, 2, 64), (1, 200, 2, 1, 128)])
+def test_ring_bwd_end_to_end(api, P, n, Hq, Hkv, d, causal):
+    """GPU ring forward, GPU D, every rank's GPU backward; against the
+    gradients of one softmax over the whole sequence."""
+    say(f"ring bwd P={P} n={n} causal={causal}")
+    B = 1
+    rng = np.random.default_rng(900 + P * n + d + int(causal))
+    qb = _bits((P, B, Hq, n, d), rng, d ** -0.5)
+    kb = _bits((P, B, Hkv, n, d), rng)
+    vb = _bits((P, B, Hkv, n, d), rng)
+    ob = _bits((P, B, Hq, n, d), rng)
+    full = lambda x: bf16_bits_to_f64(x).transpose(1, 2, 0, 3, 4).reshape(B, x.shape[2], P * n, d)
+    ref = oracle.attention_bwd_fp64(full(qb), full(kb), full(vb), full(ob), causal=causal)
+    kd, vd = dev_bf16(kb), dev_bf16(vb)
+    dk = torch.zeros((P, B, Hkv, n, d), dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+    for r in range(P):
+        qd, od = dev_bf16(qb[r]), dev_bf16(ob[r])
+        o = torch.empty((B, Hq, n, d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(B * Hq * n, dtype=torch.float32, device="cuda")
+        api.ra_ring_attention(qd, kd, vd, o, lse, rank=r, causal=causal)
+        D = torch.empty_like(lse)
+        api.ra_attention_bwd_preprocess(o, od, D)
+        dq = torch.zeros((B, Hq, n, d), dtype=torch.float32, device="cuda")
+        api.ra_ring_attention_bwd(qd, kd, vd, od, lse, D, dq, dk, dv, rank=r, causal=causal)
+        torch.cuda.synchronize()
+        check_grad(host_f64(dq), ref[0][:, :, r * n:(r + 1) * n], f"dq rank {r}")
+    dkf = host_f64(dk).transpose(1, 2, 0, 3, 4).reshape(B, Hkv, P * n, d)
+    dvf = host_f64(dv).transpose(1, 2, 0, 3, 4).reshape(B, Hkv, P * n, d)
+    check_grad(dkf, ref[1], "dk pool")
+    check_grad(dvf, ref[2], "dv pool")
