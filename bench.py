@@ -14,7 +14,8 @@ chunk-attention kernel (MFMA-bound) and the CPU oracle timed on a bounded
 sample of the same workload.  Extra figures on the other workloads (Ulysses
 permute GB/s on 8 x [16384, 32, 128] bf16, the causal 128k rank-7 ring share,
 the causal 128k GQA Ulysses share, the whole causal 128k ring under the
-contiguous and the zigzag split) go in "extras".  Logs go to stderr.
+contiguous and the zigzag split, the backward of the 32k ring) go in
+"extras".  Logs go to stderr.
 """
 from __future__ import annotations
 
@@ -191,6 +192,49 @@ def bench_causal_split(api, torch, steps=2):
     return res
 
 
+def bench_backward(api, torch, x, w, steps=2):
+    """Backward of the 32k ring: for every rank the D preprocess and the ring
+    backward (dQ of the rank, its share of every chunk's dK, dV).  TFLOP/s
+    counts 10*d per visible pair (scores recomputed, dV, dP, dQ, dK); the
+    kernels do 14*d (the dK/dV kernel recomputes the scores and dP)."""
+    qs, kp, vp = x["q"], x["k"], x["v"]
+    P = w.P
+    B, H, n, d = qs.shape[1:]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed + 100)
+    dout = torch.randn(qs.shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    o = torch.empty((P, B, H, n, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((P, B * H * n), dtype=torch.float32, device="cuda")
+    for r in range(P):
+        api.ra_ring_attention(qs[r], kp, vp, o[r], lse[r], rank=r, causal=w.causal)
+    D = torch.empty_like(lse)
+    dq = torch.zeros((B, H, n, d), dtype=torch.float32, device="cuda")
+    dk = torch.zeros(kp.shape, dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+
+    def step():
+        for r in range(P):
+            api.ra_attention_bwd_preprocess(o[r], dout[r], D[r])
+            api.ra_ring_attention_bwd(qs[r], kp, vp, dout[r], lse[r], D[r], dq, dk, dv, rank=r, causal=w.causal)
+
+    step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = w.flops() // 4 * 10
+    res = {"ms": round(ms, 3), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1),
+           "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "flops_10d": flops,
+           "workload": "backward of ring_bf16_32k (all 8 ranks: D preprocess + ring backward)"}
+    del dout, o, lse, D, dq, dk, dv
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(x_dev, w, torch, budget_rows=4096, heads=16):
     """The fp64 oracle on a bounded sample of the workload: query chunk 0
     (4096 rows) of the first `heads` heads against all 32768 keys."""
@@ -287,6 +331,8 @@ def main():
     extras = {}
     if not args.no_extras:
         try:
+            extras["ring_bf16_32k_backward"] = bench_backward(api, torch, x, w)
+            log(f"backward: {extras['ring_bf16_32k_backward']}")
             extras["ulysses"] = bench_ulysses(api, torch)
             log(f"ulysses: {extras['ulysses']}")
             extras["ring_bf16_128k_rank7_causal"] = bench_attention_extra(api, torch, "ring_bf16_128k_rank7_causal")

@@ -100,6 +100,11 @@ __device__ __forceinline__ void dma16(uint32_t voff, i32x4_t rsrc, uint32_t lds)
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
 }
 
+// 4 bytes per lane from the buffer at `voff` into LDS at m0 + 4 * lane.
+__device__ __forceinline__ void dma4(uint32_t voff, i32x4_t rsrc, uint32_t lds) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" :: "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
+}
+
 // s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8).
 constexpr unsigned waitcnt_imm(int vm, int lgkm) {
@@ -340,7 +345,9 @@ attn_bwd_dkdv_kernel(BwdParams p) {
   using C = BCfg<D, kKvWaves>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const uint32_t lds0 = (uint32_t)(size_t)(SQKV_LDS unsigned char*)smem;
-  const uint32_t Q_LDS = lds0, O_LDS = lds0 + 2 * C::TILE;   // Q and dO, two stages each
+  // Q and dO tiles, two stages each, then the tiles' lse and D (64 floats
+  // each, two stages)
+  const uint32_t Q_LDS = lds0, O_LDS = lds0 + 2 * C::TILE, L_LDS = lds0 + 4 * C::TILE, D_LDS = L_LDS + 2 * 256;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -401,10 +408,20 @@ attn_bwd_dkdv_kernel(BwdParams p) {
         static_cast<const uint16_t*>(p.dout) + b * p.do_sb + h * p.do_sh);
     const float* lse_h = p.lse + ((int64_t)b * p.Hq + h) * p.n_q;
     const float* D_h = p.D + ((int64_t)b * p.Hq + h) * p.n_q;
+    // the row statistics of query tile tq into stage `sl` (wave 0 only: one
+    // 64-lane dword load each)
+    auto issue_stats = [&](int tq, uint32_t sl) {
+      if (wave == 0) {
+        const int nv = __builtin_amdgcn_readfirstlane(min(max(p.n_q - tq * kTR, 0), kTR));
+        dma4((uint32_t)(lane * 4), buffer_rsrc(lse_h + tq * kTR, (uint32_t)nv * 4u), L_LDS + sl);
+        dma4((uint32_t)(lane * 4), buffer_rsrc(D_h + tq * kTR, (uint32_t)nv * 4u), D_LDS + sl);
+      }
+    };
     if (t0 < T) {
       drain_and_sync();                     // the previous head's tiles are no longer read
       q_dma.issue(qg, q_snb, t0 * kTR, p.n_q, Q_LDS);
       o_dma.issue(og, o_snb, t0 * kTR, p.n_q, O_LDS);
+      issue_stats(t0, 0);
     }
     for (int t = t0; t < T; ++t) {
       const uint32_t st = (uint32_t)((t - t0) & 1) * C::TILE;
@@ -412,6 +429,7 @@ attn_bwd_dkdv_kernel(BwdParams p) {
       if (t + 1 < T) {
         q_dma.issue(qg, q_snb, (t + 1) * kTR, p.n_q, Q_LDS + (C::TILE - st));
         o_dma.issue(og, o_snb, (t + 1) * kTR, p.n_q, O_LDS + (C::TILE - st));
+        issue_stats(t + 1, st == 0 ? 256u : 0u);
       }
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -429,12 +447,14 @@ attn_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int qi = qb0 + 8 * g4 + 4 * hi;    // first of 4 consecutive queries
+          const uint32_t so = (st == 0 ? 0u : 256u) + (uint32_t)(32 * qb + 8 * g4 + 4 * hi) * 4u;
+          const u32x4_t lr = lds_b128(L_LDS + so), dr = lds_b128(D_LDS + so);
           float l4[4], d4[4];
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
             const bool ok = qi + x < p.n_q;
-            l4[x] = ok ? lse_h[qi + x] : kNegInf;
-            d4[x] = ok ? D_h[qi + x] : 0.f;
+            l4[x] = ok ? __uint_as_float(lr[x]) : kNegInf;
+            d4[x] = ok ? __uint_as_float(dr[x]) : 0.f;
           }
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
@@ -534,7 +554,7 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t s) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 4 * Cq::TILE);
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 4 * Ck::TILE);
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 4 * Ck::TILE + 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -545,7 +565,7 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t s) {
   const int n_ktiles = (p.n_k + kKvRows - 1) / kKvRows;
   const int64_t bk = (int64_t)n_ktiles * p.B * p.Hkv;
   if (bk > 0)
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)bk), dim3(64 * kKvWaves), 4 * Ck::TILE, s, p);
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)bk), dim3(64 * kKvWaves), 4 * Ck::TILE + 1024, s, p);
   return hipGetLastError();
 }
 
