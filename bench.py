@@ -14,8 +14,8 @@ chunk-attention kernel (MFMA-bound) and the CPU oracle timed on a bounded
 sample of the same workload.  Extra figures on the other workloads (Ulysses
 permute GB/s on 8 x [16384, 32, 128] bf16, the causal 128k rank-7 ring share,
 the causal 128k GQA Ulysses share, the whole causal 128k ring under the
-contiguous and the zigzag split, the backward of the 32k ring) go in
-"extras".  Logs go to stderr.
+contiguous and the zigzag split, the backward of the 32k ring, the USP
+hybrid at 128k) go in "extras".  Logs go to stderr.
 """
 from __future__ import annotations
 
@@ -235,6 +235,37 @@ def bench_backward(api, torch, x, w, steps=2):
     return res
 
 
+def bench_usp(api, torch, steps=2):
+    """USP hybrid at 128k: 8 virtual ranks as Ulysses groups of P_u inside a
+    ring of P_r = 8 / P_u groups; B=1, 32 query heads, 8 key/value heads,
+    d=128, causal, bf16.  One call runs all 8 ranks' work (permutes in,
+    rings, permute out)."""
+    L, H, H_kv, d, P = 131072, 32, 8, 128, 8
+    n = L // P
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    q = (torch.randn((P, n, H, d), generator=g, device="cuda") * d ** -0.5).to(torch.bfloat16)
+    k = torch.randn((P, n, H_kv, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((P, n, H_kv, d), generator=g, device="cuda").to(torch.bfloat16)
+    o = torch.empty_like(q)
+    flops = 4 * d * H * (L * (L + 1) // 2)
+    res = {"workload": "USP causal, L=131072, 32 q heads, 8 kv heads, d=128, 8 virtual ranks", "flops": flops}
+    for P_u in (4, 2):
+        api.usp_attention(q, k, v, o, P_u=P_u, causal=True)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            api.usp_attention(q, k, v, o, P_u=P_u, causal=True)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res[f"P_u={P_u},P_r={P // P_u}"] = {"ms": round(ms, 3), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)}
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(x_dev, w, torch, budget_rows=4096, heads=16):
     """The fp64 oracle on a bounded sample of the workload: query chunk 0
     (4096 rows) of the first `heads` heads against all 32768 keys."""
@@ -342,6 +373,8 @@ def main():
             log(f"ulysses share: {extras['ulysses_share_gqa_128k_causal']}")
             extras["causal_128k_ring_split"] = bench_causal_split(api, torch)
             log(f"causal split: {extras['causal_128k_ring_split']}")
+            extras["usp_128k_causal"] = bench_usp(api, torch)
+            log(f"usp: {extras['usp_128k_causal']}")
         except Exception as e:  # extras never hide the main line
             extras["error"] = repr(e)
     if not args.no_cpu:

@@ -284,6 +284,35 @@ sqkv_status ulysses_seq_to_head(const void* src, void* dst, int P, int64_t L,
 sqkv_status ulysses_head_to_seq(const void* src, void* dst, int P, int64_t L,
                                 int H, int d, int elem_bytes, void* stream);
 
+/*
+ * usp_attention -- the hybrid of the two methods: Ulysses inside groups of
+ * P_u ranks, a ring across P_r such groups.  [HF], closing remarks of the
+ * Ulysses section, points to combining sequence and context parallelism (the
+ * USP scheme) for still longer sequences; [UL] gives the per-group all_to_all
+ * and its head limit.  Reading: P = P_u * P_r virtual ranks, rank p = i_r*P_u
+ * + i_u holds tokens p*L/P ..; the P_u ranks of ring row i_r exchange heads
+ * so that each holds the row's S = L/P_r contiguous tokens for heads
+ * i_u*H/P_u ..; the P_r ranks with the same i_u then run ring attention over
+ * the rows; the output goes back to the sequence layout.  All on one HBM
+ * pool, as three phases of the other entry points.
+ *
+ *   q, o     dense [P][L/P][H][d] bf16         input / output (sequence layout)
+ *   k, v     dense [P][L/P][H_kv][d] bf16
+ *   work_q, work_o  dense [P_r][P_u][S][H/P_u][d] bf16      caller-owned scratch
+ *   work_k, work_v  dense [P_r][P_u][S][Hk][d] bf16, Hk = max(H_kv, P_u)/P_u
+ *            (key/value heads copied up to P_u as in ulysses_seq_to_head)
+ *   lse      dense [P_r][P_u][H/P_u][S] float32: the rows' lse, by head share
+ *
+ * Causal masking uses global positions (ring rows are contiguous runs).
+ * EINVAL: P_u or P_r < 1, L % (P_u*P_r), H % H_kv, H % P_u, neither of H_kv,
+ * P_u dividing the other, null pointers, overlapping buffers; otherwise the
+ * status of the first failing phase.
+ */
+sqkv_status usp_attention(const void* q, const void* k, const void* v, void* o,
+                          void* work_q, void* work_k, void* work_v, void* work_o, float* lse,
+                          int P_u, int P_r, int64_t L, int H, int H_kv, int d,
+                          float scale, int causal, void* stream);
+
 /* Message for the last non-OK status returned on this host thread ("" if the
  * last call succeeded).  The string stays valid until the next call. */
 const char* sqkv_last_error(void);

@@ -61,6 +61,9 @@ _lib.ra_chunk_attention_bwd.argtypes = [_V, _V, _V, _V, _vp, _vp, _V, _V, _V, _c
 _lib.ra_ring_attention_bwd.restype = _c_int
 _lib.ra_ring_attention_bwd.argtypes = [_V, _V, _V, _c_i64, _c_i64, _V, _vp, _vp, _V, _V, _V, _c_i64, _c_int,
                                        _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _vp]
+_lib.usp_attention.restype = _c_int
+_lib.usp_attention.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_i64, _c_int, _c_int,
+                               _c_int, _c_f, _c_int, _vp]
 _lib.ra_lse_merge.restype = _c_int
 _lib.ra_lse_merge.argtypes = [_V, _vp, _c_int, _V, _vp, _c_int, _V, _vp, _c_int, _c_int, _c_int, _c_int,
                               _c_int, _vp]
@@ -71,7 +74,7 @@ _lib.ulysses_head_to_seq.argtypes = [_vp, _vp, _c_int, _c_i64, _c_int, _c_int, _
 
 EXPORTED = ("ra_chunk_attention", "ra_ring_attention", "ra_zigzag_attention", "ra_lse_merge",
             "ra_attention_bwd_preprocess", "ra_chunk_attention_bwd", "ra_ring_attention_bwd",
-            "ulysses_seq_to_head", "ulysses_head_to_seq", "sqkv_last_error")
+            "ulysses_seq_to_head", "ulysses_head_to_seq", "usp_attention", "sqkv_last_error")
 
 
 def _check(status: int):
@@ -307,3 +310,46 @@ def ulysses_head_to_seq(src, dst):
         st = _lib.ulysses_head_to_seq(src.data_ptr(), dst.data_ptr(), P, L, Hl * P, d, src.element_size(),
                                       _stream(src))
     _check(st)
+
+
+def usp_attention(q, k, v, o, *, P_u: int, scale: float = 1.0, causal: bool = False, work=None, lse=None):
+    """Ulysses inside groups of P_u virtual ranks, ring attention across the
+    P_r = P / P_u groups.  q, o: [P, L/P, H, d] bf16; k, v: [P, L/P, H_kv, d]
+    bf16 (sequence layout).  ``work`` = (work_q, work_k, work_v, work_o)
+    scratch and ``lse`` ([P_r, P_u, H/P_u, L/P_r] float32) are allocated here
+    when not given.  Returns lse."""
+    for t in (q, k, v, o):
+        _dense(t, "q/k/v/o")
+    _same_device(q, k, v, o)
+    P, n, H, d = q.shape
+    H_kv = k.shape[2]
+    if tuple(o.shape) != tuple(q.shape) or tuple(v.shape) != tuple(k.shape) or k.shape[:2] != q.shape[:2] \
+            or q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16 \
+            or o.dtype != torch.bfloat16:
+        raise SqkvError(SQKV_EINVAL, "q, o [P, L/P, H, d] and k, v [P, L/P, H_kv, d], all bf16")
+    P_u = int(P_u)
+    if P_u < 1 or P % P_u or H % P_u:
+        raise SqkvError(SQKV_EINVAL, "P_u must divide P and H")
+    P_r = P // P_u
+    L = P * n
+    S = L // P_r
+    Hk = max(H_kv, P_u) // P_u
+    if work is None:
+        work = (torch.empty((P_r, P_u, S, H // P_u, d), dtype=torch.bfloat16, device=q.device),
+                torch.empty((P_r, P_u, S, Hk, d), dtype=torch.bfloat16, device=q.device),
+                torch.empty((P_r, P_u, S, Hk, d), dtype=torch.bfloat16, device=q.device),
+                torch.empty((P_r, P_u, S, H // P_u, d), dtype=torch.bfloat16, device=q.device))
+    if lse is None:
+        lse = torch.empty((P_r, P_u, H // P_u, S), dtype=torch.float32, device=q.device)
+    wq, wk, wv, wo = work
+    for t in (wq, wk, wv, wo, lse):
+        _dense(t, "work/lse")
+    if wq.numel() != q.numel() or wo.numel() != q.numel() or wk.numel() != P_r * P_u * S * Hk * d \
+            or wv.numel() != wk.numel() or lse.numel() != P_r * P_u * (H // P_u) * S or lse.dtype != torch.float32:
+        raise SqkvError(SQKV_EINVAL, "work buffers or lse have the wrong size")
+    with torch.cuda.device(q.device):
+        st = _lib.usp_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), wq.data_ptr(),
+                                wk.data_ptr(), wv.data_ptr(), wo.data_ptr(), lse.data_ptr(), P_u, P_r, L, H, H_kv,
+                                d, float(scale), int(bool(causal)), _stream(q))
+    _check(st)
+    return lse

@@ -564,3 +564,66 @@ SQKV_EXPORT sqkv_status ulysses_head_to_seq(const void* src, void* dst, int P, i
   p.row_bytes = (int64_t)d * elem_bytes;
   return hip_status(sqkv::launch_head_to_seq(p, (hipStream_t)stream), "ulysses_head_to_seq launch");
 }
+
+SQKV_EXPORT sqkv_status usp_attention(const void* q, const void* k, const void* v, void* o, void* work_q,
+                                      void* work_k, void* work_v, void* work_o, float* lse, int P_u, int P_r,
+                                      int64_t L, int H, int H_kv, int d, float scale, int causal, void* stream) {
+  if (P_u < 1 || P_r < 1) return fail(SQKV_EINVAL, "need P_u >= 1 and P_r >= 1 (P_u=%d P_r=%d)", P_u, P_r);
+  const int P = P_u * P_r;
+  if (L < 0 || L % P) return fail(SQKV_EINVAL, "L=%lld must be a multiple of P_u*P_r=%d", (long long)L, P);
+  if (H < 1 || H_kv < 1 || H % H_kv) return fail(SQKV_EINVAL, "H (%d) must be a multiple of H_kv (%d)", H, H_kv);
+  if (H % P_u) return fail(SQKV_EINVAL, "H (%d) must be a multiple of P_u (%d)", H, P_u);
+  if (P_u % H_kv && H_kv % P_u)
+    return fail(SQKV_EINVAL, "key/value heads (%d) and P_u (%d): one must divide the other", H_kv, P_u);
+  if (L == 0) return ok();
+  if (!q || !k || !v || !o || !work_q || !work_k || !work_v || !work_o || !lse)
+    return fail(SQKV_EINVAL, "null pointer");
+  const int64_t n = L / P, S = L / P_r;          // tokens per shard, per ring chunk (= P_u * n)
+  const int Hl = H / P_u, Hkd = std::max(H_kv, P_u), Hkl = Hkd / P_u;
+  const int64_t qe = (int64_t)P * n * H * d, ke = (int64_t)P * n * H_kv * d, we = (int64_t)P_r * P_u * S * Hkl * d;
+  {
+    Range rq = dense_range(q, qe, 2), rk = dense_range(k, ke, 2), rv = dense_range(v, ke, 2), ro = dense_range(o, qe, 2);
+    Range wq = dense_range(work_q, qe, 2), wk = dense_range(work_k, we, 2), wv = dense_range(work_v, we, 2),
+          wo = dense_range(work_o, qe, 2), rl = dense_range(lse, (int64_t)P_r * P_u * Hl * S, 4);
+    const Range* all[] = {&rq, &rk, &rv, &ro, &wq, &wk, &wv, &wo, &rl};
+    for (int i = 0; i < 9; ++i)
+      for (int j = i + 1; j < 9; ++j)
+        if ((i >= 3 || j >= 3) && overlap(*all[i], *all[j]))
+          return fail(SQKV_EINVAL, "usp_attention buffers overlap (%d, %d)", i, j);
+  }
+  auto at = [](const void* base, int64_t elems, int eb) {
+    return static_cast<const char*>(base) + elems * eb;
+  };
+  // 1. Ulysses inside every ring row i_r: its P_u shards (a contiguous run of
+  //    S tokens) become P_u head shares of the whole run
+  for (int ir = 0; ir < P_r; ++ir) {
+    const int64_t row_q = (int64_t)ir * P_u * n * H * d, row_k = (int64_t)ir * P_u * n * H_kv * d;
+    const int64_t row_wk = (int64_t)ir * P_u * S * Hkl * d;
+    sqkv_status st = ulysses_seq_to_head(at(q, row_q, 2), (void*)at(work_q, row_q, 2), P_u, S, H, H, d, 2, stream);
+    if (st == SQKV_OK) st = ulysses_seq_to_head(at(k, row_k, 2), (void*)at(work_k, row_wk, 2), P_u, S, H_kv, Hkd, d, 2, stream);
+    if (st == SQKV_OK) st = ulysses_seq_to_head(at(v, row_k, 2), (void*)at(work_v, row_wk, 2), P_u, S, H_kv, Hkd, d, 2, stream);
+    if (st != SQKV_OK) return st;
+  }
+  // 2. a ring over the P_r rows for every head share i_u: ring rank i_r holds
+  //    tokens i_r*S .. of heads i_u*H/P_u ..; chunk j of its key/value pool is
+  //    row j's share i_u
+  for (int iu = 0; iu < P_u; ++iu)
+    for (int ir = 0; ir < P_r; ++ir) {
+      const int64_t sq = ((int64_t)ir * P_u + iu) * S * Hl * d, sk = (int64_t)iu * S * Hkl * d;
+      sqkv_view qv{(void*)at(work_q, sq, 2), 0, d, (int64_t)Hl * d};
+      sqkv_view ov{(void*)at(work_o, sq, 2), 0, d, (int64_t)Hl * d};
+      sqkv_view kv{(void*)at(work_k, sk, 2), 0, d, (int64_t)Hkl * d};
+      sqkv_view vv{(void*)at(work_v, sk, 2), 0, d, (int64_t)Hkl * d};
+      const int64_t cs = (int64_t)P_u * S * Hkl * d;
+      sqkv_status st = ra_ring_attention(qv, kv, vv, cs, cs, ov, lse + ((int64_t)ir * P_u + iu) * Hl * S, 1, Hl, Hkl,
+                                         (int)S, d, P_r, ir, SQKV_BF16, SQKV_BF16, scale, causal, stream);
+      if (st != SQKV_OK) return st;
+    }
+  // 3. back to the sequence layout inside every ring row
+  for (int ir = 0; ir < P_r; ++ir) {
+    const int64_t row_q = (int64_t)ir * P_u * n * H * d;
+    sqkv_status st = ulysses_head_to_seq(at(work_o, row_q, 2), (void*)at(o, row_q, 2), P_u, S, H, d, 2, stream);
+    if (st != SQKV_OK) return st;
+  }
+  return ok();
+}

@@ -177,6 +177,24 @@ def test_zigzag_rejects(lib):
 
 
 @no_gpu
+def test_usp_rejects(lib):
+    _setup(lib)
+    vp, i, i64, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    lib.usp_attention.argtypes = [vp] * 9 + [i, i, i64, i, i, i, f, i, vp]
+    bufs = [g * GB for g in range(1, 10)]
+
+    def call(P_u=2, P_r=2, L=1024, H=4, H_kv=2, bufs=bufs):
+        return lib.usp_attention(*bufs, P_u, P_r, L, H, H_kv, 128, 1.0, 1, None)
+
+    assert call(P_u=0) == EINVAL
+    assert call(L=1023) == EINVAL               # not a multiple of P_u * P_r
+    assert call(H=6, H_kv=2, P_u=4) == EINVAL   # H % P_u
+    assert call(H=6, H_kv=3, P_u=2) == EINVAL   # H_kv and P_u: neither divides the other
+    assert call(bufs=[None] + bufs[1:]) == EINVAL
+    assert call(bufs=bufs[:4] + [bufs[0]] + bufs[5:]) == EINVAL   # work_q overlaps q
+
+
+@no_gpu
 def test_merge_rejects(lib):
     _setup(lib)
     a, b, o = _dense(1 * GB, 4, 8, 64), _dense(2 * GB, 4, 8, 64), _dense(3 * GB, 4, 8, 64)
