@@ -12,7 +12,8 @@ Everything is plain numpy in float64, written for a reader to check against
 the pages by eye:
 
 * ``attention``  -- full (non-chunked) softmax attention, the definition the
-  chunked method must reproduce exactly up to rounding;
+  chunked method must reproduce exactly up to rounding (also at explicit
+  positions, and over packed samples that must not see each other);
 * ``ring``       -- the online-softmax / log-sum-exp merge and the ring visit
   over resident chunks, as a self-check of the merge semantics against the full
   definition;
@@ -36,7 +37,8 @@ facts other than itself (brute-force loops, closed forms, library routines,
 the pages' printed figure); ``tests/test_oracle_mutants.py`` shows that
 plausible mistakes fail those pins.  No function is left "parity unpinned".
 """
-from .attention import attention_fp64, attention_at_positions_fp64, unmasked_pairs
+from .attention import (attention_fp64, attention_at_positions_fp64, attention_packed_fp64, segment_ids,
+                        unmasked_pairs)
 from .ring import lse_merge_fp64, ring_attention_fp64, ring_visit_order
 from .ulysses import (seq_to_head_naive, head_to_seq_naive, replicated_head_source,
                       check_ulysses_shapes)
@@ -45,7 +47,7 @@ from .backward import attention_bwd_fp64, chunk_attention_bwd_fp64, rowsum_do_o_
 from .zigzag import zigzag_positions, zigzag_shard, zigzag_attention_fp64, zigzag_block_classes
 
 __all__ = [
-    "attention_fp64", "attention_at_positions_fp64", "unmasked_pairs",
+    "attention_fp64", "attention_at_positions_fp64", "attention_packed_fp64", "segment_ids", "unmasked_pairs",
     "lse_merge_fp64", "ring_attention_fp64", "ring_visit_order",
     "seq_to_head_naive", "head_to_seq_naive", "replicated_head_source",
     "check_ulysses_shapes",

@@ -118,3 +118,45 @@ def attention_at_positions_fp64(q, k, v, q_pos, k_pos, scale: float = 1.0, row_b
                 O[b, h, r0:r1] = np.where(any_vis[:, None], (w @ v[b, g]) / safe_l[:, None], 0.0)
                 lse[b, h, r0:r1] = np.where(any_vis, m + np.log(safe_l), -np.inf)
     return O, lse
+
+
+def segment_ids(L: int, seg_starts) -> np.ndarray:
+    """Sample index of every position 0..L-1 of a packed sequence whose samples
+    start at the sorted positions ``seg_starts`` (the first must be 0)."""
+    starts = np.asarray(seg_starts, dtype=np.int64)
+    if starts.size == 0 or starts[0] != 0 or np.any(np.diff(starts) <= 0) or starts[-1] >= max(L, 1):
+        raise ValueError("sample starts must be strictly increasing, begin at 0 and lie below L")
+    ids = np.zeros(L, dtype=np.int64)
+    for s in starts[1:]:
+        ids[s:] += 1
+    return ids
+
+
+def attention_packed_fp64(q, k, v, seg_starts, scale: float = 1.0, row_block: int = 256):
+    """Causal attention over a packed sequence: query t sees key u iff both lie
+    in the same sample and u <= t.  q, k, v in natural order ([B, H, L, d],
+    the same packing for every batch row)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    group = Hq // Hkv
+    ids = segment_ids(L, seg_starts)
+    O = np.zeros((B, Hq, L, d), dtype=np.float64)
+    lse = np.full((B, Hq, L), -np.inf, dtype=np.float64)
+    pos = np.arange(L)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            for r0 in range(0, L, row_block):
+                r1 = min(L, r0 + row_block)
+                s = scale * (q[b, h, r0:r1] @ k[b, g].T)
+                visible = (ids[None, :] == ids[r0:r1, None]) & (pos[None, :] <= pos[r0:r1, None])
+                s = np.where(visible, s, -np.inf)
+                m = s.max(axis=1)                        # every row sees at least itself
+                w = np.where(visible, np.exp(s - m[:, None]), 0.0)
+                l = w.sum(axis=1)
+                O[b, h, r0:r1] = (w @ v[b, g]) / l[:, None]
+                lse[b, h, r0:r1] = m + np.log(l)
+    return O, lse

@@ -568,6 +568,35 @@ def pin_backward_chunks_sum_to_full(orc):
         _close(D, Ddirect, 1e-12, "D = rowsum(P * dP)")
 
 
+# ----------------------------------------------------------------------------
+# packed samples
+# ----------------------------------------------------------------------------
+def pin_packed_equals_separate_samples(orc):
+    """Attention over a packed sequence equals causal attention run on every
+    sample by itself (the samples never see each other)."""
+    rng = np.random.default_rng(61)
+    for L, starts, Hq, Hkv, d in [(12, [0, 5, 6, 9], 2, 1, 3), (10, [0], 2, 2, 2), (9, [0, 1, 2, 3, 4, 5, 6, 7, 8], 1, 1, 2),
+                                  (16, [0, 8], 4, 2, 3)]:
+        q = rng.standard_normal((1, Hq, L, d))
+        k = rng.standard_normal((1, Hkv, L, d)) * 1.5
+        v = rng.standard_normal((1, Hkv, L, d))
+        O, lse = orc.attention_packed_fp64(q, k, v, starts, scale=0.9)
+        ends = list(starts[1:]) + [L]
+        for s0, s1 in zip(starts, ends):
+            Os, ls = orc.attention_fp64(q[:, :, s0:s1], k[:, :, s0:s1], v[:, :, s0:s1], scale=0.9, causal=True)
+            _close(O[:, :, s0:s1], Os, 1e-12, f"packed O sample {s0}..{s1}")
+            _close(lse[:, :, s0:s1], ls, 1e-12, f"packed lse sample {s0}..{s1}")
+        ids = orc.segment_ids(L, starts)
+        assert ids.tolist() == [sum(1 for s in starts if s <= t) - 1 for t in range(L)]
+    for bad in ([1, 3], [0, 3, 3], [0, 12]):
+        try:
+            orc.segment_ids(12, bad)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError(f"bad sample starts {bad} accepted")
+
+
 def pin_closed_form(orc):
     g = _load("attn_matrix_memory.json")
     b = orc.attn_matrix_bytes(g["L"], g["heads"], g["elem_bytes"])
@@ -598,4 +627,5 @@ ALL_PINS = [
     pin_backward_finite_differences,
     pin_backward_autograd,
     pin_backward_chunks_sum_to_full,
+    pin_packed_equals_separate_samples,
 ]

@@ -60,6 +60,10 @@ MUTANTS = [
      "            dk[b, g] = scale * (ds.T @ q[b, h])\n    return dq, dk, dv\n\n\ndef rowsum"),
     ("backward.py", "np.exp(s - np.where(fin, lse[b, h], 0.0)[:, None])", "np.exp(s - np.where(fin, lse[b, h], 0.0)[None, :])"),
     ("backward.py", "            ds = p * (dp - D[b, h][:, None])", "            ds = p * (dp - D[b, h][None, :])"),
+    ("attention.py", "visible = (ids[None, :] == ids[r0:r1, None]) & (pos[None, :] <= pos[r0:r1, None])",
+     "visible = (ids[None, :] <= ids[r0:r1, None]) & (pos[None, :] <= pos[r0:r1, None])"),
+    ("attention.py", "        ids[s:] += 1", "        ids[s + 1:] += 1"),
+    ("attention.py", "O[b, h, r0:r1] = (w @ v[b, g]) / l[:, None]", "O[b, h, r0:r1] = (w @ v[b, g])"),
     ("backward.py", "return (np.asarray(do, dtype=np.float64) * np.asarray(o, dtype=np.float64)).sum(axis=-1)",
      "return (np.asarray(do, dtype=np.float64) * np.asarray(o, dtype=np.float64)).sum(axis=-2)"),
 ]
