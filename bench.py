@@ -15,7 +15,8 @@ sample of the same workload.  Extra figures on the other workloads (Ulysses
 permute GB/s on 8 x [16384, 32, 128] bf16, the causal 128k rank-7 ring share,
 the causal 128k GQA Ulysses share, the whole causal 128k ring under the
 contiguous and the zigzag split, the backward of the 32k ring, the USP
-hybrid at 128k) go in "extras".  Logs go to stderr.
+hybrid at 128k, the 32k ring packing 2k-token samples) go in "extras".  Logs go
+to stderr.
 """
 from __future__ import annotations
 
@@ -266,6 +267,37 @@ def bench_usp(api, torch, steps=2):
     return res
 
 
+def bench_packed(api, torch, x, w, sample_len=2048, steps=2):
+    """The 32k ring with the sequence packing samples of `sample_len` tokens
+    (causal inside each sample, samples blind to each other).  TFLOP/s counts
+    the visible pairs only."""
+    qs, kp, vp = x["q"], x["k"], x["v"]
+    P = w.P
+    B, H, n, d = qs.shape[1:]
+    L = P * n
+    starts = torch.arange(0, L, sample_len, dtype=torch.int64, device="cuda")
+    o = torch.empty((B, H, n, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B * H * n, dtype=torch.float32, device="cuda")
+
+    def step():
+        for r in range(P):
+            api.ra_ring_attention_packed(qs[r], kp, vp, o, lse, starts, rank=r)
+
+    step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    pairs = (L // sample_len) * sample_len * (sample_len + 1) // 2
+    flops = 4 * d * pairs * B * H
+    return {"ms": round(ms, 3), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1), "flops": flops,
+            "workload": f"ring_bf16_32k packing {L // sample_len} causal samples of {sample_len} tokens"}
+
+
 def cpu_baseline(x_dev, w, torch, budget_rows=4096, heads=16):
     """The fp64 oracle on a bounded sample of the workload: query chunk 0
     (4096 rows) of the first `heads` heads against all 32768 keys."""
@@ -362,6 +394,8 @@ def main():
     extras = {}
     if not args.no_extras:
         try:
+            extras["ring_bf16_32k_packed_2k"] = bench_packed(api, torch, x, w)
+            log(f"packed: {extras['ring_bf16_32k_packed_2k']}")
             extras["ring_bf16_32k_backward"] = bench_backward(api, torch, x, w)
             log(f"backward: {extras['ring_bf16_32k_backward']}")
             extras["ulysses"] = bench_ulysses(api, torch)

@@ -136,6 +136,32 @@ sqkv_status ra_ring_attention(sqkv_view q, sqkv_view k, sqkv_view v,
                               float scale, int causal, void* stream);
 
 /*
+ * ra_ring_attention_packed -- ra_ring_attention (causal) over a sequence that
+ * packs several samples one after another.  [HF], sequence-parallel
+ * configuration notes: samples packed into one sequence are told apart by
+ * position_ids, and an attention that treats the packed sequence as one
+ * sample (as sdpa does there) lets samples see each other.  Here a query at
+ * global position t sees key u iff u <= t and both lie in the same sample.
+ *
+ *   seg_starts  int64 [n_seg], DEVICE memory: the samples' start positions in
+ *               the whole sequence of P*n tokens, strictly increasing,
+ *               seg_starts[0] = 0 (what position_ids resetting to 0 marks).
+ *               Shared by every batch row.
+ *
+ * Other arguments as ra_ring_attention (always causal).  Chunks and tiles
+ * holding no key of a block's samples are skipped.  EINVAL additionally for
+ * n_seg < 1 or a null seg_starts; EUNSUPPORTED for in_dtype other than BF16
+ * or a seg_starts pointer not 8-byte aligned.  The contents of seg_starts
+ * are not checked (they live on the device); out-of-order starts give
+ * undefined attention results but no out-of-bounds access.
+ */
+sqkv_status ra_ring_attention_packed(sqkv_view q, sqkv_view k, sqkv_view v,
+                                     int64_t k_chunk_stride, int64_t v_chunk_stride,
+                                     sqkv_view o, float* lse, const int64_t* seg_starts, int n_seg,
+                                     int B, int Hq, int Hkv, int n, int d, int P, int rank,
+                                     sqkv_dtype in_dtype, sqkv_dtype out_dtype, float scale, void* stream);
+
+/*
  * Backward of chunked attention.  [RA], "pet project" steps 5-7: after the
  * ring forward a loss is computed and backpropagated, and the result must
  * match full attention.  The pages give no formulas; the gradients are the

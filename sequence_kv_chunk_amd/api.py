@@ -64,6 +64,9 @@ _lib.ra_ring_attention_bwd.argtypes = [_V, _V, _V, _c_i64, _c_i64, _V, _vp, _vp,
 _lib.usp_attention.restype = _c_int
 _lib.usp_attention.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_i64, _c_int, _c_int,
                                _c_int, _c_f, _c_int, _vp]
+_lib.ra_ring_attention_packed.restype = _c_int
+_lib.ra_ring_attention_packed.argtypes = [_V, _V, _V, _c_i64, _c_i64, _V, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                                          _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_f, _vp]
 _lib.ra_lse_merge.restype = _c_int
 _lib.ra_lse_merge.argtypes = [_V, _vp, _c_int, _V, _vp, _c_int, _V, _vp, _c_int, _c_int, _c_int, _c_int,
                               _c_int, _vp]
@@ -72,7 +75,8 @@ _lib.ulysses_seq_to_head.argtypes = [_vp, _vp, _c_int, _c_i64, _c_int, _c_int, _
 _lib.ulysses_head_to_seq.restype = _c_int
 _lib.ulysses_head_to_seq.argtypes = [_vp, _vp, _c_int, _c_i64, _c_int, _c_int, _c_int, _vp]
 
-EXPORTED = ("ra_chunk_attention", "ra_ring_attention", "ra_zigzag_attention", "ra_lse_merge",
+EXPORTED = ("ra_chunk_attention", "ra_ring_attention", "ra_ring_attention_packed", "ra_zigzag_attention",
+            "ra_lse_merge",
             "ra_attention_bwd_preprocess", "ra_chunk_attention_bwd", "ra_ring_attention_bwd",
             "ulysses_seq_to_head", "ulysses_head_to_seq", "usp_attention", "sqkv_last_error")
 
@@ -167,6 +171,27 @@ def ra_ring_attention(q, k_pool, v_pool, o, lse, *, rank: int, scale: float = 1.
                                     v_pool.stride(0), _view(o), _lse_ptr(lse, B * Hq * n),
                                     B, Hq, k_pool.shape[2], n, d, P, int(rank), _dtype_code(q),
                                     _dtype_code(o), float(scale), int(bool(causal)), _stream(q))
+    _check(st)
+
+
+def ra_ring_attention_packed(q, k_pool, v_pool, o, lse, seg_starts, *, rank: int, scale: float = 1.0):
+    """Causal ring attention of virtual rank ``rank`` over a packed sequence:
+    ``seg_starts`` (int64 device tensor) holds the samples' start positions in
+    the whole sequence; a query sees only keys of its own sample."""
+    if k_pool.dim() != 5 or v_pool.shape != k_pool.shape:
+        raise SqkvError(SQKV_EINVAL, "k_pool, v_pool must be [P, B, Hkv, n, d]")
+    _same_device(q, k_pool, v_pool, o, lse, seg_starts)
+    if seg_starts.dtype != torch.int64 or seg_starts.dim() != 1 or not seg_starts.is_contiguous():
+        raise SqkvError(SQKV_EINVAL, "seg_starts must be a contiguous 1-D int64 tensor")
+    P = k_pool.shape[0]
+    B, Hq, n, d = q.shape
+    if tuple(o.shape) != (B, Hq, n, d) or k_pool.shape[3] != n or k_pool.shape[1] != B:
+        raise SqkvError(SQKV_EINVAL, "shapes disagree")
+    with torch.cuda.device(q.device):
+        st = _lib.ra_ring_attention_packed(_view(q), _view(k_pool[0]), _view(v_pool[0]), k_pool.stride(0),
+                                           v_pool.stride(0), _view(o), _lse_ptr(lse, B * Hq * n), seg_starts.data_ptr(),
+                                           seg_starts.numel(), B, Hq, k_pool.shape[2], n, d, P, int(rank),
+                                           _dtype_code(q), _dtype_code(o), float(scale), _stream(q))
     _check(st)
 
 

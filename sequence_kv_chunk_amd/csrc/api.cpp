@@ -171,6 +171,8 @@ sqkv::AttnParams make_params(const sqkv_view& q, const sqkv_view& k, const sqkv_
   p.q_pos0 = q_pos0;
   p.k_pos0 = k_pos0;
   p.lse_in_hs = p.lse_out_hs = n_q;   // dense [B, Hq, n_q]
+  p.seg = nullptr;
+  p.n_seg = 0;
   // a single chunk; ra_ring_attention widens this to the ring visit
   p.k_cs = p.v_cs = 0;
   p.k_posstride = 0;
@@ -229,6 +231,39 @@ SQKV_EXPORT sqkv_status ra_ring_attention(sqkv_view q, sqkv_view k, sqkv_view v,
   p.rank = rank;
   p.nseg = causal ? rank + 1 : P;
   return hip_status(launch_attention(p, d, in_dtype, (hipStream_t)stream), "ra_ring_attention launch");
+}
+
+SQKV_EXPORT sqkv_status ra_ring_attention_packed(sqkv_view q, sqkv_view k, sqkv_view v, int64_t k_chunk_stride,
+                                                 int64_t v_chunk_stride, sqkv_view o, float* lse,
+                                                 const int64_t* seg_starts, int n_seg, int B, int Hq, int Hkv, int n,
+                                                 int d, int P, int rank, sqkv_dtype in_dtype, sqkv_dtype out_dtype,
+                                                 float scale, void* stream) {
+  if (n_seg < 1 || !seg_starts) return fail(SQKV_EINVAL, "need at least one sample start (n_seg=%d)", n_seg);
+  if (((uintptr_t)seg_starts) % 8) return fail(SQKV_EUNSUPPORTED, "seg_starts must be 8-byte aligned");
+  if (in_dtype != SQKV_BF16) return fail(SQKV_EUNSUPPORTED, "packed samples need bf16 inputs");
+  if (P < 1 || rank < 0 || rank >= P) return fail(SQKV_EINVAL, "need P >= 1 and 0 <= rank < P (P=%d rank=%d)", P, rank);
+  if (k_chunk_stride < 0 || v_chunk_stride < 0) return fail(SQKV_EINVAL, "negative chunk stride");
+  if ((k_chunk_stride * 2) % 16 || (v_chunk_stride * 2) % 16)
+    return fail(SQKV_EUNSUPPORTED, "chunk strides must be multiples of 16 bytes");
+  AttnCheck a{q, k, v, sqkv_view{nullptr, 0, 0, 0}, o, nullptr, lse, B, Hq, Hkv, n, n,
+              (int64_t)(P - 1) * std::max(k_chunk_stride, v_chunk_stride) * 2, d,
+              in_dtype, SQKV_F32, out_dtype, scale};
+  sqkv_status st = check_attention(a);
+  if (st != SQKV_OK || n == 0) return st;
+  if (overlap(dense_range(seg_starts, n_seg, 8), view_range(o, B, Hq, n, d, dtype_bytes(out_dtype))) ||
+      overlap(dense_range(seg_starts, n_seg, 8), dense_range(lse, (int64_t)B * Hq * n, 4)))
+    return fail(SQKV_EINVAL, "seg_starts overlaps an output");
+  sqkv::AttnParams p = make_params(q, k, v, sqkv_view{nullptr, 0, 0, 0}, nullptr, o, lse, B, Hq, Hkv, n, n,
+                                   SQKV_F32, out_dtype, scale, 1, (int64_t)rank * n, 0);
+  p.k_cs = k_chunk_stride;
+  p.v_cs = v_chunk_stride;
+  p.k_posstride = n;
+  p.P = P;
+  p.rank = rank;
+  p.nseg = rank + 1;
+  p.seg = seg_starts;
+  p.n_seg = n_seg;
+  return hip_status(launch_attention(p, d, in_dtype, (hipStream_t)stream), "ra_ring_attention_packed launch");
 }
 
 SQKV_EXPORT sqkv_status ra_zigzag_attention(sqkv_view q, sqkv_view k, sqkv_view v, int64_t k_chunk_stride,

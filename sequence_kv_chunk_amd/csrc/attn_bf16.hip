@@ -198,7 +198,9 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int D>
+// PACKED: the sequence packs several samples (p.seg holds their sorted start
+// positions); a query sees only the keys of its own sample.
+template <int D, bool PACKED>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bf16_kernel(AttnParams p, int n_qtiles) {
@@ -322,6 +324,28 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   const int qrel = (int)min((int64_t)(1 << 30), max((int64_t)-(1 << 30), p.q_pos0 + qw0 - kpos_own));
   const int tt_mask = max(0, (qrel + 1) / kBN);
 
+  // Packed samples: the sample of a query starts at the largest sample start
+  // <= its position; lo_row for this lane's row, lo_blk for the block's first
+  // row (the earliest key any row of the block can see), lo_wmax for the
+  // wave's last row (tiles starting before it need the sample mask).
+  int64_t lo_row = 0, lo_blk = 0, lo_wmax = 0;
+  if constexpr (PACKED) {
+    auto sample_start = [&](int64_t pos) {
+      int a = 0, e = p.n_seg;
+      while (e - a > 1) {
+        const int m = (a + e) >> 1;
+        if (p.seg[m] <= pos) a = m;
+        else e = m;
+      }
+      return p.seg[a];
+    };
+    lo_row = sample_start(p.q_pos0 + min(qw0 + l32, p.n_q - 1));
+    lo_blk = sample_start(p.q_pos0 + q0);
+    const uint64_t u = (uint64_t)lo_row;
+    lo_wmax = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(u >> 32), 31) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 31));
+  }
+
   // The visit: chunks in ring order, and in each chunk the tiles holding keys
   // visible to at least one of the block's query rows.  Only the first chunk
   // (the rank's own, or the single chunk of one ring step) can be cut short
@@ -335,11 +359,44 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   }
   const int ntl0 = (int)((lim0 + kBN - 1) / kBN);
   const int ntl_full = (p.n_k + kBN - 1) / kBN;
-  const int T = ntl0 == 0 ? 0 : ntl0 + (p.nseg - 1) * ntl_full;
+  // Packed samples narrow the visit to keys from lo_blk on: own-chunk tiles
+  // from t0_own, chunks down to the one holding lo_blk (nseg_v of them), and
+  // in that last chunk the tiles from t_lo.
+  int t0_own = 0, nseg_v = p.nseg, t_lo = 0;
+  if constexpr (PACKED) {
+    if (lo_blk >= kpos_own || p.k_posstride == 0) {
+      t0_own = (int)min((int64_t)ntl0, max((int64_t)0, (lo_blk - kpos_own) / kBN));
+      nseg_v = 1;
+    } else {
+      const int64_t jl = max((int64_t)0, (lo_blk - p.k_pos0) / p.k_posstride);
+      nseg_v = min(p.nseg, p.rank - (int)jl + 1);
+      t_lo = (int)min((int64_t)ntl_full, max((int64_t)0, (lo_blk - p.k_pos0 - jl * p.k_posstride) / kBN));
+    }
+  }
+  const int T = ntl0 - t0_own <= 0 ? 0 : (ntl0 - t0_own) + (nseg_v >= 2 ? (nseg_v - 1) * ntl_full - t_lo : 0);
 
-  // Tile g of the visit with nv valid keys: own-chunk tiles from tt_mask on
-  // are masked on the causal diagonal, short tiles past their last key.
-  auto mask = [&](STile& s, int g, int nv) {
+  // Tile g of the visit with nv valid keys starting at key position kp:
+  // own-chunk tiles from tt_mask on are masked on the causal diagonal, short
+  // tiles past their last key; with packed samples, tiles reaching past the
+  // wave's first query or starting before its last row's sample are masked
+  // key by key against each row's [sample start, position].
+  const int64_t qpos_w0 = p.q_pos0 + qw0;
+  auto mask = [&](STile& s, int g, int nv, int64_t kp) {
+    if constexpr (PACKED) {
+      if (!(nv < kBN || kp + kBN - 1 > qpos_w0 || kp < lo_wmax)) return;
+      const int64_t last = min(p.q_pos0 + qw0 + l32 - kp, (int64_t)nv - 1);   // last visible key
+      const int64_t first = lo_row - kp;                                       // first visible key
+      const int lk = (int)max((int64_t)-1, min(last, (int64_t)kBN)) - 4 * hi;
+      const int fk = (int)max((int64_t)0, min(first, (int64_t)kBN + 1)) - 4 * hi;
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int u = 32 * nb + 8 * (j >> 2) + (j & 3);
+          if (u > lk || u < fk) s.b[nb][j] = kNegInf;
+        }
+      return;
+    }
     const bool diag = p.causal && g >= tt_mask && g < ntl0;
     if (!(nv < kBN || diag)) return;
     int64_t rel = (int64_t)qrel + l32 - (int64_t)g * kBN;   // last visible key of the tile
@@ -462,13 +519,16 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     int tl;                     // tiles of the current chunk from this tile on
     int j;                      // current chunk
     int left;                   // chunks of the visit after the current one
+    int64_t kp;                 // key position of the current tile (packed samples only)
   };
-  auto walk_start = [&](const unsigned char* hbase, int64_t csb) {
-    return DmaWalk{hbase + (int64_t)p.rank * csb, (int)lim0, ntl0, p.rank, p.nseg - 1};
+  auto walk_start = [&](const unsigned char* hbase, int64_t csb, int snb) {
+    return DmaWalk{hbase + (int64_t)p.rank * csb + (int64_t)t0_own * kBN * snb, (int)lim0 - t0_own * kBN,
+                   ntl0 - t0_own, p.rank, nseg_v - 1, kpos_own + (int64_t)t0_own * kBN};
   };
   auto walk_step = [&](DmaWalk& w, const unsigned char* hbase, int64_t csb, int snb) {
     w.ptr += kBN * snb;
     w.rows -= kBN;
+    if constexpr (PACKED) w.kp += kBN;
     if (--w.tl == 0) {
       if (w.left > 0) {
         w.left -= 1;
@@ -476,6 +536,15 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
         w.ptr = hbase + (int64_t)w.j * csb;
         w.rows = p.n_k;
         w.tl = ntl_full;
+        if constexpr (PACKED) {
+          w.kp = p.k_pos0 + (int64_t)w.j * p.k_posstride;
+          if (w.left == 0) {               // the last chunk starts at tile t_lo
+            w.ptr += (int64_t)t_lo * kBN * snb;
+            w.rows -= t_lo * kBN;
+            w.tl -= t_lo;
+            w.kp += (int64_t)t_lo * kBN;
+          }
+        }
       } else {
         w.rows = -(1 << 30);   // the visit is over
       }
@@ -498,13 +567,15 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     for (int i = 0; i < C::NL; ++i) dma16(voff[i], rs, stage + mw + i * kWaves * C::RPW * C::ROWB);
     return nv;
   };
-  DmaWalk wk = walk_start(kg, k_csb), wv = walk_start(vg, v_csb);
+  DmaWalk wk = walk_start(kg, k_csb, k_snb), wv = walk_start(vg, v_csb, v_snb);
+  int64_t kp_issued = 0;   // key position of the last V tile issued (packed samples)
   auto issue_k = [&](int stage) {
     issue(wk, k_snb, lds0 + C::K_LDS + stage * C::TILE, dko);
     walk_step(wk, kg, k_csb, k_snb);
   };
   auto issue_v = [&](int stage) {
     const int nv = issue(wv, v_snb, lds0 + C::V_LDS + stage * C::TILE, dvo);
+    if constexpr (PACKED) kp_issued = wv.kp;
     walk_step(wv, vg, v_csb, v_snb);
     return nv;
   };
@@ -546,13 +617,15 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     issue_k(1);
     issue_k(2);
     const int nv0 = issue_v(0);          // V(0), V(1)
+    const int64_t kp0 = kp_issued;
     issue_k(3);
     const int nv1 = issue_v(1);
+    const int64_t kp1 = kp_issued;
     wait_dma_and_sync<4 * C::NL>();      // K(0), K(1) landed
     scores(sa, Step<0>{});
     scores(sb, Step<1>{});
-    mask(sa, 0, nv0);
-    mask(sb, 1, nv1);
+    mask(sa, 0, nv0, kp0);
+    mask(sb, 1, nv1, kp1);
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) sm_group(sa, g);   // O is still zero: no rescale
 #pragma unroll
@@ -561,6 +634,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     lds_reads_done_sync();               // K stage 0 is free
     issue_k(0);                          // K(4)
     int nv_next = issue_v(2);            // V(2); valid keys of the tile masked next
+    int64_t kp_next = kp_issued;
     int g = 2;                           // tile masked at the end of the current iteration
 
     u32x4_t kfr[kMF];
@@ -585,11 +659,15 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
       constexpr int r = decltype(R)::value;
       constexpr int ks = (r + 2) % kStages, vs = r;
       const int nv_mask = nv_next;         // tile t+2
+      const int64_t kp_mask = kp_next;
       resc = false;
       static_for<kSlots>([&](auto I) {
         constexpr int i = decltype(I)::value;
         if constexpr (i == kDmaSlotK) issue_k((r + 5) % kStages);          // K(t+5)
-        if constexpr (i == kDmaSlotV) nv_next = issue_v((r + 3) % kStages);   // V(t+3)
+        if constexpr (i == kDmaSlotV) {
+          nv_next = issue_v((r + 3) % kStages);   // V(t+3)
+          kp_next = kp_issued;
+        }
         constexpr int ahead = i + kLead, fa = ahead >> 1;   // fragment needed kLead slots from now
         if constexpr ((ahead & 1) == 0) {
           if constexpr (fa >= kMF) read_k(fa - kMF, Step<(r + 3) % kStages>{});
@@ -614,7 +692,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
       });
       pin(l_run);
       if (resc) rescale();
-      mask(nx, g, nv_mask);
+      mask(nx, g, nv_mask, kp_mask);
       g += 1;
       wait_dma_and_sync<2 * C::NL, kPreLds>();   // K(t+4), V(t+2) landed
     };
@@ -670,7 +748,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   }
 }
 
-template <int D>
+template <int D, bool PACKED>
 hipError_t launch_d(const AttnParams& p, hipStream_t s) {
   using C = Cfg<D>;
   const int n_qtiles = (p.n_q + kBM - 1) / kBM;
@@ -678,12 +756,12 @@ hipError_t launch_d(const AttnParams& p, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_kernel<D>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_kernel<D, PACKED>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(attn_bf16_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), C::LDS_BYTES, s, p,
+  hipLaunchKernelGGL((attn_bf16_kernel<D, PACKED>), dim3((unsigned)blocks), dim3(kThreads), C::LDS_BYTES, s, p,
                      n_qtiles);
   return hipGetLastError();
 }
@@ -691,8 +769,8 @@ hipError_t launch_d(const AttnParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnParams& p, int d, hipStream_t s) {
-  if (d == 128) return launch_d<128>(p, s);
-  return launch_d<64>(p, s);
+  if (p.seg != nullptr) return d == 128 ? launch_d<128, true>(p, s) : launch_d<64, true>(p, s);
+  return d == 128 ? launch_d<128, false>(p, s) : launch_d<64, false>(p, s);
 }
 
 }  // namespace sqkv

@@ -41,6 +41,10 @@ struct AttnParams {
   float scale_log2;   // scale * log2(e): logits are handled in base 2
   int causal;
   int64_t q_pos0, k_pos0;
+  // packed samples (nullptr: one sample): sorted start positions, seg[0] = 0;
+  // a query sees only keys of its own sample (with the causal mask)
+  const int64_t* seg;
+  int n_seg;
 };
 
 // One chunk pair of the attention backward: query chunk (q, dout, lse, D)

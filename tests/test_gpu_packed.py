@@ -1,0 +1,53 @@
+"""Causal ring attention over packed samples (ra_ring_attention_packed)
+against the fp64 oracle: every rank of small rings, with samples that span
+chunk boundaries, start exactly on chunk and tile boundaries, are one token
+long or cover the whole sequence."""
+import numpy as np
+import pytest
+
+import oracle
+from sequence_kv_chunk_amd.synth import bf16_bits_to_f64, f32_to_bf16_bits
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from gpu_util import check_close, dev_bf16, host_f64, say  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def api():
+    from sequence_kv_chunk_amd import api
+    return api
+
+
+CASES = [
+    # P, n, Hq, Hkv, d, sample starts
+    (4, 256, 2, 2, 128, [0]),                                       # one sample: the plain causal ring
+    (4, 256, 4, 2, 128, [0, 100, 400, 401, 700, 1000]),             # samples across chunk boundaries
+    (4, 256, 2, 1, 128, [0, 256, 512, 768]),                        # one sample per chunk
+    (2, 300, 2, 2, 64, list(range(0, 600, 17))),                    # many short samples, ragged chunks
+    (1, 700, 2, 2, 128, [0, 64, 128, 129, 511, 512, 699]),          # one chunk; tile-aligned starts
+    (8, 128, 2, 2, 128, [0, 5, 900]),                               # a sample over seven chunks
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"P{c[0]}_n{c[1]}_s{len(c[5])}" for c in CASES])
+def test_packed_ring(api, case):
+    P, n, Hq, Hkv, d, starts = case
+    say(f"packed {case[:5]} {len(starts)} samples")
+    L = P * n
+    rng = np.random.default_rng(5000 + L + len(starts))
+    qb = f32_to_bf16_bits(rng.standard_normal((P, 1, Hq, n, d), dtype=np.float32) * np.float32(d ** -0.5))
+    kb = f32_to_bf16_bits(rng.standard_normal((P, 1, Hkv, n, d), dtype=np.float32))
+    vb = f32_to_bf16_bits(rng.standard_normal((P, 1, Hkv, n, d), dtype=np.float32))
+    full = lambda x: bf16_bits_to_f64(x).transpose(1, 2, 0, 3, 4).reshape(1, x.shape[2], L, d)
+    ref_o, ref_l = oracle.attention_packed_fp64(full(qb), full(kb), full(vb), starts)
+    kd, vd = dev_bf16(kb), dev_bf16(vb)
+    seg = torch.tensor(starts, dtype=torch.int64, device="cuda")
+    for r in range(P):
+        o = torch.full((1, Hq, n, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((Hq * n,), float("nan"), dtype=torch.float32, device="cuda")
+        api.ra_ring_attention_packed(dev_bf16(qb[r]), kd, vd, o, lse, seg, rank=r)
+        torch.cuda.synchronize()
+        check_close(host_f64(o), ref_o[:, :, r * n:(r + 1) * n], "bf16", f"O rank {r}")
+        check_close(host_f64(lse).reshape(1, Hq, n), ref_l[:, :, r * n:(r + 1) * n], "bf16", f"lse rank {r}")
