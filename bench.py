@@ -388,7 +388,7 @@ def main():
                    "parallelism": "single GPU; 8 virtual ranks"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "attn_bf16_kernel<128>", "flops_per_launch": per_launch_flops,
+                     "kernel": "attn_bf16_kernel<128, false>", "flops_per_launch": per_launch_flops,
                      "launch_ms": round(launch_ms, 4)},
     }
     extras = {}
