@@ -92,10 +92,11 @@ struct Cfg {
   static constexpr int K_LDS = 0;                        // kStages K tiles
   static constexpr int V_LDS = kStages * TILE;           // kStages V tiles
   static constexpr int LDS_BYTES = 2 * kStages * TILE;
+  static constexpr int LDS_ALLOC = LDS_BYTES + 16;      // + the workgroup's redo flag
   // every wave issues the same number of loads per tile, so that its vmcnt
   // bookkeeping is uniform
   static_assert(NL >= 1 && NLT % kWaves == 0, "tile loads must spread evenly over the waves");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(LDS_ALLOC <= 160 * 1024, "LDS");
 };
 
 // Position of 16-byte chunk c of tile row r: c ^ swizzle(r).
@@ -254,7 +255,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   // ---- Q fragments (B operand of S^T = K Q^T) -------------------------------
   // lane holds Q[row = qw0 + l32][16*kc + 8*hi .. +7]
   u32x4_t qf[C::KC];
-  {
+  auto load_q = [&]() {
     const int row = qw0 + l32;
     const bool ok = row < p.n_q;
     const uint16_t* src = qg + (int64_t)(ok ? row : 0) * p.q_sn + 8 * hi;
@@ -263,8 +264,20 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
       const u32x4_t z = {0u, 0u, 0u, 0u};
       qf[kc] = ok ? *reinterpret_cast<const u32x4_t*>(src + 16 * kc) : z;
     }
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // Q is in registers before any DMA is counted
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // Q is in registers before any DMA is counted
+  };
+  // Q * scale*log2(e), rounded to bf16: the scores come out of the MFMA in
+  // base-2 units (the fast pass)
+  auto prescale_q = [&](float cs) {
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t u = qf[kc][w];
+        qf[kc][w] = pack_bf16x2(__uint_as_float(u << 16) * cs, __uint_as_float(u & 0xffff0000u) * cs);
+      }
+  };
+  load_q();
 
   // ---- per-lane LDS offsets ---------------------------------------------------
   // K fragment (A operand of S^T): row l32, 16-byte chunk 2*kc + hi
@@ -427,8 +440,18 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   // P columns cc (16 keys of the P V contraction step cc) are x(8*cc) ..
   // x(8*cc + 7).  The groups are spread over the MFMAs of the next tiles;
   // none is a long dependency chain (the wave issues in order).
-  auto sm_group = [&](STile& v, int g) {
+  // The fast pass (FAST) takes the scores as base-2 exponents directly: no
+  // maximum, no subtraction; only the exponential groups remain.
+  auto sm_group = [&](STile& v, int g, auto fast) {
     auto x = [&](int e) { return v.b[e >> 4][e & 15]; };
+    if constexpr (decltype(fast)::value) {
+      if (g >= 6) {
+        const int e0 = 4 * (g - 6);
+#pragma unroll
+        for (int e = e0; e < e0 + 4; ++e) v.b[e >> 4][e & 15] = __builtin_amdgcn_exp2f(x(e));
+      }
+      return;
+    }
     if (g == 0) {                      // partial maxima over x(0..11)
 #pragma unroll
       for (int k = 0; k < 4; ++k) mpart[k] = __builtin_fmaxf(__builtin_fmaxf(x(3 * k), x(3 * k + 1)), x(3 * k + 2));
@@ -567,7 +590,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     for (int i = 0; i < C::NL; ++i) dma16(voff[i], rs, stage + mw + i * kWaves * C::RPW * C::ROWB);
     return nv;
   };
-  DmaWalk wk = walk_start(kg, k_csb, k_snb), wv = walk_start(vg, v_csb, v_snb);
+  DmaWalk wk, wv;
   int64_t kp_issued = 0;   // key position of the last V tile issued (packed samples)
   auto issue_k = [&](int stage) {
     issue(wk, k_snb, lds0 + C::K_LDS + stage * C::TILE, dko);
@@ -611,7 +634,20 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     return after_exp > after_pv ? after_exp : after_pv;
   };
 
-  if (T > 0) {
+  // One pass over the visit.  The state starts afresh: the fast pass with the
+  // reference exponent fixed at 0, the exact pass with the running maximum.
+  auto run_pass = [&](auto fast) {
+    constexpr bool FAST = decltype(fast)::value;
+#pragma unroll
+    for (int md = 0; md < C::MD; ++md) oacc[md] = (f32x16_t){};
+    m_run = FAST ? 0.f : kNegInf;
+    l_run = 0.f;
+    alpha = 1.f;
+    mneg = 0.f;
+    resc = false;
+    wk = walk_start(kg, k_csb, k_snb);
+    wv = walk_start(vg, v_csb, v_snb);
+    kp_issued = 0;
     STile sa, sb;
     issue_k(0);                          // K(0) .. K(3) into stages 0..3
     issue_k(1);
@@ -627,7 +663,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     mask(sa, 0, nv0, kp0);
     mask(sb, 1, nv1, kp1);
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) sm_group(sa, g);   // O is still zero: no rescale
+    for (int g = 0; g < kGroups; ++g) sm_group(sa, g, fast);   // O is still zero: no rescale
 #pragma unroll
     for (int cc = 0; cc < kNCC; ++cc) pack(sa, cc);
     pin(l_run);
@@ -680,7 +716,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
         if constexpr ((i & 1) == 0) mfma_s(nx, kfr[m], m);
         else mfma_pv(vfr[m], m / C::MD, m % C::MD);
         static_for<kGroups>([&](auto G) {
-          if constexpr (kSlotOfGroup(decltype(G)::value) == i) sm_group(cu, decltype(G)::value);
+          if constexpr (kSlotOfGroup(decltype(G)::value) == i) sm_group(cu, decltype(G)::value, fast);
         });
         static_for<kNCC>([&](auto Q) {
           if constexpr (kSlotOfPack(decltype(Q)::value) == i) pack(cu, decltype(Q)::value);
@@ -691,7 +727,8 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
         if constexpr (kSlotOfPack(decltype(Q)::value) >= kSlots) pack(cu, decltype(Q)::value);
       });
       pin(l_run);
-      if (resc) rescale();
+      if constexpr (!FAST)
+        if (resc) rescale();
       mask(nx, g, nv_mask, kp_mask);
       g += 1;
       wait_dma_and_sync<2 * C::NL, kPreLds>();   // K(t+4), V(t+2) landed
@@ -705,6 +742,34 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
       body(Step<3>{}, sb, sa);
     }
     pv(Step<0>{});                       // V of the last (padded) tile landed above
+    };
+
+  // The fast pass (Q pre-scaled by scale*log2(e) and rounded to bf16, weights
+  // 2^score with no maximum subtracted) is kept when every row's sum lies in
+  // [2^-24, 2^40] and every accumulator is finite: then no weight overflowed,
+  // the ones that underflowed are below 2^-100 of the sum, and no row's
+  // scores sit far from zero, where the rounding of the pre-scaled Q (half a
+  // bf16 unit per element, the size of Q's own rounding to bf16) moves a
+  // score furthest.  Otherwise the whole workgroup (its waves share the LDS
+  // pipeline) runs the exact pass with the running maximum.
+  volatile int* redo_flag = reinterpret_cast<volatile int*>(smem + C::LDS_BYTES);
+  if (threadIdx.x == 0) *redo_flag = 0;
+  if (T > 0) {
+    prescale_q(c);
+    run_pass(std::true_type{});
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    const float lt = sum_half(l_run);
+    bool ok = (qw0 + l32 >= p.n_q) || (lt >= 0x1p-24f && lt <= 0x1p40f);
+#pragma unroll
+    for (int md = 0; md < C::MD; ++md)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ok &= __builtin_isfinite(oacc[md][j]);
+    if (__any(!ok) && lane == 0) *redo_flag = 1;
+    lds_reads_done_sync();   // (the first barrier of the pass ordered the clearing before this)
+    if (*redo_flag != 0) {
+      load_q();
+      run_pass(std::false_type{});
+    }
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no DMA may outlive the workgroup's LDS
 
@@ -757,11 +822,11 @@ hipError_t launch_d(const AttnParams& p, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_kernel<D, PACKED>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_ALLOC);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((attn_bf16_kernel<D, PACKED>), dim3((unsigned)blocks), dim3(kThreads), C::LDS_BYTES, s, p,
+  hipLaunchKernelGGL((attn_bf16_kernel<D, PACKED>), dim3((unsigned)blocks), dim3(kThreads), C::LDS_ALLOC, s, p,
                      n_qtiles);
   return hipGetLastError();
 }

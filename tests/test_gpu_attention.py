@@ -131,6 +131,68 @@ def test_running_max_rescale(api, in_dt):
     assert np.max(np.abs(got_l - ref_l) / np.maximum(np.abs(ref_l), 1.0)) < (1e-5 if in_dt == "f32" else 1e-3)
 
 
+def _extreme_inputs(B, H, nq, nk, d, seed, kind):
+    """bf16 inputs whose base-2 scores leave float's range without a shift.
+
+    Every key and query shares a large common direction u, so every score of a
+    row is far from zero whatever the mask: "overflow" puts them near +384
+    (nats), "underflow" near -256, both with a spread of a few nats from the
+    rest; "mixed" is overflow on even heads and ordinary scores on odd heads
+    (workgroups of one launch take different passes)."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, nq, d), dtype=np.float32)
+    k = rng.standard_normal((B, H, nk, d), dtype=np.float32)
+    v = rng.standard_normal((B, H, nk, d), dtype=np.float32)
+    u = rng.standard_normal((B, H, 1, d), dtype=np.float32)
+    if kind == "underflow":
+        q, k = np.float32(-2.0) * u + np.float32(0.1) * q, u + np.float32(0.1) * k
+    else:
+        qx, kx = np.float32(3.0) * u + np.float32(0.3) * q, u + np.float32(0.3) * k
+        if kind == "mixed":
+            qx[:, 1::2] = q[:, 1::2] / np.float32(math.sqrt(d))
+            kx[:, 1::2] = k[:, 1::2]
+        q, k = qx, kx
+    bits = [f32_to_bf16_bits(x) for x in (q, k, v)]
+    return [bf16_bits_to_f64(b) for b in bits], [dev_bf16(b) for b in bits]
+
+
+def _check_extreme(o, lse, ref_o, ref_l, what):
+    check_close(host_f64(o), ref_o, "bf16", f"{what} O")
+    check_close(host_f64(lse).reshape(ref_l.shape), ref_l, "bf16", f"{what} lse")
+
+
+@pytest.mark.parametrize("kind", ["overflow", "underflow", "mixed"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fast_pass_fallback(api, kind, causal):
+    """Scores whose exponentials leave float's range without a shift: the
+    workgroups concerned redo the visit with the running maximum."""
+    B, H, nq, nk, d = 1, 4, 520, 600, 128
+    say(f"fast-pass fallback {kind} causal={causal}")
+    (q, k, v), (qd, kd, vd) = _extreme_inputs(B, H, nq, nk, d, seed=31, kind=kind)
+    ref_o, ref_l = oracle.attention_fp64(q, k, v, scale=1.0, causal=causal, q_pos0=nk - nq)
+    o, lse = _out(B, H, nq, d, torch.float32)
+    api.ra_chunk_attention(qd, kd, vd, o, lse, scale=1.0, causal=causal, q_pos0=nk - nq)
+    torch.cuda.synchronize()
+    _check_extreme(o, lse, ref_o, ref_l, kind)
+
+
+def test_fast_pass_fallback_ring(api):
+    """The fallback over a ring visit of three chunks (the walkers restart)."""
+    P, B, H, n, d = 3, 1, 2, 300, 128
+    say("fast-pass fallback ring")
+    (q, k, v), (qd, kd, vd) = _extreme_inputs(B, H, P * n, P * n, d, seed=33, kind="mixed")
+    ref_o, ref_l = oracle.attention_fp64(q, k, v, scale=1.0, causal=True)
+    pool = lambda x: x.reshape(B, H, P, n, d).permute(2, 0, 1, 3, 4).contiguous()
+    kp, vp = pool(kd), pool(vd)
+    for i in range(P):
+        o, lse = _out(B, H, n, d, torch.bfloat16)
+        api.ra_ring_attention(qd[:, :, i * n:(i + 1) * n].contiguous(), kp, vp, o, lse, rank=i, scale=1.0,
+                              causal=True)
+        torch.cuda.synchronize()
+        sl = slice(i * n, (i + 1) * n)
+        _check_extreme(o, lse, ref_o[:, :, sl], ref_l[:, :, sl], f"rank {i}")
+
+
 def test_shd_layout_gqa(api):
     """A Ulysses share in its natural [S, H, d] layout (strided views), GQA 4:1, causal."""
     S, Hq, Hkv, d = 700, 4, 1, 128

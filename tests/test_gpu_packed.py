@@ -51,3 +51,32 @@ def test_packed_ring(api, case):
         torch.cuda.synchronize()
         check_close(host_f64(o), ref_o[:, :, r * n:(r + 1) * n], "bf16", f"O rank {r}")
         check_close(host_f64(lse).reshape(1, Hq, n), ref_l[:, :, r * n:(r + 1) * n], "bf16", f"lse rank {r}")
+
+
+def test_packed_fast_pass_fallback(api):
+    """Scores near +384 (weights past float's range without a shift) on one head:
+    its workgroups redo the visit with the running maximum; the other head's
+    do not."""
+    P, n, H, d, starts = 2, 300, 2, 128, [0, 150, 451]
+    say("packed fast-pass fallback")
+    L = P * n
+    rng = np.random.default_rng(77)
+    q = rng.standard_normal((P, 1, H, n, d), dtype=np.float32) * np.float32(d ** -0.5)
+    k = rng.standard_normal((P, 1, H, n, d), dtype=np.float32)
+    u = rng.standard_normal(d, dtype=np.float32)        # head 0: every score near +384 (nats)
+    q[:, :, 0] = np.float32(3.0) * u + np.float32(0.3 * d ** 0.5) * q[:, :, 0]
+    k[:, :, 0] = u + np.float32(0.3) * k[:, :, 0]
+    qb = f32_to_bf16_bits(q)
+    kb = f32_to_bf16_bits(k)
+    vb = f32_to_bf16_bits(rng.standard_normal((P, 1, H, n, d), dtype=np.float32))
+    full = lambda x: bf16_bits_to_f64(x).transpose(1, 2, 0, 3, 4).reshape(1, x.shape[2], L, d)
+    ref_o, ref_l = oracle.attention_packed_fp64(full(qb), full(kb), full(vb), starts)
+    kd, vd = dev_bf16(kb), dev_bf16(vb)
+    seg = torch.tensor(starts, dtype=torch.int64, device="cuda")
+    for r in range(P):
+        o = torch.full((1, H, n, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((H * n,), float("nan"), dtype=torch.float32, device="cuda")
+        api.ra_ring_attention_packed(dev_bf16(qb[r]), kd, vd, o, lse, seg, rank=r)
+        torch.cuda.synchronize()
+        check_close(host_f64(o), ref_o[:, :, r * n:(r + 1) * n], "bf16", f"O rank {r}")
+        check_close(host_f64(lse).reshape(1, H, n), ref_l[:, :, r * n:(r + 1) * n], "bf16", f"lse rank {r}")
