@@ -44,8 +44,15 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    with open(ATTN_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the attention kernel's code: `//` comments and blank
+    lines are dropped, so that editing a comment keeps the counters valid."""
+    lines = []
+    with open(ATTN_SRC, encoding="utf-8") as f:
+        for ln in f:
+            code = ln.split("//", 1)[0].rstrip()
+            if code:
+                lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
 def load_traffic():

@@ -14,17 +14,17 @@
 //   registers.  Two waves per SIMD let the hardware overlap one wave's LDS
 //   reads and softmax arithmetic with the other wave's MFMAs; a wave fits in
 //   256 registers.
-// * Keys are processed in tiles of 32.  Scores are computed transposed,
-//   S^T = K Q^T (keys on the MFMA M axis, queries on N): in the 32x32
-//   accumulator layout a lane holds 16 keys of ONE query, so the row max and
-//   row sum are in-lane reductions plus one v_permlane32_swap with the lane 32
-//   apart.
+// * Keys are processed in tiles of 64 (two 32-key MFMA blocks).  Scores are
+//   computed transposed, S^T = K Q^T (keys on the MFMA M axis, queries on N):
+//   in the 32x32 accumulator layout a lane holds 16 keys of ONE query per
+//   block, so the row max and row sum are in-lane reductions plus one
+//   v_permlane32_swap with the lane 32 apart.
 // * Those accumulators, rounded to bf16, are directly the B operand of
 //   O^T = V^T P^T; the key order inside a 16-key contraction step follows the
 //   accumulator layout and the V^T operand is read in that order with
 //   ds_read_b64_tr_b16 (a 4x16 block of V rows transposed across 16 lanes),
 //   so V is stored in LDS exactly as it sits in memory.
-// * K and V tiles (32 keys x d) are copied global -> LDS by buffer_load ...
+// * K and V tiles (64 keys x d) are copied global -> LDS by buffer_load ...
 //   lds (16 bytes per lane, no register staging); rows past the end of a
 //   chunk fall outside the buffer's range and arrive as zeros.  16-byte chunks
 //   of a row are XOR-swizzled so that the K fragment reads (ds_read_b128) and
@@ -43,12 +43,18 @@
 //   would otherwise wait for every in-flight LDS DMA before each LDS read.
 //   The tile count is padded to 4k+1 with empty tiles (fully masked,
 //   zero-filled), which contribute nothing.
-// * Softmax runs in base 2 with scale*log2(e) folded into one FMA.  The
-//   running maximum is only moved (and O rescaled) when a tile raises it by
-//   more than kRescaleLog2; weights are taken against the slightly stale
-//   maximum in between, which leaves the normalised result unchanged and
-//   bounds weights by 2^kRescaleLog2.  The row sum is taken over the weights
-//   as they enter the P V product (rounded to bf16).
+// * Softmax runs in base 2, in up to two passes over the visit.  The fast
+//   pass multiplies Q by scale*log2(e) once (rounded to bf16), so the scores
+//   come out of the MFMA as base-2 exponents, and takes 2^score as the weight
+//   with no maximum: one exponential per score and nothing else.  A
+//   workgroup keeps its result when every row sum lies in a range that rules
+//   out overflow, harmful underflow and large scores; otherwise it runs the
+//   exact pass: scale*log2(e) folded into one FMA with the running maximum,
+//   which is only moved (and O rescaled) when a tile raises it by more than
+//   kRescaleLog2; weights are taken against the slightly stale maximum in
+//   between, which leaves the normalised result unchanged and bounds weights
+//   by 2^kRescaleLog2.  The row sum is taken over the weights as they enter
+//   the P V product (rounded to bf16).
 // * Masks (causal diagonal, ragged chunk end) are applied only to tiles that
 //   need them; tiles entirely in the future of the whole block are never
 //   fetched.
@@ -626,14 +632,18 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   // of columns cc, so it comes after the exponentials of those columns (groups
   // 6 + 2*cc, 7 + 2*cc) and after the last P V MFMA of this iteration that
   // reads them (slot 2*MD*(cc+1) - 1); a pack that falls past the last slot
-  // runs after the slot loop.
-  constexpr auto kSlotOfGroup = [](int g) { return (g * kSlots) / (kGroups + kNCC); };
-  constexpr auto kSlotOfPack = [](int cc) {
-    const int after_exp = ((7 + 2 * cc) * kSlots) / (kGroups + kNCC) + 1;
+  // runs after the slot loop.  The fast pass has only the exponential groups:
+  // they are spread evenly over the slots.
+  constexpr int kFastLead = 2;
+  constexpr auto kSlotOfGroup = [](int g, bool fast) {
+    if (fast) return g < 6 ? -1 : kFastLead + ((g - 6) * kSlots) / 8;
+    return (g * kSlots) / (kGroups + kNCC);
+  };
+  constexpr auto kSlotOfPack = [=](int cc, bool fast) {
+    const int after_exp = kSlotOfGroup(7 + 2 * cc, fast) + 1;
     const int after_pv = 2 * C::MD * (cc + 1);
     return after_exp > after_pv ? after_exp : after_pv;
   };
-
   // One pass over the visit.  The state starts afresh: the fast pass with the
   // reference exponent fixed at 0, the exact pass with the running maximum.
   auto run_pass = [&](auto fast) {
@@ -716,15 +726,15 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
         if constexpr ((i & 1) == 0) mfma_s(nx, kfr[m], m);
         else mfma_pv(vfr[m], m / C::MD, m % C::MD);
         static_for<kGroups>([&](auto G) {
-          if constexpr (kSlotOfGroup(decltype(G)::value) == i) sm_group(cu, decltype(G)::value, fast);
+          if constexpr (kSlotOfGroup(decltype(G)::value, FAST) == i) sm_group(cu, decltype(G)::value, fast);
         });
         static_for<kNCC>([&](auto Q) {
-          if constexpr (kSlotOfPack(decltype(Q)::value) == i) pack(cu, decltype(Q)::value);
+          if constexpr (kSlotOfPack(decltype(Q)::value, FAST) == i) pack(cu, decltype(Q)::value);
         });
         __builtin_amdgcn_sched_barrier(0);
       });
       static_for<kNCC>([&](auto Q) {
-        if constexpr (kSlotOfPack(decltype(Q)::value) >= kSlots) pack(cu, decltype(Q)::value);
+        if constexpr (kSlotOfPack(decltype(Q)::value, FAST) >= kSlots) pack(cu, decltype(Q)::value);
       });
       pin(l_run);
       if constexpr (!FAST)
