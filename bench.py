@@ -37,17 +37,21 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 METRIC = "chunked-attention TFLOP/s (% bf16 MFMA peak); Ulysses permute GB/s (% HBM)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_ring32k_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "sequence_kv_chunk_amd", "csrc", "attn_bf16.hip")
+MFMA_FILE = os.path.join(ROOT, "profiles", "attn_bf16_ring32k_mfma.json")
+PERMUTE_SRC = os.path.join(ROOT, "sequence_kv_chunk_amd", "csrc", "ulysses.hip")
+PERMUTE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ulysses_permute_131k_traffic.json")
+EXTRAS = ("packed", "backward", "ulysses", "rank7", "ulysses_share", "causal_split", "usp")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """sha256[:16] of the attention kernel's code: `//` comments and blank
-    lines are dropped, so that editing a comment keeps the counters valid."""
+def kernel_source_hash(path: str = ATTN_SRC) -> str:
+    """sha256[:16] of a kernel file's code: `//` comments and blank lines are
+    dropped, so that editing a comment keeps the counters valid."""
     lines = []
-    with open(ATTN_SRC, encoding="utf-8") as f:
+    with open(path, encoding="utf-8") as f:
         for ln in f:
             code = ln.split("//", 1)[0].rstrip()
             if code:
@@ -55,17 +59,24 @@ def kernel_source_hash() -> str:
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
-def load_traffic():
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    passes, if they were taken on the current kernel source."""
+def load_profile(path: str, src: str):
+    """A committed rocprofv3 counter summary, if it was taken on the current
+    kernel source (else None: the counters describe older code)."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if t.get("kernel_source_sha256_16") != kernel_source_hash(src):
         return None
-    return t.get("bytes_per_launch")
+    return t
+
+
+def load_traffic():
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    passes, if they were taken on the current kernel source."""
+    t = load_profile(TRAFFIC_FILE, ATTN_SRC)
+    return None if t is None else t.get("bytes_per_launch")
 
 
 def time_ring(api, torch, w, x, steps, warmup):
@@ -99,15 +110,20 @@ def time_ring(api, torch, w, x, steps, warmup):
 
 
 def bench_ulysses(api, torch, iters=10):
+    """Ulysses seq->head and head->seq on 8 shards of [16384, 32, 128] bf16.
+    Every launch is timed on its own with HIP events on the stream it runs on,
+    after a 768 MiB fill that evicts the 256 MiB last-level cache, so each
+    launch reads from HBM.  A plain device copy of the same bytes, timed the
+    same way, gives the streaming ceiling the permute is held against."""
     from sequence_kv_chunk_amd.synth import ULYSSES_WORKLOADS, device_ulysses_input
     w = ULYSSES_WORKLOADS["ulysses_131k_32h"]
     src = device_ulysses_input(w)
     mid = torch.empty((w.P, w.L, w.H // w.P, w.d), dtype=torch.bfloat16, device="cuda")
     back = torch.empty_like(src)
     flush = torch.empty(768 << 20, dtype=torch.uint8, device="cuda")   # > 256 MiB MALL
-    res = {}
-    for name, fn in (("seq_to_head", lambda: api.ulysses_seq_to_head(src, mid)),
-                     ("head_to_seq", lambda: api.ulysses_head_to_seq(mid, back))):
+    nbytes = w.bytes_per_direction()
+
+    def timed(fn):
         fn()
         ts = []
         for _ in range(iters):
@@ -118,16 +134,37 @@ def bench_ulysses(api, torch, iters=10):
             e1.record()
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
+        return ts
+
+    res = {}
+    for name, fn in (("seq_to_head", lambda: api.ulysses_seq_to_head(src, mid)),
+                     ("head_to_seq", lambda: api.ulysses_head_to_seq(mid, back))):
+        ts = timed(fn)
+        avg = sum(ts) / len(ts)
         ts.sort()
-        med = ts[len(ts) // 2]
-        gbs = w.bytes_per_direction() / (med * 1e-3) / 1e9
-        res[name] = {"ms_median": round(med, 4), "ms_min": round(ts[0], 4), "GB/s": round(gbs, 1),
-                     "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        res[name] = {"ms_avg": round(avg, 4), "ms_median": round(ts[len(ts) // 2], 4), "ms_min": round(ts[0], 4),
+                     "GB/s": round(nbytes / (avg * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(nbytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     torch.cuda.synchronize()
     ok = bool(torch.equal(back.view(torch.int16), src.view(torch.int16)))
+    copy_ts = timed(lambda: back.copy_(src))
+    copy_avg = sum(copy_ts) / len(copy_ts)
+    res["plain_copy_same_bytes"] = {"ms_avg": round(copy_avg, 4),
+                                    "GB/s": round(nbytes / (copy_avg * 1e-3) / 1e9, 1),
+                                    "kernel": "torch copy_ of 1 GiB (read 1 GiB + write 1 GiB)"}
     res["round_trip_bit_exact"] = ok
     res["workload"] = "ulysses_131k_32h: 8 shards [16384, 32, 128] bf16 <-> [131072, 4, 128]"
-    res["bytes_per_direction"] = w.bytes_per_direction()
+    res["bytes_per_direction"] = nbytes
+    prof = load_profile(PERMUTE_TRAFFIC_FILE, PERMUTE_SRC)
+    both_ms = (res["seq_to_head"]["ms_avg"] + res["head_to_seq"]["ms_avg"]) / 2
+    achieved = nbytes / (both_ms * 1e-3) / 1e9
+    res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                       "frac": round(achieved / PEAK_HBM_GBS, 4),
+                       "traffic": None if prof is None else prof.get("bytes_per_launch"),
+                       "kernel": "permute_kernel<16, *> (seq->head and head->seq, mean of the two)",
+                       "bytes_per_launch": nbytes, "launch_ms": round(both_ms, 4)}
+    del src, mid, back, flush
+    torch.cuda.empty_cache()
     return res
 
 
@@ -341,6 +378,10 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads' figures")
+    ap.add_argument("--extras", default="all",
+                    help="comma-separated subset of " + ",".join(EXTRAS) + " (default: all)")
+    ap.add_argument("--only-extras", action="store_true",
+                    help="skip the ring and the CPU baseline; print the chosen extras only (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
@@ -354,10 +395,11 @@ def main():
     from sequence_kv_chunk_amd import api
     from sequence_kv_chunk_amd.synth import WORKLOADS, device_attention_inputs
 
-    w = WORKLOADS["ring_bf16_32k"]
-    x = device_attention_inputs(w)
-    torch.cuda.synchronize()
-    log(f"workload {w.name}: inputs resident ({sum(t.numel() * 2 for t in x.values()) / 2**30:.2f} GiB)")
+    chosen = () if args.no_extras else (EXTRAS if args.extras == "all" else tuple(args.extras.split(",")))
+    unknown = [e for e in chosen if e not in EXTRAS]
+    if unknown:
+        print(f"bench.py: unknown extras {unknown}; choose from {','.join(EXTRAS)}", file=sys.stderr)
+        sys.exit(2)
 
     if args.calibrate_copy:
         a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
@@ -366,6 +408,28 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    w = WORKLOADS["ring_bf16_32k"]
+    x = device_attention_inputs(w)
+    torch.cuda.synchronize()
+    log(f"workload {w.name}: inputs resident ({sum(t.numel() * 2 for t in x.values()) / 2**30:.2f} GiB)")
+
+    result = {}
+    if not args.only_extras:
+        result = ring_result(api, torch, w, x, args)
+    extras = run_extras(api, torch, w, x, chosen)
+    if not args.no_cpu and not args.only_extras:
+        result["cpu_baseline"] = cpu_baseline(x, w, torch)
+        log(f"cpu baseline: {result['cpu_baseline']}")
+    elif not args.only_extras:
+        result["cpu_baseline"] = None
+    if extras:
+        result["extras"] = extras
+    print(json.dumps(result), flush=True)
+
+
+def ring_result(api, torch, w, x, args):
+    """The headline line: the 32k ring step, its throughput and the roofline
+    of the chunk-attention kernel."""
     wall_ms, gpu_ms, launches = time_ring(api, torch, w, x, args.steps, args.warmup)
     flops = w.flops()
     value = flops / (wall_ms * 1e-3) / 1e12
@@ -373,10 +437,10 @@ def main():
     launch_ms = gpu_ms / launches      # the timed region holds only chunk-attention launches
     achieved = per_launch_flops / (launch_ms * 1e-3) / 1e12
     traffic = load_traffic()
+    mfma = load_profile(MFMA_FILE, ATTN_SRC)
     log(f"ring step {wall_ms:.3f} ms (events {gpu_ms:.3f} ms), {value:.1f} TFLOP/s, "
         f"{launches} launches of {launch_ms:.4f} ms")
-
-    result = {
+    return {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
@@ -396,36 +460,31 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "kernel": "attn_bf16_kernel<128, false>", "flops_per_launch": per_launch_flops,
-                     "launch_ms": round(launch_ms, 4)},
+                     "launch_ms": round(launch_ms, 4),
+                     "mfma_busy_pct_counters": None if mfma is None else mfma.get("MfmaUtil_pct")},
     }
+
+
+def run_extras(api, torch, w, x, chosen):
+    """The other workloads' figures; a failure here never hides the main line."""
     extras = {}
-    if not args.no_extras:
-        try:
-            extras["ring_bf16_32k_packed_2k"] = bench_packed(api, torch, x, w)
-            log(f"packed: {extras['ring_bf16_32k_packed_2k']}")
-            extras["ring_bf16_32k_backward"] = bench_backward(api, torch, x, w)
-            log(f"backward: {extras['ring_bf16_32k_backward']}")
-            extras["ulysses"] = bench_ulysses(api, torch)
-            log(f"ulysses: {extras['ulysses']}")
-            extras["ring_bf16_128k_rank7_causal"] = bench_attention_extra(api, torch, "ring_bf16_128k_rank7_causal")
-            log(f"rank7 causal: {extras['ring_bf16_128k_rank7_causal']}")
-            extras["ulysses_share_gqa_128k_causal"] = bench_attention_extra(api, torch,
-                                                                            "ulysses_share_gqa_128k_causal")
-            log(f"ulysses share: {extras['ulysses_share_gqa_128k_causal']}")
-            extras["causal_128k_ring_split"] = bench_causal_split(api, torch)
-            log(f"causal split: {extras['causal_128k_ring_split']}")
-            extras["usp_128k_causal"] = bench_usp(api, torch)
-            log(f"usp: {extras['usp_128k_causal']}")
-        except Exception as e:  # extras never hide the main line
-            extras["error"] = repr(e)
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(x, w, torch)
-        log(f"cpu baseline: {result['cpu_baseline']}")
-    else:
-        result["cpu_baseline"] = None
-    if extras:
-        result["extras"] = extras
-    print(json.dumps(result), flush=True)
+    runs = (("packed", "ring_bf16_32k_packed_2k", lambda: bench_packed(api, torch, x, w)),
+            ("backward", "ring_bf16_32k_backward", lambda: bench_backward(api, torch, x, w)),
+            ("ulysses", "ulysses", lambda: bench_ulysses(api, torch)),
+            ("rank7", "ring_bf16_128k_rank7_causal",
+             lambda: bench_attention_extra(api, torch, "ring_bf16_128k_rank7_causal")),
+            ("ulysses_share", "ulysses_share_gqa_128k_causal",
+             lambda: bench_attention_extra(api, torch, "ulysses_share_gqa_128k_causal")),
+            ("causal_split", "causal_128k_ring_split", lambda: bench_causal_split(api, torch)),
+            ("usp", "usp_128k_causal", lambda: bench_usp(api, torch)))
+    try:
+        for key, name, fn in runs:
+            if key in chosen:
+                extras[name] = fn()
+                log(f"{name}: {extras[name]}")
+    except Exception as e:
+        extras["error"] = repr(e)
+    return extras
 
 
 if __name__ == "__main__":

@@ -13,9 +13,13 @@
 // 2 B = 1 KiB, i.e. exactly one 64-lane x 16-byte wavefront access, so every
 // read and every write is already a full, aligned, coalesced transaction; an
 // LDS transpose would add traffic without improving coalescing.  The kernel is
-// therefore a streaming copy: each thread keeps kItems independent 16-byte
-// loads in flight, then stores them, with non-temporal hints (the data is
-// touched once).
+// therefore a streaming copy with non-temporal hints (the data is touched
+// once).  Each thread moves kItems vectors (16 bytes where the run allows).
+// Measured at the 128k shape: one vector per thread in 256-thread workgroups
+// reaches ~6.4 TB/s, as fast as a plain linear copy of the same bytes in the
+// same launch shape, while four vectors per thread (more loads in flight, 4x
+// fewer workgroups) reach ~6.0 TB/s and plain (temporal) loads and stores
+// ~5.2 TB/s.
 #include "sqkv_internal.h"
 
 namespace sqkv {
@@ -52,7 +56,7 @@ template <> struct VecOf<2> { typedef uint16_t T; };
 template <> struct VecOf<1> { typedef uint8_t T; };
 
 constexpr int kThreads = 256;
-constexpr int kItems = 4;
+constexpr int kItems = 1;
 
 enum Mode { kSeqToHead = 0, kSeqToHeadRep = 1, kHeadToSeq = 2 };
 
