@@ -337,17 +337,63 @@ attn_bwd_dq_kernel(BwdParams p, int n_qtiles) {
 // ============================================================================
 constexpr int kKvWaves = 4;
 constexpr int kKvRows = 32 * kKvWaves;
+constexpr int kKvStages = 3;   // LDS stages of (Q tile, dO tile, lse, D)
 
+template <int R>
+using Step = std::integral_constant<int, R>;
+
+// f(Step<0>{}), ..., f(Step<N-1>{}) as straight-line code.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(Step<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Keeps a value in registers at this point of the program (the compiler may
+// not sink its computation past it or recompute it later).
+template <typename T>
+__device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
+
+// S and dP of one 32-query block for the wave's 32 keys: element j holds
+// query 8*(j/4) + 4*hi + j%4 of the block, key `key` (lane % 32).
+struct SdBlock {
+  f32x16_t s, dp;
+};
+
+// The weights P and dS of one block rounded to bf16, as B operands of the
+// dV and dK products: half h covers queries 16*h .. 16*h + 15 of the block.
+struct PdsBlock {
+  u32x4_t pf[2], df[2];
+};
+
+// Walks 32-query blocks u = 0, 1, ... over the (query head of the GQA group,
+// 64-query tile) sequence, two blocks per tile.  Step u is a software
+// pipeline of three blocks: the S and dP products of block u+2, the
+// softmax-gradient VALU work of block u+1 and the dV, dK products of block u
+// share one slot schedule (one MFMA per slot, S/dP and dV/dK alternating,
+// the VALU work spread over the slots), so the VALU work of one block runs
+// under the MFMAs of the others.  Tiles sit in three LDS stages: at the top
+// of tile tau (blocks 2tau, 2tau+1) tiles tau and tau+1 have landed, and the
+// copy of tile tau+2 goes into the stage of tile tau-1, which every wave has
+// finished reading.
 template <int D>
 __global__ void __launch_bounds__(64 * kKvWaves)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_bwd_dkdv_kernel(BwdParams p) {
   using C = BCfg<D, kKvWaves>;
+  constexpr int NSD = 2 * C::KC;      // S and dP MFMAs per block
+  constexpr int NKV = 4 * C::MD;      // dV and dK MFMAs per block
+  static_assert(NSD == NKV, "one S/dP MFMA per dV/dK MFMA");
+  constexpr int kSlots = NSD + NKV;
+  constexpr int kLead = 4;            // fragments are read this many slots ahead
+  constexpr int kItems = 24;          // softmax-gradient work items per block (6 per 4 queries)
+  constexpr uint32_t kStage = 2 * C::TILE;                 // Q tile, then dO tile
+  constexpr uint32_t kStats = kKvStages * kStage;          // per stage: lse (256 B), D (256 B)
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const uint32_t lds0 = (uint32_t)(size_t)(SQKV_LDS unsigned char*)smem;
-  // Q and dO tiles, two stages each, then the tiles' lse and D (64 floats
-  // each, two stages)
-  const uint32_t Q_LDS = lds0, O_LDS = lds0 + 2 * C::TILE, L_LDS = lds0 + 4 * C::TILE, D_LDS = L_LDS + 2 * 256;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -361,7 +407,17 @@ attn_bwd_dkdv_kernel(BwdParams p) {
   const int key = kw0 + l32;
   const bool key_ok = key < p.n_k;
 
-  // K and V rows of the lane's key (B operands of S and dP)
+  // the first query that can see the workgroup's first key
+  int qstart = 0;
+  if (p.causal) qstart = (int)min((int64_t)p.n_q, max((int64_t)0, p.k_pos0 + k0 - p.q_pos0));
+  const int t0 = qstart / kTR;
+  const int T = (p.n_q + kTR - 1) / kTR;
+  const int Tq = T - t0;                      // tiles per query head
+  const int NT = p.group * Tq;                // tiles of the whole walk
+  if (NT <= 0) return;                        // no query sees these keys: nothing to add
+
+  // K and V rows of the lane's key (B operands of S and dP); a key past the
+  // chunk end reads zeros and only ever touches its own (unstored) column
   const uint16_t* krow = static_cast<const uint16_t*>(p.k) + b * p.k_sb + hk * p.k_sh + (int64_t)(key_ok ? key : 0) * p.k_sn;
   const uint16_t* vrow = static_cast<const uint16_t*>(p.v) + b * p.v_sb + hk * p.v_sh + (int64_t)(key_ok ? key : 0) * p.v_sn;
   u32x4_t kf[C::KC], vf[C::KC];
@@ -371,13 +427,8 @@ attn_bwd_dkdv_kernel(BwdParams p) {
     vf[kc] = load_row8(vrow, key_ok, 16 * kc + 8 * hi);
   }
   const int64_t kpos = p.k_pos0 + key;
+  const int64_t kpos_wave_last = p.k_pos0 + kw0 + 31;
   const float c = p.scale_log2;
-
-  // the first query that can see the workgroup's first key
-  int qstart = 0;
-  if (p.causal) qstart = (int)min((int64_t)p.n_q, max((int64_t)0, p.k_pos0 + k0 - p.q_pos0));
-  const int t0 = qstart / kTR;
-  const int T = (p.n_q + kTR - 1) / kTR;
 
   const int q_snb = (int)(p.q_sn * 2), o_snb = (int)(p.do_sn * 2);
   TileDma<D, kKvWaves> q_dma, o_dma;
@@ -400,95 +451,223 @@ attn_bwd_dkdv_kernel(BwdParams p) {
     dva[md] = (f32x16_t){};
   }
 
-  for (int gi = 0; gi < p.group; ++gi) {
+  // Q, dO rows [t*64, t*64 + 64) of query head hk*group + gi, and their lse
+  // and D (wave 0: one 64-lane dword load each), into LDS stage `stage`;
+  // rows past the chunk end arrive as zeros.
+  auto issue_tile = [&](int gi, int t, int stage) {
     const int h = hk * p.group + gi;
     const unsigned char* qg = reinterpret_cast<const unsigned char*>(
         static_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh);
     const unsigned char* og = reinterpret_cast<const unsigned char*>(
         static_cast<const uint16_t*>(p.dout) + b * p.do_sb + h * p.do_sh);
-    const float* lse_h = p.lse + ((int64_t)b * p.Hq + h) * p.n_q;
-    const float* D_h = p.D + ((int64_t)b * p.Hq + h) * p.n_q;
-    // the row statistics of query tile tq into stage `sl` (wave 0 only: one
-    // 64-lane dword load each)
-    auto issue_stats = [&](int tq, uint32_t sl) {
-      if (wave == 0) {
-        const int nv = __builtin_amdgcn_readfirstlane(min(max(p.n_q - tq * kTR, 0), kTR));
-        dma4((uint32_t)(lane * 4), buffer_rsrc(lse_h + tq * kTR, (uint32_t)nv * 4u), L_LDS + sl);
-        dma4((uint32_t)(lane * 4), buffer_rsrc(D_h + tq * kTR, (uint32_t)nv * 4u), D_LDS + sl);
-      }
-    };
-    if (t0 < T) {
-      drain_and_sync();                     // the previous head's tiles are no longer read
-      q_dma.issue(qg, q_snb, t0 * kTR, p.n_q, Q_LDS);
-      o_dma.issue(og, o_snb, t0 * kTR, p.n_q, O_LDS);
-      issue_stats(t0, 0);
+    const uint32_t base = lds0 + (uint32_t)stage * kStage;
+    q_dma.issue(qg, q_snb, t * kTR, p.n_q, base);
+    o_dma.issue(og, o_snb, t * kTR, p.n_q, base + C::TILE);
+    if (wave == 0) {
+      const int nv = __builtin_amdgcn_readfirstlane(min(max(p.n_q - t * kTR, 0), kTR));
+      const int64_t row = ((int64_t)b * p.Hq + h) * p.n_q + (int64_t)t * kTR;
+      const uint32_t sl = lds0 + kStats + (uint32_t)stage * 512u;
+      dma4((uint32_t)(lane * 4), buffer_rsrc(p.lse + row, (uint32_t)nv * 4u), sl);
+      dma4((uint32_t)(lane * 4), buffer_rsrc(p.D + row, (uint32_t)nv * 4u), sl + 256u);
     }
-    for (int t = t0; t < T; ++t) {
-      const uint32_t st = (uint32_t)((t - t0) & 1) * C::TILE;
-      drain_and_sync();
-      if (t + 1 < T) {
-        q_dma.issue(qg, q_snb, (t + 1) * kTR, p.n_q, Q_LDS + (C::TILE - st));
-        o_dma.issue(og, o_snb, (t + 1) * kTR, p.n_q, O_LDS + (C::TILE - st));
-        issue_stats(t + 1, st == 0 ? 256u : 0u);
-      }
+  };
+
+  // ---- one block's pieces -------------------------------------------------
+  // S/dP MFMA m (kc = m/2; even: S from the Q tile, odd: dP from the dO
+  // tile) reads a row fragment at ra[kc] + qb*32 rows.
+  auto sd_read = [&](auto M, const uint32_t (&ra)[C::KC], auto QB) -> u32x4_t {
+    constexpr int m = decltype(M)::value, qb = decltype(QB)::value;
+    return lds_b128(ra[m / 2] + (uint32_t)(qb * 32 * C::ROWB + (m & 1) * C::TILE));
+  };
+  auto sd_mfma = [&](auto M, SdBlock& o, const u32x4_t& fr) {
+    constexpr int m = decltype(M)::value, kc = m / 2;
+    if constexpr ((m & 1) == 0)
+      o.s = mfma(as_bf16x8(fr), as_bf16x8(kf[kc]), kc == 0 ? (f32x16_t){} : o.s);
+    else
+      o.dp = mfma(as_bf16x8(fr), as_bf16x8(vf[kc]), kc == 0 ? (f32x16_t){} : o.dp);
+  };
+  // dV/dK MFMA m: half = m / (2 MD), md = (m / 2) % MD; even: dV^T += dO^T P
+  // (transposed dO fragment), odd: dK^T += Q^T dS (transposed Q fragment).
+  auto kv_read = [&](auto M, const uint32_t (&ta)[C::MD][2], auto QB) -> bf16x8_t {
+    constexpr int m = decltype(M)::value, qb = decltype(QB)::value;
+    constexpr int half = m / (2 * C::MD), md = (m / 2) % C::MD;
+    constexpr uint32_t o = (uint32_t)((32 * qb + 16 * half) * C::ROWB + ((m & 1) ? 0 : C::TILE));
+    return tr_frag(ta[md][0] + o, ta[md][1] + o);
+  };
+  auto kv_mfma = [&](auto M, const PdsBlock& w, const bf16x8_t& fr) {
+    constexpr int m = decltype(M)::value;
+    constexpr int half = m / (2 * C::MD), md = (m / 2) % C::MD;
+    if constexpr ((m & 1) == 0) dva[md] = mfma(fr, as_bf16x8(w.pf[half]), dva[md]);
+    else dka[md] = mfma(fr, as_bf16x8(w.df[half]), dka[md]);
+  };
+
+  // Softmax-gradient work of a block: P = exp2(c*s - lse*log2e) and
+  // dS = P (dP - D), masked causally, rounded to bf16.  Item k of the 24:
+  // for each 4-query group g = k / 6: the group's statistics, its four
+  // elements, then the mask and the bf16 packs.
+  struct SmState {
+    u32x4_t lr[4], dr[4];
+    float nl[4], d4[4];
+    float pw[16], dsw[16];
+    int lo;
+    bool msk;
+  };
+  auto sm_stats = [&](SmState& st, uint32_t sa, auto QB) {
+    constexpr int qb = decltype(QB)::value;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        // S and dP for 32 queries: element j holds query
-        // t*64 + 32*qb + 8*(j/4) + 4*hi + j%4 of key `key`
-        f32x16_t s = {}, dp = {};
-#pragma unroll
-        for (int kc = 0; kc < C::KC; ++kc) {
-          const uint32_t o = rofs[kc] + st + qb * 32 * C::ROWB;
-          s = mfma(as_bf16x8(lds_b128(Q_LDS + o)), as_bf16x8(kf[kc]), s);
-          dp = mfma(as_bf16x8(lds_b128(O_LDS + o)), as_bf16x8(vf[kc]), dp);
-        }
-        const int qb0 = t * kTR + 32 * qb;
-        float pw[16], dsw[16];
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int qi = qb0 + 8 * g4 + 4 * hi;    // first of 4 consecutive queries
-          const uint32_t so = (st == 0 ? 0u : 256u) + (uint32_t)(32 * qb + 8 * g4 + 4 * hi) * 4u;
-          const u32x4_t lr = lds_b128(L_LDS + so), dr = lds_b128(D_LDS + so);
-          float l4[4], d4[4];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const bool ok = qi + x < p.n_q;
-            l4[x] = ok ? __uint_as_float(lr[x]) : kNegInf;
-            d4[x] = ok ? __uint_as_float(dr[x]) : 0.f;
-          }
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const int j = 4 * g4 + x;
-            const int64_t qp = p.q_pos0 + qi + x;
-            const bool vis = key_ok && l4[x] != kNegInf && (!p.causal || kpos <= qp);
-            const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(s[j], c, -l4[x] * kLog2e)) : 0.f;
-            pw[j] = pr;
-            dsw[j] = pr * (dp[j] - d4[x]);
-          }
-        }
-        u32x4_t pf[2], df[2];
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            pf[half][x] = pack_bf16x2(pw[8 * half + 2 * x], pw[8 * half + 2 * x + 1]);
-            df[half][x] = pack_bf16x2(dsw[8 * half + 2 * x], dsw[8 * half + 2 * x + 1]);
-          }
-        // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int md = 0; md < C::MD; ++md) {
-            const uint32_t o = st + (32 * qb + 16 * half) * C::ROWB;
-            dva[md] = mfma(tr_frag(O_LDS + o + tofs[md][0], O_LDS + o + tofs[md][1]), as_bf16x8(pf[half]), dva[md]);
-            dka[md] = mfma(tr_frag(Q_LDS + o + tofs[md][0], Q_LDS + o + tofs[md][1]), as_bf16x8(df[half]), dka[md]);
-          }
-      }
+    for (int g = 0; g < 4; ++g) {
+      st.lr[g] = lds_b128(sa + (uint32_t)((32 * qb + 8 * g) * 4));
+      st.dr[g] = lds_b128(sa + 256u + (uint32_t)((32 * qb + 8 * g) * 4));
     }
+  };
+  auto sm_setup = [&](SmState& st, int t, auto QB) {
+    constexpr int qb = decltype(QB)::value;
+    const int qb0 = t * kTR + 32 * qb;
+    const int64_t q0pos = p.q_pos0 + qb0;
+    st.msk = p.causal && kpos_wave_last > q0pos;
+    const int64_t lo = kpos - q0pos - 4 * hi;
+    st.lo = (int)min(max(lo, (int64_t)-1), (int64_t)33);
+  };
+  auto sm_item = [&](auto K, SmState& st, const SdBlock& sd, PdsBlock& w) {
+    constexpr int k = decltype(K)::value, g = k / 6, r = k % 6;
+    if constexpr (r == 0) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        // lse = -inf only for a row that sees no key anywhere, so none of
+        // this pair: the causal mask below (a select) zeroes its elements
+        st.nl[x] = -__uint_as_float(st.lr[g][x]) * kLog2e;
+        st.d4[x] = __uint_as_float(st.dr[g][x]);
+      }
+    } else if constexpr (r <= 4) {
+      constexpr int x = r - 1, j = 4 * g + x;
+      const float pr = __builtin_amdgcn_exp2f(fmaf(sd.s[j], c, st.nl[x]));
+      st.pw[j] = pr;
+      st.dsw[j] = pr * (sd.dp[j] - st.d4[x]);
+    } else {
+      if (st.msk) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const bool vis = 8 * g + x >= st.lo;
+          st.pw[4 * g + x] = vis ? st.pw[4 * g + x] : 0.f;
+          st.dsw[4 * g + x] = vis ? st.dsw[4 * g + x] : 0.f;
+        }
+      }
+      constexpr int half = g / 2, xx = 2 * (g & 1);
+      w.pf[half][xx] = pack_bf16x2(st.pw[4 * g], st.pw[4 * g + 1]);
+      w.pf[half][xx + 1] = pack_bf16x2(st.pw[4 * g + 2], st.pw[4 * g + 3]);
+      w.df[half][xx] = pack_bf16x2(st.dsw[4 * g], st.dsw[4 * g + 1]);
+      w.df[half][xx + 1] = pack_bf16x2(st.dsw[4 * g + 2], st.dsw[4 * g + 3]);
+    }
+  };
+  constexpr auto kSlotOfItem = [](int k) { return 1 + (k * (kSlots - 2)) / kItems; };
+
+  // Per-tile addresses: row fragments of tile tau+1, transposed fragments of
+  // tile tau, statistics of tiles tau and tau+1.
+  uint32_t ra[C::KC], ta[C::MD][2], sa_cur, sa_nxt;
+  auto set_addr = [&](int s_cur, int s_nxt) {
+    const uint32_t bc = lds0 + (uint32_t)s_cur * kStage, bn = lds0 + (uint32_t)s_nxt * kStage;
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc) {
+      ra[kc] = rofs[kc] + bn;
+      pin(ra[kc]);
+    }
+#pragma unroll
+    for (int md = 0; md < C::MD; ++md) {
+      ta[md][0] = tofs[md][0] + bc;
+      ta[md][1] = tofs[md][1] + bc;
+      pin(ta[md][0]);
+      pin(ta[md][1]);
+    }
+    sa_cur = lds0 + kStats + (uint32_t)s_cur * 512u + (uint32_t)(16 * hi);
+    sa_nxt = lds0 + kStats + (uint32_t)s_nxt * 512u + (uint32_t)(16 * hi);
+    pin(sa_cur);
+    pin(sa_nxt);
+  };
+
+  // One pipeline step: dV/dK of the block in `kvw` (tile tau, half QB of
+  // the tile), the softmax gradient of `smi` into `smo` (tile of sa_sm,
+  // query tile t_sm, half 1 - QB) and S/dP of the block after it into `sdo`
+  // (tile tau+1, half QB).
+  auto step = [&](auto QB, const PdsBlock& kvw, const SdBlock& smi, PdsBlock& smo, SdBlock& sdo,
+                  uint32_t sa_sm, int t_sm) {
+    constexpr int qb = decltype(QB)::value;
+    using SQB = Step<1 - qb>;
+    SmState st;
+    sm_stats(st, sa_sm, SQB{});
+    sm_setup(st, t_sm, SQB{});
+    bf16x8_t kvfr[NKV];
+    u32x4_t sdfr[NSD];
+    static_for<kLead>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if constexpr ((i & 1) == 0) kvfr[i / 2] = kv_read(Step<i / 2>{}, ta, QB);
+      else sdfr[i / 2] = sd_read(Step<i / 2>{}, ra, QB);
+    });
+    static_for<kSlots>([&](auto I) {
+      constexpr int i = decltype(I)::value, ia = i + kLead;
+      if constexpr (ia < kSlots) {
+        if constexpr ((ia & 1) == 0) kvfr[ia / 2] = kv_read(Step<ia / 2>{}, ta, QB);
+        else sdfr[ia / 2] = sd_read(Step<ia / 2>{}, ra, QB);
+      }
+      if constexpr ((i & 1) == 0) kv_mfma(Step<i / 2>{}, kvw, kvfr[i / 2]);
+      else sd_mfma(Step<i / 2>{}, sdo, sdfr[i / 2]);
+      static_for<kItems>([&](auto K) {
+        if constexpr (kSlotOfItem(decltype(K)::value) == i) sm_item(K, st, smi, smo);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // ---- prologue: tiles 0 and 1 in flight, S/dP of blocks 0 and 1, P/dS of block 0
+  int gi_d = 0, t_d = t0;                     // next tile to copy
+  auto advance = [&](int& gi, int& t) {
+    if (++t == T) {
+      t = t0;
+      ++gi;
+    }
+  };
+  issue_tile(gi_d, t_d, 0);
+  advance(gi_d, t_d);
+  if (NT > 1) {
+    issue_tile(gi_d, t_d, 1);
+    advance(gi_d, t_d);
+  }
+  drain_and_sync();
+
+  SdBlock sA, sB;
+  PdsBlock wA, wB;
+  set_addr(kKvStages - 1, 0);                 // row fragments and statistics of tile 0
+  {
+    static_for<NSD>([&](auto M) { sd_mfma(M, sA, sd_read(M, ra, Step<0>{})); });
+    static_for<NSD>([&](auto M) { sd_mfma(M, sB, sd_read(M, ra, Step<1>{})); });
+    SmState st;
+    sm_stats(st, sa_nxt, Step<0>{});
+    sm_setup(st, t0, Step<0>{});
+    static_for<kItems>([&](auto K) { sm_item(K, st, sA, wA); });
+  }
+
+  int s_cur = 0;                              // stage of tile tau
+  int t_cur = t0, gi_cur = 0;                 // query tile of tau
+  for (int tau = 0; tau < NT; ++tau) {
+    if (tau > 0) drain_and_sync();            // tile tau+1 landed; tile tau-1 no longer read
+    const int s_nxt = s_cur == kKvStages - 1 ? 0 : s_cur + 1;
+    if (tau + 2 < NT) {
+      const int s_dma = s_nxt == kKvStages - 1 ? 0 : s_nxt + 1;
+      issue_tile(gi_d, t_d, s_dma);
+      advance(gi_d, t_d);
+    }
+    int gi_n = gi_cur, t_nxt = t_cur;
+    advance(gi_n, t_nxt);
+    set_addr(s_cur, s_nxt);
+    step(Step<0>{}, wA, sB, wB, sA, sa_cur, t_cur);   // dV/dK(2tau), P/dS(2tau+1), S/dP(2tau+2)
+    step(Step<1>{}, wB, sA, wA, sB, sa_nxt, t_nxt);   // dV/dK(2tau+1), P/dS(2tau+2), S/dP(2tau+3)
+    s_cur = s_nxt;
+    t_cur = t_nxt;
+    gi_cur = gi_n;
   }
   __builtin_amdgcn_s_waitcnt(0);   // no DMA may outlive the workgroup's LDS
 
   if (key_ok) {
+
     float* dkr = p.dk + b * p.dk_sb + hk * p.dk_sh + (int64_t)key * p.dk_sn;
     float* dvr = p.dv + b * p.dv_sb + hk * p.dv_sh + (int64_t)key * p.dv_sn;
 #pragma unroll
@@ -544,6 +723,11 @@ __global__ void __launch_bounds__(256) bwd_rowdot_kernel(RowDotParams p) {
   if (r < rows && sub == 0) p.D[r] = acc;
 }
 
+// LDS of the dK/dV kernel: three stages of (Q tile, dO tile) and of the
+// tiles' lse and D.
+template <int D>
+constexpr int kKvLds = kKvStages * (2 * BCfg<D, kKvWaves>::TILE + 512);
+
 template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t s) {
   using Cq = BCfg<D, kDqWaves>;
@@ -554,7 +738,7 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t s) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 4 * Cq::TILE);
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 4 * Ck::TILE + 1024);
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kKvLds<D>);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -565,7 +749,7 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t s) {
   const int n_ktiles = (p.n_k + kKvRows - 1) / kKvRows;
   const int64_t bk = (int64_t)n_ktiles * p.B * p.Hkv;
   if (bk > 0)
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)bk), dim3(64 * kKvWaves), 4 * Ck::TILE + 1024, s, p);
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)bk), dim3(64 * kKvWaves), kKvLds<D>, s, p);
   return hipGetLastError();
 }
 
