@@ -426,6 +426,10 @@ attn_bwd_dkdv_kernel(BwdParams p) {
     kf[kc] = load_row8(krow, key_ok, 16 * kc + 8 * hi);
     vf[kc] = load_row8(vrow, key_ok, 16 * kc + 8 * hi);
   }
+  // -V: the dP product of a block starts from the rows' D and ends at
+  // D - dO V^T = -(dP - D)
+#pragma unroll
+  for (int kc = 0; kc < C::KC; ++kc) vf[kc] ^= (u32x4_t){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
   const int64_t kpos = p.k_pos0 + key;
   const int64_t kpos_wave_last = p.k_pos0 + kw0 + 31;
   const float c = p.scale_log2;
@@ -434,15 +438,6 @@ attn_bwd_dkdv_kernel(BwdParams p) {
   TileDma<D, kKvWaves> q_dma, o_dma;
   q_dma.init(lane, wave, q_snb);
   o_dma.init(lane, wave, o_snb);
-
-  uint32_t rofs[C::KC], tofs[C::MD][2];
-#pragma unroll
-  for (int kc = 0; kc < C::KC; ++kc) rofs[kc] = row_ofs<D>(l32, kc, hi);
-#pragma unroll
-  for (int md = 0; md < C::MD; ++md) {
-    tofs[md][0] = tr_ofs<D>(lane, md, 0);
-    tofs[md][1] = tr_ofs<D>(lane, md, 1);
-  }
 
   f32x16_t dka[C::MD], dva[C::MD];
 #pragma unroll
@@ -473,18 +468,33 @@ attn_bwd_dkdv_kernel(BwdParams p) {
   };
 
   // ---- one block's pieces -------------------------------------------------
-  // S/dP MFMA m (kc = m/2; even: S from the Q tile, odd: dP from the dO
-  // tile) reads a row fragment at ra[kc] + qb*32 rows.
+  // S/dP MFMA m: m < KC, S from the Q tile (kc = m); m >= KC, D - dP from the
+  // dO tile (kc = m - KC), starting from the block's D values `dinit`.  Each
+  // reads a row fragment at ra[kc] + qb*32 rows.
   auto sd_read = [&](auto M, const uint32_t (&ra)[C::KC], auto QB) -> u32x4_t {
     constexpr int m = decltype(M)::value, qb = decltype(QB)::value;
-    return lds_b128(ra[m / 2] + (uint32_t)(qb * 32 * C::ROWB + (m & 1) * C::TILE));
+    constexpr int kc = m % C::KC;
+    return lds_b128(ra[kc] + (uint32_t)(qb * 32 * C::ROWB + (m / C::KC) * C::TILE));
   };
-  auto sd_mfma = [&](auto M, SdBlock& o, const u32x4_t& fr) {
-    constexpr int m = decltype(M)::value, kc = m / 2;
-    if constexpr ((m & 1) == 0)
+  auto sd_mfma = [&](auto M, SdBlock& o, const u32x4_t& fr, const f32x16_t& dinit) {
+    constexpr int m = decltype(M)::value, kc = m % C::KC;
+    if constexpr (m < C::KC)
       o.s = mfma(as_bf16x8(fr), as_bf16x8(kf[kc]), kc == 0 ? (f32x16_t){} : o.s);
     else
-      o.dp = mfma(as_bf16x8(fr), as_bf16x8(vf[kc]), kc == 0 ? (f32x16_t){} : o.dp);
+      o.dp = mfma(as_bf16x8(fr), as_bf16x8(vf[kc]), kc == 0 ? dinit : o.dp);
+  };
+  // D of the 32 queries of half QB of a tile (stats at `sa`), laid out as
+  // the dP accumulator: element j holds query 8*(j/4) + 4*hi + j%4.
+  auto d_init = [&](uint32_t sa, auto QB) -> f32x16_t {
+    constexpr int qb = decltype(QB)::value;
+    f32x16_t r;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const u32x4_t v = lds_b128(sa + 256u + (uint32_t)((32 * qb + 8 * g) * 4));
+#pragma unroll
+      for (int x = 0; x < 4; ++x) r[4 * g + x] = __uint_as_float(v[x]);
+    }
+    return r;
   };
   // dV/dK MFMA m: half = m / (2 MD), md = (m / 2) % MD; even: dV^T += dO^T P
   // (transposed dO fragment), odd: dK^T += Q^T dS (transposed Q fragment).
@@ -502,23 +512,20 @@ attn_bwd_dkdv_kernel(BwdParams p) {
   };
 
   // Softmax-gradient work of a block: P = exp2(c*s - lse*log2e) and
-  // dS = P (dP - D), masked causally, rounded to bf16.  Item k of the 24:
-  // for each 4-query group g = k / 6: the group's statistics, its four
-  // elements, then the mask and the bf16 packs.
+  // dS = P (dP - D) = -P (D - dP), masked causally, rounded to bf16.  Item k
+  // of the 24: for each 4-query group g = k / 6: the group's lse, its four
+  // elements, then the mask and the bf16 packs.  The group's lse is read
+  // from LDS a few slots before its first item.
   struct SmState {
-    u32x4_t lr[4], dr[4];
-    float nl[4], d4[4];
+    u32x4_t lr[4];
+    float nl[4];
     float pw[16], dsw[16];
     int lo;
     bool msk;
   };
-  auto sm_stats = [&](SmState& st, uint32_t sa, auto QB) {
-    constexpr int qb = decltype(QB)::value;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      st.lr[g] = lds_b128(sa + (uint32_t)((32 * qb + 8 * g) * 4));
-      st.dr[g] = lds_b128(sa + 256u + (uint32_t)((32 * qb + 8 * g) * 4));
-    }
+  auto sm_read = [&](SmState& st, uint32_t sa, auto QB, auto G) {
+    constexpr int qb = decltype(QB)::value, g = decltype(G)::value;
+    st.lr[g] = lds_b128(sa + (uint32_t)((32 * qb + 8 * g) * 4));
   };
   auto sm_setup = [&](SmState& st, int t, auto QB) {
     constexpr int qb = decltype(QB)::value;
@@ -531,18 +538,15 @@ attn_bwd_dkdv_kernel(BwdParams p) {
   auto sm_item = [&](auto K, SmState& st, const SdBlock& sd, PdsBlock& w) {
     constexpr int k = decltype(K)::value, g = k / 6, r = k % 6;
     if constexpr (r == 0) {
+      // lse = -inf only for a row that sees no key anywhere, so none of
+      // this pair: the causal mask below (a select) zeroes its elements
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        // lse = -inf only for a row that sees no key anywhere, so none of
-        // this pair: the causal mask below (a select) zeroes its elements
-        st.nl[x] = -__uint_as_float(st.lr[g][x]) * kLog2e;
-        st.d4[x] = __uint_as_float(st.dr[g][x]);
-      }
+      for (int x = 0; x < 4; ++x) st.nl[x] = -__uint_as_float(st.lr[g][x]) * kLog2e;
     } else if constexpr (r <= 4) {
       constexpr int x = r - 1, j = 4 * g + x;
       const float pr = __builtin_amdgcn_exp2f(fmaf(sd.s[j], c, st.nl[x]));
       st.pw[j] = pr;
-      st.dsw[j] = pr * (sd.dp[j] - st.d4[x]);
+      st.dsw[j] = -(pr * sd.dp[j]);
     } else {
       if (st.msk) {
 #pragma unroll
@@ -557,43 +561,51 @@ attn_bwd_dkdv_kernel(BwdParams p) {
       w.pf[half][xx + 1] = pack_bf16x2(st.pw[4 * g + 2], st.pw[4 * g + 3]);
       w.df[half][xx] = pack_bf16x2(st.dsw[4 * g], st.dsw[4 * g + 1]);
       w.df[half][xx + 1] = pack_bf16x2(st.dsw[4 * g + 2], st.dsw[4 * g + 3]);
+      pin(w.pf[half]);
+      pin(w.df[half]);
     }
   };
   constexpr auto kSlotOfItem = [](int k) { return 1 + (k * (kSlots - 2)) / kItems; };
 
-  // Per-tile addresses: row fragments of tile tau+1, transposed fragments of
-  // tile tau, statistics of tiles tau and tau+1.
+  // Per-tile addresses: row fragments of tile tau+1 (ra), transposed
+  // fragments of tile tau (ta), statistics of tiles tau and tau+1.  Moving
+  // to the next tile adds the distance between the stages' bases.
   uint32_t ra[C::KC], ta[C::MD][2], sa_cur, sa_nxt;
-  auto set_addr = [&](int s_cur, int s_nxt) {
-    const uint32_t bc = lds0 + (uint32_t)s_cur * kStage, bn = lds0 + (uint32_t)s_nxt * kStage;
+#pragma unroll
+  for (int kc = 0; kc < C::KC; ++kc) ra[kc] = lds0 + row_ofs<D>(l32, kc, hi);                       // stage 0
+#pragma unroll
+  for (int md = 0; md < C::MD; ++md) {
+    ta[md][0] = lds0 + (uint32_t)(kKvStages - 1) * kStage + tr_ofs<D>(lane, md, 0);   // stage S-1
+    ta[md][1] = lds0 + (uint32_t)(kKvStages - 1) * kStage + tr_ofs<D>(lane, md, 1);
+  }
+  auto move_addr = [&](int s_cur, int s_nxt, uint32_t d_cur, uint32_t d_nxt) {
 #pragma unroll
     for (int kc = 0; kc < C::KC; ++kc) {
-      ra[kc] = rofs[kc] + bn;
+      ra[kc] += d_nxt;
       pin(ra[kc]);
     }
 #pragma unroll
     for (int md = 0; md < C::MD; ++md) {
-      ta[md][0] = tofs[md][0] + bc;
-      ta[md][1] = tofs[md][1] + bc;
+      ta[md][0] += d_cur;
+      ta[md][1] += d_cur;
       pin(ta[md][0]);
       pin(ta[md][1]);
     }
     sa_cur = lds0 + kStats + (uint32_t)s_cur * 512u + (uint32_t)(16 * hi);
     sa_nxt = lds0 + kStats + (uint32_t)s_nxt * 512u + (uint32_t)(16 * hi);
-    pin(sa_cur);
-    pin(sa_nxt);
   };
 
   // One pipeline step: dV/dK of the block in `kvw` (tile tau, half QB of
-  // the tile), the softmax gradient of `smi` into `smo` (tile of sa_sm,
-  // query tile t_sm, half 1 - QB) and S/dP of the block after it into `sdo`
-  // (tile tau+1, half QB).
+  // the tile), the softmax gradient of `smi` into `smo` (statistics at
+  // sa_sm, query tile t_sm, half 1 - QB) and S/dP of the block after it into
+  // `sdo` (tile tau+1, half QB, statistics at sa_sd).
   auto step = [&](auto QB, const PdsBlock& kvw, const SdBlock& smi, PdsBlock& smo, SdBlock& sdo,
-                  uint32_t sa_sm, int t_sm) {
+                  uint32_t sa_sm, int t_sm, uint32_t sa_sd) {
     constexpr int qb = decltype(QB)::value;
     using SQB = Step<1 - qb>;
     SmState st;
-    sm_stats(st, sa_sm, SQB{});
+    sm_read(st, sa_sm, SQB{}, Step<0>{});
+    const f32x16_t dinit = d_init(sa_sd, QB);
     sm_setup(st, t_sm, SQB{});
     bf16x8_t kvfr[NKV];
     u32x4_t sdfr[NSD];
@@ -608,8 +620,12 @@ attn_bwd_dkdv_kernel(BwdParams p) {
         if constexpr ((ia & 1) == 0) kvfr[ia / 2] = kv_read(Step<ia / 2>{}, ta, QB);
         else sdfr[ia / 2] = sd_read(Step<ia / 2>{}, ra, QB);
       }
+      static_for<3>([&](auto G) {
+        constexpr int g = decltype(G)::value + 1;
+        if constexpr (kSlotOfItem(6 * g) - 3 == i) sm_read(st, sa_sm, SQB{}, Step<g>{});
+      });
       if constexpr ((i & 1) == 0) kv_mfma(Step<i / 2>{}, kvw, kvfr[i / 2]);
-      else sd_mfma(Step<i / 2>{}, sdo, sdfr[i / 2]);
+      else sd_mfma(Step<i / 2>{}, sdo, sdfr[i / 2], dinit);
       static_for<kItems>([&](auto K) {
         if constexpr (kSlotOfItem(decltype(K)::value) == i) sm_item(K, st, smi, smo);
       });
@@ -635,12 +651,13 @@ attn_bwd_dkdv_kernel(BwdParams p) {
 
   SdBlock sA, sB;
   PdsBlock wA, wB;
-  set_addr(kKvStages - 1, 0);                 // row fragments and statistics of tile 0
+  sa_nxt = lds0 + kStats + (uint32_t)(16 * hi);   // statistics of tile 0 (stage 0)
   {
-    static_for<NSD>([&](auto M) { sd_mfma(M, sA, sd_read(M, ra, Step<0>{})); });
-    static_for<NSD>([&](auto M) { sd_mfma(M, sB, sd_read(M, ra, Step<1>{})); });
+    const f32x16_t d0 = d_init(sa_nxt, Step<0>{}), d1 = d_init(sa_nxt, Step<1>{});
+    static_for<NSD>([&](auto M) { sd_mfma(M, sA, sd_read(M, ra, Step<0>{}), d0); });
+    static_for<NSD>([&](auto M) { sd_mfma(M, sB, sd_read(M, ra, Step<1>{}), d1); });
     SmState st;
-    sm_stats(st, sa_nxt, Step<0>{});
+    static_for<4>([&](auto G) { sm_read(st, sa_nxt, Step<0>{}, G); });
     sm_setup(st, t0, Step<0>{});
     static_for<kItems>([&](auto K) { sm_item(K, st, sA, wA); });
   }
@@ -651,15 +668,17 @@ attn_bwd_dkdv_kernel(BwdParams p) {
     if (tau > 0) drain_and_sync();            // tile tau+1 landed; tile tau-1 no longer read
     const int s_nxt = s_cur == kKvStages - 1 ? 0 : s_cur + 1;
     if (tau + 2 < NT) {
-      const int s_dma = s_nxt == kKvStages - 1 ? 0 : s_nxt + 1;
+      const int s_dma = s_nxt == kKvStages - 1 ? 0 : s_nxt + 1;   // the stage of tile tau-1
       issue_tile(gi_d, t_d, s_dma);
       advance(gi_d, t_d);
     }
     int gi_n = gi_cur, t_nxt = t_cur;
     advance(gi_n, t_nxt);
-    set_addr(s_cur, s_nxt);
-    step(Step<0>{}, wA, sB, wB, sA, sa_cur, t_cur);   // dV/dK(2tau), P/dS(2tau+1), S/dP(2tau+2)
-    step(Step<1>{}, wB, sA, wA, sB, sa_nxt, t_nxt);   // dV/dK(2tau+1), P/dS(2tau+2), S/dP(2tau+3)
+    // ra moves from tile tau's stage to tile tau+1's, ta from tau-1's to tau's
+    const uint32_t back = (uint32_t)(-(int)((kKvStages - 1) * kStage));
+    move_addr(s_cur, s_nxt, s_cur == 0 ? back : kStage, tau == 0 ? kStage : (s_nxt == 0 ? back : kStage));
+    step(Step<0>{}, wA, sB, wB, sA, sa_cur, t_cur, sa_nxt);   // dV/dK(2tau), P/dS(2tau+1), S/dP(2tau+2)
+    step(Step<1>{}, wB, sA, wA, sB, sa_nxt, t_nxt, sa_nxt);   // dV/dK(2tau+1), P/dS(2tau+2), S/dP(2tau+3)
     s_cur = s_nxt;
     t_cur = t_nxt;
     gi_cur = gi_n;
