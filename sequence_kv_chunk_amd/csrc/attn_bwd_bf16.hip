@@ -182,6 +182,24 @@ __device__ __forceinline__ u32x4_t load_row8(const uint16_t* rowp, bool ok, int 
   return ok ? *reinterpret_cast<const u32x4_t*>(rowp + e0) : z;
 }
 
+template <int R>
+using Step = std::integral_constant<int, R>;
+
+// f(Step<0>{}), ..., f(Step<N-1>{}) as straight-line code.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(Step<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Keeps a value in registers at this point of the program (the compiler may
+// not sink its computation past it or recompute it later).
+template <typename T>
+__device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
+
 // ============================================================================
 // dQ: query rows in registers, K/V tiles streamed
 // ============================================================================
@@ -246,72 +264,146 @@ attn_bwd_dq_kernel(BwdParams p, int n_qtiles) {
   dk_dma.init(lane, wave, k_snb);
   dv_dma.init(lane, wave, v_snb);
 
-  uint32_t kofs[C::KC], tofs[C::MD][2];
+  // Lane addresses of the row fragments (K rows for S^T; the V rows for
+  // dP^T sit two tiles further) and of the transposed K fragments, in the
+  // stage of the current tile; the other stage is one tile away.
+  uint32_t ra[C::KC], ta[C::MD][2];
 #pragma unroll
-  for (int kc = 0; kc < C::KC; ++kc) kofs[kc] = row_ofs<D>(l32, kc, hi);
+  for (int kc = 0; kc < C::KC; ++kc) ra[kc] = K_LDS + row_ofs<D>(l32, kc, hi);
 #pragma unroll
   for (int md = 0; md < C::MD; ++md) {
-    tofs[md][0] = tr_ofs<D>(lane, md, 0);
-    tofs[md][1] = tr_ofs<D>(lane, md, 1);
+    ta[md][0] = K_LDS + tr_ofs<D>(lane, md, 0);
+    ta[md][1] = K_LDS + tr_ofs<D>(lane, md, 1);
   }
+  auto move_addr = [&](uint32_t delta) {
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc) {
+      ra[kc] += delta;
+      pin(ra[kc]);
+    }
+#pragma unroll
+    for (int md = 0; md < C::MD; ++md) {
+      ta[md][0] += delta;
+      ta[md][1] += delta;
+      pin(ta[md][0]);
+      pin(ta[md][1]);
+    }
+  };
 
   f32x16_t acc[C::MD];
 #pragma unroll
   for (int md = 0; md < C::MD; ++md) acc[md] = (f32x16_t){};
+
+  // A tile is two blocks of 32 keys.  Block nb: S^T and dP^T (2 KC MFMAs,
+  // the two chains alternating), then P, dS^T (VALU), then dQ^T += K^T dS^T
+  // (2 MD MFMAs, transposed K fragments of the block's 32 keys).  Element j
+  // of block nb holds key t*64 + 32*nb + 8*(j/4) + 4*hi + j%4 of query `row`.
+  f32x16_t s[2], dp[2];
+  u32x4_t dsf[4];
+  float w[2][16];
+  auto sd_read = [&](auto NB, auto M) -> u32x4_t {
+    constexpr int nb = decltype(NB)::value, m = decltype(M)::value;
+    return lds_b128(ra[m / 2] + (uint32_t)(nb * 32 * C::ROWB + (m & 1) * 2 * C::TILE));
+  };
+  auto sd_mfma = [&](auto NB, auto M, const u32x4_t& fr) {
+    constexpr int nb = decltype(NB)::value, m = decltype(M)::value, kc = m / 2;
+    if constexpr ((m & 1) == 0) s[nb] = mfma(as_bf16x8(fr), as_bf16x8(qf[kc]), kc == 0 ? (f32x16_t){} : s[nb]);
+    else dp[nb] = mfma(as_bf16x8(fr), as_bf16x8(dof[kc]), kc == 0 ? (f32x16_t){} : dp[nb]);
+  };
+  auto dq_read = [&](auto NB, auto M) -> bf16x8_t {
+    constexpr int nb = decltype(NB)::value, m = decltype(M)::value;
+    constexpr int cc = 2 * nb + m / C::MD, md = m % C::MD;
+    return tr_frag(ta[md][0] + (uint32_t)(16 * cc * C::ROWB), ta[md][1] + (uint32_t)(16 * cc * C::ROWB));
+  };
+  auto dq_mfma = [&](auto NB, auto M, const bf16x8_t& fr) {
+    constexpr int nb = decltype(NB)::value, m = decltype(M)::value;
+    constexpr int cc = 2 * nb + m / C::MD, md = m % C::MD;
+    acc[md] = mfma(fr, as_bf16x8(dsf[cc]), acc[md]);
+  };
+  // Item k of block nb's 20 (5 per group g of 4 keys): the group's four
+  // elements, then the mask (only for a block that reaches past a query's
+  // last visible key) and the bf16 packs.
+  bool msk[2];
+  int lk = 0;
+  auto sm_item = [&](auto NB, auto K) {
+    constexpr int nb = decltype(NB)::value, k = decltype(K)::value, g = k / 5, r = k % 5;
+    if constexpr (r < 4) {
+      constexpr int j = 4 * g + r;
+      const float pr = __builtin_amdgcn_exp2f(fmaf(s[nb][j], c, -lse2));
+      w[nb][j] = pr * (dp[nb][j] - Dq);
+    } else {
+      if (msk[nb]) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) w[nb][4 * g + x] = (32 * nb + 8 * g + x <= lk) ? w[nb][4 * g + x] : 0.f;
+      }
+      constexpr int half = g / 2, xx = 2 * (g & 1);
+      dsf[2 * nb + half][xx] = pack_bf16x2(w[nb][4 * g], w[nb][4 * g + 1]);
+      dsf[2 * nb + half][xx + 1] = pack_bf16x2(w[nb][4 * g + 2], w[nb][4 * g + 3]);
+      pin(dsf[2 * nb + half]);
+    }
+  };
+
+  // Slot schedule of one tile (one MFMA per slot):
+  //   A  slots  0..15  S^T, dP^T of block 0
+  //   B  slots 16..31  S^T, dP^T of block 1    + P, dS^T of block 0
+  //   C  slots 32..39  dQ^T of block 0         + P, dS^T of block 1, keys 0..15
+  //   D  slots 40..47  dQ^T of block 1         + P, dS^T of block 1, keys 16..31
+  // (dQ^T of block 1 reads the keys 0..15 packs in its first four slots and
+  // the keys 16..31 packs, made in slots 40..43, in its last four).
+  constexpr int NSD = 2 * C::KC, NDQ = 2 * C::MD;
+  constexpr int kSlots = 2 * NSD + 2 * NDQ;
+  constexpr int kLead = 3;
+  constexpr auto kSlotB = [](int k) { return NSD + (k * NSD) / 20; };
+  constexpr auto kSlotC = [](int k) {
+    return k < 10 ? 2 * NSD + (k * NDQ) / 10 : 2 * NSD + NDQ + ((k - 10) * (NDQ / 2)) / 10;
+  };
+  auto read_frag = [&](auto I, u32x4_t (&sdfr)[2 * NSD], bf16x8_t (&dqfr)[2 * NDQ]) {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i < NSD) sdfr[i] = sd_read(Step<0>{}, Step<i>{});
+    else if constexpr (i < 2 * NSD) sdfr[i] = sd_read(Step<1>{}, Step<i - NSD>{});
+    else if constexpr (i < 2 * NSD + NDQ) dqfr[i - 2 * NSD] = dq_read(Step<0>{}, Step<i - 2 * NSD>{});
+    else dqfr[i - 2 * NSD] = dq_read(Step<1>{}, Step<i - 2 * NSD - NDQ>{});
+  };
 
   if (T > 0) {
     dk_dma.issue(kg, k_snb, 0, n_vis, K_LDS);
     dv_dma.issue(vg, v_snb, 0, n_vis, V_LDS);
   }
   for (int t = 0; t < T; ++t) {
-    const uint32_t st = (uint32_t)(t & 1) * C::TILE;
-    drain_and_sync();                       // tile t landed; stage (t+1)&1 is free
+    drain_and_sync();                       // tile t landed; the other stage is free
     if (t + 1 < T) {
-      dk_dma.issue(kg, k_snb, (t + 1) * kTR, n_vis, K_LDS + (C::TILE - st));
-      dv_dma.issue(vg, v_snb, (t + 1) * kTR, n_vis, V_LDS + (C::TILE - st));
+      const uint32_t other = (uint32_t)((t + 1) & 1) * C::TILE;
+      dk_dma.issue(kg, k_snb, (t + 1) * kTR, n_vis, K_LDS + other);
+      dv_dma.issue(vg, v_snb, (t + 1) * kTR, n_vis, V_LDS + other);
     }
-    // S^T and dP^T for the two 32-key blocks: element j of block nb holds key
-    // t*64 + 32*nb + 8*(j/4) + 4*hi + j%4 of query `row`
-    f32x16_t s[2], dp[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      s[nb] = (f32x16_t){};
-      dp[nb] = (f32x16_t){};
-#pragma unroll
-      for (int kc = 0; kc < C::KC; ++kc) {
-        const uint32_t o = kofs[kc] + st + nb * 32 * C::ROWB;
-        s[nb] = mfma(as_bf16x8(lds_b128(K_LDS + o)), as_bf16x8(qf[kc]), s[nb]);
-        dp[nb] = mfma(as_bf16x8(lds_b128(V_LDS + o)), as_bf16x8(dof[kc]), dp[nb]);
-      }
-    }
-    // weights and dS^T; keys past the visible range or after the query are 0
+    if (t > 0) move_addr((t & 1) ? (uint32_t)C::TILE : (uint32_t)(-(int)C::TILE));
+    // keys past the visible range or after the query get weight 0
     const int kbase = t * kTR;
     int64_t lastk = p.causal ? (qpos - p.k_pos0 - kbase) : (int64_t)kTR;   // last visible key of the tile
     lastk = min(lastk, (int64_t)(n_vis - kbase - 1));
-    const int lk = (int)max((int64_t)-1, min(lastk, (int64_t)kTR)) - 4 * hi;
-    u32x4_t dsf[4];
+    lk = (int)max((int64_t)-1, min(lastk, (int64_t)kTR)) - 4 * hi;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float w[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const bool vis = 32 * nb + 8 * (j >> 2) + (j & 3) <= lk;
-        const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(s[nb][j], c, -lse2)) : 0.f;
-        w[j] = pr * (dp[nb][j] - Dq);
-      }
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int x = 0; x < 4; ++x) dsf[2 * nb + half][x] = pack_bf16x2(w[8 * half + 2 * x], w[8 * half + 2 * x + 1]);
-    }
-    // dQ^T[d][query] += K^T[d][key] dS^T[key][query]
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-      for (int md = 0; md < C::MD; ++md)
-        acc[md] = mfma(tr_frag(K_LDS + st + tofs[md][0] + 16 * cc * C::ROWB,
-                               K_LDS + st + tofs[md][1] + 16 * cc * C::ROWB),
-                       as_bf16x8(dsf[cc]), acc[md]);
+    for (int nb = 0; nb < 2; ++nb)
+      msk[nb] = (kbase + 32 * nb + 32 > n_vis) ||
+                (p.causal && p.k_pos0 + kbase + 32 * nb + 31 > p.q_pos0 + qw0);
+
+    u32x4_t sdfr[2 * NSD];
+    bf16x8_t dqfr[2 * NDQ];
+    static_for<kLead>([&](auto I) { read_frag(I, sdfr, dqfr); });
+    static_for<kSlots>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i + kLead < kSlots) read_frag(Step<i + kLead>{}, sdfr, dqfr);
+      if constexpr (i < NSD) sd_mfma(Step<0>{}, Step<i>{}, sdfr[i]);
+      else if constexpr (i < 2 * NSD) sd_mfma(Step<1>{}, Step<i - NSD>{}, sdfr[i]);
+      else if constexpr (i < 2 * NSD + NDQ) dq_mfma(Step<0>{}, Step<i - 2 * NSD>{}, dqfr[i - 2 * NSD]);
+      else dq_mfma(Step<1>{}, Step<i - 2 * NSD - NDQ>{}, dqfr[i - 2 * NSD]);
+      static_for<20>([&](auto K) {
+        constexpr int k = decltype(K)::value;
+        if constexpr (kSlotB(k) == i) sm_item(Step<0>{}, K);
+        if constexpr (kSlotC(k) == i) sm_item(Step<1>{}, K);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
   }
   __builtin_amdgcn_s_waitcnt(0);   // no DMA may outlive the workgroup's LDS
 
@@ -339,23 +431,6 @@ constexpr int kKvWaves = 4;
 constexpr int kKvRows = 32 * kKvWaves;
 constexpr int kKvStages = 3;   // LDS stages of (Q tile, dO tile, lse, D)
 
-template <int R>
-using Step = std::integral_constant<int, R>;
-
-// f(Step<0>{}), ..., f(Step<N-1>{}) as straight-line code.
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(Step<I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// Keeps a value in registers at this point of the program (the compiler may
-// not sink its computation past it or recompute it later).
-template <typename T>
-__device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
 
 // S and dP of one 32-query block for the wave's 32 keys: element j holds
 // query 8*(j/4) + 4*hi + j%4 of the block, key `key` (lane % 32).
