@@ -17,18 +17,21 @@
 //   dP^T = V dO^T (keys on the MFMA M axis: a lane holds 16 keys of ONE
 //   query, so lse and D are one scalar per lane), the weights and dS^T in
 //   registers, and dQ^T += K^T dS^T with the K^T operand read from LDS with
-//   ds_read_b64_tr_b16 and dS^T rounded to bf16 as the B operand.
+//   ds_read_b64_tr_b16 and dS^T rounded to bf16 as the B operand.  The two
+//   32-key blocks of a tile are staggered so that one block's VALU work runs
+//   between the other block's MFMAs.
 // * attn_bwd_dkdv: parallel over keys (4 waves x 32 keys per workgroup, one
-//   wave per SIMD: K and V rows of the wave's keys, dK^T and dV^T stay in
-//   registers).  Per 32-query block it forms S = Q K^T and dP = dO V^T
-//   (queries on M: a lane holds 16 queries of ONE key), P and dS, and
+//   wave per SIMD: K and -V rows of the wave's keys in registers, dK^T and
+//   dV^T accumulators alongside).  Per 32-query block it forms S = Q K^T and
+//   D - dP (queries on M: a lane holds 16 queries of ONE key), P and dS, and
 //   dV^T += dO^T P, dK^T += Q^T dS with transposed reads of the dO and Q
-//   tiles.  The query heads of a GQA group are walked inside the workgroup so
-//   that a key/value head's gradients sum over them without atomics.
-// Tiles (64 rows) are copied global -> LDS by buffer_load ... lds, double
-// buffered.  Every tile is read both as rows (ds_read_b128) and transposed
-// (ds_read_b64_tr_b16); the 16-byte chunk swizzle below keeps both
-// conflict-free.
+//   tiles, three blocks in flight at once.  The query heads of a GQA group
+//   are walked inside the workgroup so that a key/value head's gradients sum
+//   over them without atomics.
+// Tiles (64 rows) are copied global -> LDS by buffer_load ... lds, two
+// (dQ) or three (dK/dV) stages deep.  Every tile is read both as rows
+// (ds_read_b128) and transposed (ds_read_b64_tr_b16); the 16-byte chunk
+// swizzle below keeps both conflict-free.
 #include <type_traits>
 #include <utility>
 
