@@ -131,3 +131,53 @@ def test_ring_bwd_end_to_end(api, P, n, Hq, Hkv, d, causal):
     dvf = host_f64(dv).transpose(1, 2, 0, 3, 4).reshape(B, Hkv, P * n, d)
     check_grad(dkf, ref[1], "dk pool")
     check_grad(dvf, ref[2], "dv pool")
+
+
+@pytest.mark.slow
+def test_ring_bwd_32k_full_sampled(api):
+    """The backward of the whole 32k ring (8 ranks x 8 resident chunks of
+    4096, 32 heads, d=128, the shape and launch sequence bench.py times),
+    checked on sampled query rows (dQ) and sampled keys (dK, dV) of two heads.
+    The oracle works from its own full-row lse and D (one softmax per row over
+    all 32768 keys), so none of its inputs comes from the GPU."""
+    from sequence_kv_chunk_amd.synth import WORKLOADS, attention_inputs
+    w = WORKLOADS["ring_bf16_32k"]
+    say(f"full-size backward {w.name}")
+    x = attention_inputs(w)
+    P, n, d, H, B = w.P, w.n, w.d, w.Hq, w.B
+    rng = np.random.default_rng(777)
+    ob = _bits(x["q"].shape, rng)
+    kd, vd = dev_bf16(x["k"]), dev_bf16(x["v"])
+    dk = torch.zeros(x["k"].shape, dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+    dqs = []
+    for r in range(P):
+        qd, od = dev_bf16(x["q"][r]), dev_bf16(ob[r])
+        o = torch.empty((B, H, n, d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(B * H * n, dtype=torch.float32, device="cuda")
+        api.ra_ring_attention(qd, kd, vd, o, lse, rank=r, causal=False)
+        D = torch.empty_like(lse)
+        api.ra_attention_bwd_preprocess(o, od, D)
+        dq = torch.zeros((B, H, n, d), dtype=torch.float32, device="cuda")
+        api.ra_ring_attention_bwd(qd, kd, vd, od, lse, D, dq, dk, dv, rank=r, causal=False)
+        dqs.append(dq)
+    torch.cuda.synchronize()
+
+    heads = [0, H - 1]
+    full = lambda bits: bf16_bits_to_f64(bits[:, :, heads]).transpose(1, 2, 0, 3, 4).reshape(B, len(heads), P * n, d)
+    qf, kf, vf, of = full(x["q"]), full(x["k"]), full(x["v"]), full(ob)
+    o_ref, lse_ref = oracle.attention_fp64(qf, kf, vf)
+    D_ref = oracle.rowsum_do_o_fp64(of, o_ref)
+    pick = lambda: sorted({0, 1, n - 1, n, P * n - 1, *(int(i) for i in rng.integers(0, P * n, size=8))})
+    rows, keys = pick(), pick()
+
+    dq_ref, _, _ = oracle.chunk_attention_bwd_fp64(qf[:, :, rows], kf, vf, of[:, :, rows],
+                                                   lse_ref[:, :, rows], D_ref[:, :, rows])
+    dq_got = np.stack([host_f64(dqs[r // n][:, heads][:, :, r % n]) for r in rows], axis=2)
+    check_grad(dq_got, dq_ref, "dq sampled rows")
+
+    _, dk_ref, dv_ref = oracle.chunk_attention_bwd_fp64(qf, kf[:, :, keys], vf[:, :, keys], of, lse_ref, D_ref)
+    dk_got = np.stack([host_f64(dk[j // n][:, heads][:, :, j % n]) for j in keys], axis=2)
+    dv_got = np.stack([host_f64(dv[j // n][:, heads][:, :, j % n]) for j in keys], axis=2)
+    check_grad(dk_got, dk_ref, "dk sampled keys")
+    check_grad(dv_got, dv_ref, "dv sampled keys")
