@@ -40,7 +40,8 @@ ATTN_SRC = os.path.join(ROOT, "sequence_kv_chunk_amd", "csrc", "attn_bf16.hip")
 MFMA_FILE = os.path.join(ROOT, "profiles", "attn_bf16_ring32k_mfma.json")
 PERMUTE_SRC = os.path.join(ROOT, "sequence_kv_chunk_amd", "csrc", "ulysses.hip")
 PERMUTE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ulysses_permute_131k_traffic.json")
-EXTRAS = ("packed", "backward", "ulysses", "rank7", "ulysses_share", "causal_split", "usp")
+EXTRAS = ("packed", "backward", "ulysses", "rank7", "ulysses_share", "causal_split", "usp", "lse_merge",
+          "f32_tiny")
 
 
 def log(*a):
@@ -84,7 +85,7 @@ def time_ring(api, torch, w, x, steps, warmup):
     P = w.P
     qs, kp, vp = x["q"], x["k"], x["v"]
     B, H, n, d = qs.shape[1:]
-    o = torch.empty((B, H, n, d), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((B, H, n, d), dtype=qs.dtype, device="cuda")     # bf16 in -> bf16 out, fp32 -> fp32
     lse = torch.empty(B * H * n, dtype=torch.float32, device="cuda")
     ranks = w.query_ranks
 
@@ -166,6 +167,52 @@ def bench_ulysses(api, torch, iters=10):
     del src, mid, back, flush
     torch.cuda.empty_cache()
     return res
+
+
+def bench_lse_merge(api, torch, iters=10):
+    """The standalone log-sum-exp merge (the unfused ring's step) on the
+    partials of one 128k ring step: O fp32 [1, 32, 16384, 128] and lse
+    [1, 32, 16384], twice in, once out.  HBM-bound: bytes = read both
+    partials + write the merged one.  Each launch follows a 768 MiB fill so
+    that it reads HBM."""
+    B, H, n, d = 1, 32, 16384, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    oa = torch.randn((B, H, n, d), generator=g, device="cuda")
+    ob = torch.randn((B, H, n, d), generator=g, device="cuda")
+    la = torch.randn((B * H * n,), generator=g, device="cuda")
+    lb = torch.randn((B * H * n,), generator=g, device="cuda")
+    oo = torch.empty_like(oa)
+    lo = torch.empty_like(la)
+    flush = torch.empty(768 << 20, dtype=torch.uint8, device="cuda")
+    api.ra_lse_merge(oa, la, ob, lb, oo, lo)
+    ts = []
+    for _ in range(iters):
+        flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        api.ra_lse_merge(oa, la, ob, lb, oo, lo)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    avg = sum(ts) / len(ts)
+    nbytes = 3 * (B * H * n * d * 4 + B * H * n * 4)
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    del oa, ob, la, lb, oo, lo, flush
+    torch.cuda.empty_cache()
+    return {"ms_avg": round(avg, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+            "bytes": nbytes, "workload": "lse merge of two fp32 partials [1, 32, 16384, 128] + lse (one 128k ring step)"}
+
+
+def bench_f32_tiny(api, torch, steps=20):
+    """The tiny fp32 ring (4 virtual ranks x 4 chunks of 256, 4 heads, d=64):
+    a correctness workload; its time is reported, not held against a roofline."""
+    from sequence_kv_chunk_amd.synth import WORKLOADS, device_attention_inputs
+    w = WORKLOADS["ring_f32_tiny"]
+    x = device_attention_inputs(w)
+    _, ms, launches = time_ring(api, torch, w, x, steps, 2)
+    return {"ms": round(ms, 4), "launches": launches, "flops": w.flops(),
+            "workload": "ring_f32_tiny: fp32, B=1, 4 heads, d=64, L=1024 as 4 chunks of 256, all 4 ranks"}
 
 
 def bench_attention_extra(api, torch, name, steps=3):
@@ -476,7 +523,9 @@ def run_extras(api, torch, w, x, chosen):
             ("ulysses_share", "ulysses_share_gqa_128k_causal",
              lambda: bench_attention_extra(api, torch, "ulysses_share_gqa_128k_causal")),
             ("causal_split", "causal_128k_ring_split", lambda: bench_causal_split(api, torch)),
-            ("usp", "usp_128k_causal", lambda: bench_usp(api, torch)))
+            ("usp", "usp_128k_causal", lambda: bench_usp(api, torch)),
+            ("lse_merge", "lse_merge_128k_step", lambda: bench_lse_merge(api, torch)),
+            ("f32_tiny", "ring_f32_tiny", lambda: bench_f32_tiny(api, torch)))
     try:
         for key, name, fn in runs:
             if key in chosen:
