@@ -80,3 +80,37 @@ def test_packed_fast_pass_fallback(api):
         torch.cuda.synchronize()
         check_close(host_f64(o), ref_o[:, :, r * n:(r + 1) * n], "bf16", f"O rank {r}")
         check_close(host_f64(lse).reshape(1, H, n), ref_l[:, :, r * n:(r + 1) * n], "bf16", f"lse rank {r}")
+
+
+@pytest.mark.slow
+def test_packed_32k_full_sampled(api):
+    """The 32k ring packing 16 samples of 2048 tokens, the shape bench.py
+    times (8 ranks x 4096 tokens, 32 heads, d = 128): sampled rows of every
+    rank against the oracle's softmax over the row's own sample prefix."""
+    from sequence_kv_chunk_amd.synth import WORKLOADS, attention_inputs
+    w = WORKLOADS["ring_bf16_32k"]
+    say(f"packed full size {w.name}, samples of 2048")
+    x = attention_inputs(w)
+    P, n, H, d, L = w.P, w.n, w.Hq, w.d, w.L
+    seg_len = 2048
+    seg = torch.arange(0, L, seg_len, dtype=torch.int64, device="cuda")
+    kd, vd = dev_bf16(x["k"]), dev_bf16(x["v"])
+    kf = x["k"].transpose(1, 2, 0, 3, 4).reshape(H, L, d)          # [H, L, d] bits, natural order
+    vf = x["v"].transpose(1, 2, 0, 3, 4).reshape(H, L, d)
+    rng = np.random.default_rng(6000)
+    for r in range(P):
+        o = torch.full((1, H, n, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((H * n,), float("nan"), dtype=torch.float32, device="cuda")
+        api.ra_ring_attention_packed(dev_bf16(x["q"][r]), kd, vd, o, lse, seg, rank=r)
+        torch.cuda.synchronize()
+        go, gl = host_f64(o)[0], host_f64(lse).reshape(H, n)
+        rows = sorted({0, 1, seg_len - 1, seg_len, n - 1, *(int(i) for i in rng.integers(0, n, size=2))})
+        for h in (0, 17, H - 1):
+            for row in rows:
+                t = r * n + row
+                s0 = (t // seg_len) * seg_len
+                qr = bf16_bits_to_f64(x["q"][r][0, h, row])[None, None, None]
+                ref_o, ref_l = oracle.attention_fp64(qr, bf16_bits_to_f64(kf[h, s0:t + 1])[None, None],
+                                                     bf16_bits_to_f64(vf[h, s0:t + 1])[None, None])
+                check_close(go[h, row][None, None, None], ref_o, "bf16", f"O rank {r} row {row} head {h}")
+                check_close(np.array([[[gl[h, row]]]]), ref_l, "bf16", f"lse rank {r} row {row} head {h}")
