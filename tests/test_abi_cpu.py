@@ -78,17 +78,23 @@ def _setup(lib):
 
 
 GB = 1 << 30
+BASE = 0            # device address the offsets below are relative to
 
 
-def _dense(base, H, n, d):
-    return View(base, H * n * d, n * d, d)
+def at(off):
+    """Device address BASE + off (None stays None)."""
+    return None if off is None else BASE + off
+
+
+def _dense(off, H, n, d):
+    return View(at(off), H * n * d, n * d, d)
 
 
 def _attn_args(**kw):
     """A valid bf16 chunk-attention call on fake, disjoint addresses, overridden by kw."""
     B, Hq, Hkv, nq, nk, d = 1, 4, 2, 64, 64, 128
     a = dict(q=_dense(1 * GB, Hq, nq, d), k=_dense(2 * GB, Hkv, nk, d), v=_dense(3 * GB, Hkv, nk, d),
-             o_in=View(None, 0, 0, 0), lse_in=None, o_out=_dense(4 * GB, Hq, nq, d), lse_out=5 * GB,
+             o_in=View(None, 0, 0, 0), lse_in=None, o_out=_dense(4 * GB, Hq, nq, d), lse_out=at(5 * GB),
              B=B, Hq=Hq, Hkv=Hkv, n_q=nq, n_k=nk, d=d, in_dt=BF16, acc_dt=F32, out_dt=BF16, scale=0.5,
              causal=0, q_pos0=0, k_pos0=0, stream=None)
     a.update(kw)
@@ -101,26 +107,26 @@ def _call_attn(lib, a):
                                   a["out_dt"], a["scale"], a["causal"], a["q_pos0"], a["k_pos0"], a["stream"])
 
 
-ATTN_BAD = [
-    ("d=96", dict(d=96), EUNSUP),
-    ("Hq%Hkv", dict(Hq=6, Hkv=4), EINVAL),
-    ("scale=0", dict(scale=0.0), EINVAL),
-    ("scale<0", dict(scale=-1.0), EINVAL),
-    ("scale=inf", dict(scale=float("inf")), EINVAL),
-    ("null q", dict(q=View(None, 0, 0, 0)), EINVAL),
-    ("null lse_out", dict(lse_out=None), EINVAL),
-    ("null k", dict(k=View(None, 0, 0, 0)), EINVAL),
-    ("o_in without lse_in", dict(o_in=_dense(6 * GB, 4, 64, 128)), EINVAL),
-    ("negative size", dict(n_q=-1), EINVAL),
-    ("bad dtype", dict(in_dt=7), EUNSUP),
-    ("misaligned q ptr", dict(q=View(1 * GB + 8, 4 * 64 * 128, 64 * 128, 128)), EUNSUP),
-    ("misaligned q stride", dict(q=View(1 * GB, 4 * 64 * 130, 64 * 130, 130)), EUNSUP),
-    ("negative stride", dict(q=View(1 * GB, 0, -64 * 128, 128)), EINVAL),
-    ("o_out overlaps q", dict(o_out=_dense(1 * GB + 4096, 4, 64, 128)), EINVAL),
-    ("lse_out overlaps k", dict(lse_out=2 * GB + 64), EINVAL),
-    ("o_out partially overlaps o_in", dict(o_in=_dense(6 * GB, 4, 64, 128), lse_in=7 * GB,
+ATTN_BAD = [   # (name, overrides built at call time, expected status)
+    ("d=96", lambda: dict(d=96), EUNSUP),
+    ("Hq%Hkv", lambda: dict(Hq=6, Hkv=4), EINVAL),
+    ("scale=0", lambda: dict(scale=0.0), EINVAL),
+    ("scale<0", lambda: dict(scale=-1.0), EINVAL),
+    ("scale=inf", lambda: dict(scale=float("inf")), EINVAL),
+    ("null q", lambda: dict(q=View(None, 0, 0, 0)), EINVAL),
+    ("null lse_out", lambda: dict(lse_out=None), EINVAL),
+    ("null k", lambda: dict(k=View(None, 0, 0, 0)), EINVAL),
+    ("o_in without lse_in", lambda: dict(o_in=_dense(6 * GB, 4, 64, 128)), EINVAL),
+    ("negative size", lambda: dict(n_q=-1), EINVAL),
+    ("bad dtype", lambda: dict(in_dt=7), EUNSUP),
+    ("misaligned q ptr", lambda: dict(q=View(at(1 * GB + 8), 4 * 64 * 128, 64 * 128, 128)), EUNSUP),
+    ("misaligned q stride", lambda: dict(q=View(at(1 * GB), 4 * 64 * 130, 64 * 130, 130)), EUNSUP),
+    ("negative stride", lambda: dict(q=View(at(1 * GB), 0, -64 * 128, 128)), EINVAL),
+    ("o_out overlaps q", lambda: dict(o_out=_dense(1 * GB + 4096, 4, 64, 128)), EINVAL),
+    ("lse_out overlaps k", lambda: dict(lse_out=at(2 * GB + 64)), EINVAL),
+    ("o_out partially overlaps o_in", lambda: dict(o_in=_dense(6 * GB, 4, 64, 128), lse_in=at(7 * GB),
                                             o_out=_dense(6 * GB + 1024, 4, 64, 128), acc_dt=BF16), EINVAL),
-    ("in-place with dtype change", dict(o_in=_dense(6 * GB, 4, 64, 128), lse_in=7 * GB,
+    ("in-place with dtype change", lambda: dict(o_in=_dense(6 * GB, 4, 64, 128), lse_in=at(7 * GB),
                                          o_out=_dense(6 * GB, 4, 64, 128), acc_dt=F32, out_dt=BF16), EINVAL),
 ]
 
@@ -128,17 +134,25 @@ ATTN_BAD = [
 @no_gpu
 @pytest.mark.parametrize("name,kw,want", ATTN_BAD, ids=[c[0] for c in ATTN_BAD])
 def test_chunk_attention_rejects(lib, name, kw, want):
+    check_attn_case(lib, name, kw, want)
+
+
+def check_attn_case(lib, name, kw, want):
     _setup(lib)
-    st = _call_attn(lib, _attn_args(**kw))
+    st = _call_attn(lib, _attn_args(**kw()))
     assert st == want, f"{name}: got {st}"
     assert lib.sqkv_last_error().decode() != ""
 
 
 @no_gpu
 def test_ring_rejects(lib):
+    check_ring(lib)
+
+
+def check_ring(lib):
     _setup(lib)
     q, k, v = _dense(1 * GB, 4, 64, 128), _dense(2 * GB, 4, 64, 128), _dense(3 * GB, 4, 64, 128)
-    o, lse, none = _dense(4 * GB, 4, 64, 128), 5 * GB, View(None, 0, 0, 0)
+    o, lse, none = _dense(4 * GB, 4, 64, 128), at(5 * GB), View(None, 0, 0, 0)
     cs = 4 * 64 * 128
 
     def call(P=4, rank=0, out_dt=BF16, causal=0, kcs=cs):
@@ -156,14 +170,18 @@ def test_ring_rejects(lib):
 
 @no_gpu
 def test_zigzag_rejects(lib):
+    check_zigzag(lib)
+
+
+def check_zigzag(lib):
     _setup(lib)
     q, k, v = _dense(1 * GB, 4, 64, 128), _dense(2 * GB, 4, 64, 128), _dense(3 * GB, 4, 64, 128)
-    o, lse = _dense(4 * GB, 4, 64, 128), 5 * GB
+    o, lse = _dense(4 * GB, 4, 64, 128), at(5 * GB)
     cs = 4 * 64 * 128
 
     def call(P=4, rank=0, n=64, wo=6 * GB, wl=7 * GB, kcs=cs):
-        return lib.ra_zigzag_attention(q, k, v, kcs, cs, o, lse, wo, wl, 1, 4, 4, n, 128, P, rank, BF16, BF16,
-                                       1.0, None)
+        return lib.ra_zigzag_attention(q, k, v, kcs, cs, o, lse, at(wo), at(wl), 1, 4, 4, n, 128, P, rank, BF16,
+                                       BF16, 1.0, None)
 
     assert call(rank=4) == EINVAL
     assert call(P=0) == EINVAL
@@ -178,10 +196,14 @@ def test_zigzag_rejects(lib):
 
 @no_gpu
 def test_usp_rejects(lib):
+    check_usp(lib)
+
+
+def check_usp(lib):
     _setup(lib)
     vp, i, i64, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
     lib.usp_attention.argtypes = [vp] * 9 + [i, i, i64, i, i, i, f, i, vp]
-    bufs = [g * GB for g in range(1, 10)]
+    bufs = [at(g * GB) for g in range(1, 10)]
 
     def call(P_u=2, P_r=2, L=1024, H=4, H_kv=2, bufs=bufs):
         return lib.usp_attention(*bufs, P_u, P_r, L, H, H_kv, 128, 1.0, 1, None)
@@ -196,11 +218,15 @@ def test_usp_rejects(lib):
 
 @no_gpu
 def test_merge_rejects(lib):
+    check_merge(lib)
+
+
+def check_merge(lib):
     _setup(lib)
     a, b, o = _dense(1 * GB, 4, 8, 64), _dense(2 * GB, 4, 8, 64), _dense(3 * GB, 4, 8, 64)
 
     def call(d=64, oa=a, ob=b, oo=o, la=4 * GB, lb=5 * GB, lo=6 * GB, dt=F32):
-        return lib.ra_lse_merge(oa, la, dt, ob, lb, dt, oo, lo, dt, 1, 4, 8, d, None)
+        return lib.ra_lse_merge(oa, at(la), dt, ob, at(lb), dt, oo, at(lo), dt, 1, 4, 8, d, None)
 
     assert call(d=32) == EUNSUP
     assert call(la=None) == EINVAL
@@ -211,9 +237,13 @@ def test_merge_rejects(lib):
 
 @no_gpu
 def test_ulysses_rejects(lib):
+    check_ulysses(lib)
+
+
+def check_ulysses(lib):
     _setup(lib)
     s2h, h2s = lib.ulysses_seq_to_head, lib.ulysses_head_to_seq
-    src, dst = 1 * GB, 2 * GB
+    src, dst = at(1 * GB), at(2 * GB)
     assert s2h(src, dst, 4, 10, 8, 8, 2, 2, None) == EINVAL        # L % P
     assert s2h(src, dst, 3, 12, 8, 8, 2, 2, None) == EINVAL        # H % P
     assert s2h(src, dst, 8, 16, 4, 4, 2, 2, None) == EINVAL        # P > H
@@ -230,8 +260,12 @@ def test_ulysses_rejects(lib):
 
 @no_gpu
 def test_empty_sizes_are_noops(lib):
+    check_empty(lib)
+
+
+def check_empty(lib):
     _setup(lib)
     # nothing to do: OK without touching memory
     assert _call_attn(lib, _attn_args(n_q=0)) == 0
-    assert lib.ulysses_seq_to_head(1 * GB, 2 * GB, 4, 0, 8, 8, 2, 2, None) == 0
+    assert lib.ulysses_seq_to_head(at(1 * GB), at(2 * GB), 4, 0, 8, 8, 2, 2, None) == 0
     assert lib.sqkv_last_error().decode() == ""
