@@ -41,7 +41,7 @@ MFMA_FILE = os.path.join(ROOT, "profiles", "attn_bf16_ring32k_mfma.json")
 PERMUTE_SRC = os.path.join(ROOT, "sequence_kv_chunk_amd", "csrc", "ulysses.hip")
 PERMUTE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ulysses_permute_131k_traffic.json")
 EXTRAS = ("packed", "backward", "ulysses", "rank7", "ulysses_share", "causal_split", "usp", "lse_merge",
-          "f32_tiny")
+          "f32_tiny", "capacity_1m")
 
 
 def log(*a):
@@ -213,6 +213,41 @@ def bench_f32_tiny(api, torch, steps=20):
     _, ms, launches = time_ring(api, torch, w, x, steps, 2)
     return {"ms": round(ms, 4), "launches": launches, "flops": w.flops(),
             "workload": "ring_f32_tiny: fp32, B=1, 4 heads, d=64, L=1024 as 4 chunks of 256, all 4 ranks"}
+
+
+def bench_capacity_1m(api, torch):
+    """Sequence-length capacity: causal attention over 1,048,576 tokens on one
+    GPU in one call, the Ulysses-share head shape (4 query heads, 1 key/value
+    head, d=128, bf16).  A materialised score matrix would take L*L*2 bytes per
+    head (2 TiB here); the call allocates nothing beyond its inputs/outputs."""
+    L, Hq, Hkv, d = 1 << 20, 4, 1, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8)
+    q = (torch.randn((L, Hq, d), generator=g, device="cuda") * d ** -0.5).to(torch.bfloat16)
+    k = torch.randn((L, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((L, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    o = torch.empty_like(q)
+    lse = torch.empty(Hq * L, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    api.ra_chunk_attention(q, k, v, o, lse, scale=1.0, causal=True)
+    torch.cuda.synchronize()
+    extra = free0 - torch.cuda.mem_get_info()[0]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    api.ra_chunk_attention(q, k, v, o, lse, scale=1.0, causal=True)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    flops = 4 * d * Hq * (L * (L + 1) // 2)
+    io_bytes = sum(t.numel() * t.element_size() for t in (q, k, v, o, lse))
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return {"tokens": L, "ms": round(ms, 2), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "device_bytes_inputs_outputs": io_bytes, "device_bytes_allocated_by_call": int(max(extra, 0)),
+            "score_matrix_bytes_if_materialised_per_head": L * L * 2,
+            "workload": "causal attention, 1048576 tokens, 4 q heads, 1 kv head, d=128, bf16, one call"}
 
 
 def bench_attention_extra(api, torch, name, steps=3):
@@ -525,7 +560,8 @@ def run_extras(api, torch, w, x, chosen):
             ("causal_split", "causal_128k_ring_split", lambda: bench_causal_split(api, torch)),
             ("usp", "usp_128k_causal", lambda: bench_usp(api, torch)),
             ("lse_merge", "lse_merge_128k_step", lambda: bench_lse_merge(api, torch)),
-            ("f32_tiny", "ring_f32_tiny", lambda: bench_f32_tiny(api, torch)))
+            ("f32_tiny", "ring_f32_tiny", lambda: bench_f32_tiny(api, torch)),
+            ("capacity_1m", "capacity_1m_causal", lambda: bench_capacity_1m(api, torch)))
     try:
         for key, name, fn in runs:
             if key in chosen:

@@ -369,3 +369,38 @@ def test_ulysses_share_gqa_128k_full(api):
         ref_o, ref_l = oracle.attention_fp64(qh, kf, vf, causal=True, q_pos0=r, k_pos0=0)
         check_close(oh[r:r + 1].transpose(1, 0, 2)[None], ref_o, "bf16", f"O row {r}")
         check_close(lh[:, r:r + 1][None], ref_l, "bf16", f"lse row {r}")
+
+
+@pytest.mark.slow
+def test_causal_1m_tokens_sampled(api):
+    """Capacity: causal attention over 1,048,576 tokens in one call (4 query
+    heads, 1 key/value head, d=128), with no L x L allocation (2 TiB per head
+    at this length); sampled rows against the oracle."""
+    L, Hq, Hkv, d = 1 << 20, 4, 1, 128
+    say(f"causal attention over {L} tokens")
+    rng = np.random.default_rng(11)
+    qb = f32_to_bf16_bits(rng.standard_normal((L, Hq, d), dtype=np.float32) * np.float32(d ** -0.5))
+    kb = f32_to_bf16_bits(rng.standard_normal((L, Hkv, d), dtype=np.float32))
+    vb = f32_to_bf16_bits(rng.standard_normal((L, Hkv, d), dtype=np.float32))
+    qd, kd, vd = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    o = torch.full((L, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(Hq * L, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    api.ra_chunk_attention(qd, kd, vd, o, lse, causal=True)
+    torch.cuda.synchronize()
+    # no L x L buffer (2 TiB per head here): the only device memory the call
+    # can take is what the HIP runtime reserves on a kernel's first launch
+    # (per-queue scratch for its spilled registers, tens of MiB)
+    assert free0 - torch.cuda.mem_get_info()[0] < oracle.attn_matrix_bytes(L) // 4096
+    rows = sorted({0, 1, 4095, L // 2 + 7, L - 1, *(int(i) for i in rng.integers(0, L, size=3))})
+    oh = {r: host_f64(o[r:r + 1]) for r in rows}                      # [1, Hq, d] each
+    lh = host_f64(lse).reshape(Hq, L)
+    del qd, kd, vd, o, lse
+    kf = bf16_bits_to_f64(kb).transpose(1, 0, 2)[None]
+    vf = bf16_bits_to_f64(vb).transpose(1, 0, 2)[None]
+    for r in rows:
+        qh = bf16_bits_to_f64(qb[r:r + 1]).transpose(1, 0, 2)[None]
+        ref_o, ref_l = oracle.attention_fp64(qh, kf[:, :, :r + 1], vf[:, :, :r + 1])
+        check_close(oh[r].transpose(1, 0, 2)[None], ref_o, "bf16", f"O row {r}")
+        check_close(lh[:, r:r + 1][None], ref_l, "bf16", f"lse row {r}")
