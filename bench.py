@@ -424,6 +424,28 @@ def bench_packed(api, torch, x, w, sample_len=2048, steps=2):
             "workload": f"ring_bf16_32k packing {L // sample_len} causal samples of {sample_len} tokens"}
 
 
+def cpu_baseline_ulysses(torch):
+    """The oracle's index copies (seq->head, then head->seq) on the whole
+    Ulysses workload, 8 shards [16384, 32, 128] bf16 (1 GiB), on the host: the
+    CPU figure beside the permute kernel's.  The input is the same seeded
+    device tensor bench_ulysses permutes, copied to host memory."""
+    import oracle
+    from sequence_kv_chunk_amd.synth import ULYSSES_WORKLOADS, device_ulysses_input
+    w = ULYSSES_WORKLOADS["ulysses_131k_32h"]
+    src = device_ulysses_input(w).cpu().view(torch.int16).numpy().view(np.uint16)
+    res = {}
+    t0 = time.perf_counter()
+    mid = oracle.seq_to_head_naive(src, w.P)
+    res["seq_to_head_s"] = round(time.perf_counter() - t0, 3)
+    t0 = time.perf_counter()
+    oracle.head_to_seq_naive(mid, w.P)
+    res["head_to_seq_s"] = round(time.perf_counter() - t0, 3)
+    secs = (res["seq_to_head_s"] + res["head_to_seq_s"]) / 2
+    res.update({"value": round(w.bytes_per_direction() / secs / 1e9, 2), "unit": "GB/s", "cores": 1,
+                "kind": "oracle", "sample": "the whole workload, both directions (numpy strided copies, one thread)"})
+    return res
+
+
 def cpu_baseline(x_dev, w, torch, budget_rows=4096, heads=16):
     """The fp64 oracle on a bounded sample of the workload: query chunk 0
     (4096 rows) of the first `heads` heads against all 32768 keys."""
@@ -502,6 +524,8 @@ def main():
     if not args.no_cpu and not args.only_extras:
         result["cpu_baseline"] = cpu_baseline(x, w, torch)
         log(f"cpu baseline: {result['cpu_baseline']}")
+        extras["cpu_oracle_ulysses"] = cpu_baseline_ulysses(torch)
+        log(f"cpu oracle ulysses: {extras['cpu_oracle_ulysses']}")
     elif not args.only_extras:
         result["cpu_baseline"] = None
     if extras:
