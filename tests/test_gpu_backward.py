@@ -51,6 +51,10 @@ CASES = [
     (1, 4, 1, 200, 300, 128, True, 500, 300, 1.0),   # queries ahead of the keys
     (1, 2, 2, 130, 200, 64, True, 0, 60, 1.0),       # first rows see nothing
     (1, 8, 2, 129, 513, 128, False, 0, 0, 1.2),      # GQA 4:1, several key tiles
+    (1, 2, 2, 1, 1, 128, False, 0, 0, 1.0),          # one query, one key
+    (1, 4, 2, 3, 200, 64, False, 0, 0, 0.7),         # three queries, ragged keys
+    (1, 2, 1, 70, 40, 128, True, 0, 100, 1.0),       # every key after every query: no contribution
+    (2, 2, 2, 200, 1, 128, True, 50, 0, 1.0),        # one key, seen by every row
 ]
 
 
