@@ -12,11 +12,14 @@ from a seeded generator and are resident in HBM before timing starts.
 Printed: ONE JSON line on stdout with the metric, the roofline of the
 chunk-attention kernel (MFMA-bound) and the CPU oracle timed on a bounded
 sample of the same workload.  Extra figures on the other workloads (Ulysses
-permute GB/s on 8 x [16384, 32, 128] bf16, the causal 128k rank-7 ring share,
-the causal 128k GQA Ulysses share, the whole causal 128k ring under the
-contiguous and the zigzag split, the backward of the 32k ring, the USP
-hybrid at 128k, the 32k ring packing 2k-token samples) go in "extras".  Logs go
-to stderr.
+permute GB/s on 8 x [16384, 32, 128] bf16 with its own HBM roofline and a
+device copy of the same bytes, the causal 128k rank-7 ring share, the causal
+128k GQA Ulysses share, the whole causal 128k ring under the contiguous and
+the zigzag split, the backward of the 32k ring, the USP hybrid at 128k, the
+32k ring packing 2k-token samples, the standalone lse merge of a 128k ring
+step, the tiny fp32 ring, causal attention over 1,048,576 tokens, and with
+the CPU baseline the oracle's Ulysses copies) go in "extras".  Logs go to
+stderr.
 """
 from __future__ import annotations
 
