@@ -43,18 +43,19 @@
 //   would otherwise wait for every in-flight LDS DMA before each LDS read.
 //   The tile count is padded to 4k+1 with empty tiles (fully masked,
 //   zero-filled), which contribute nothing.
-// * Softmax runs in base 2, in up to two passes over the visit.  The fast
-//   pass multiplies Q by scale*log2(e) once (rounded to bf16), so the scores
-//   come out of the MFMA as base-2 exponents, and takes 2^score as the weight
-//   with no maximum: one exponential per score and nothing else.  A
-//   workgroup keeps its result when every row sum lies in a range that rules
-//   out overflow, harmful underflow and large scores; otherwise it runs the
-//   exact pass: scale*log2(e) folded into one FMA with the running maximum,
-//   which is only moved (and O rescaled) when a tile raises it by more than
-//   kRescaleLog2; weights are taken against the slightly stale maximum in
-//   between, which leaves the normalised result unchanged and bounds weights
-//   by 2^kRescaleLog2.  The row sum is taken over the weights as they enter
-//   the P V product (rounded to bf16).
+// * Softmax runs in base 2, in up to two passes over the visit.  Both take
+//   the fp32 score of the bf16 Q and K and multiply it by scale*log2(e) in
+//   fp32 right before the exponential, so the exponent carries only fp32
+//   rounding (Q itself is never rescaled and re-rounded).  The fast pass
+//   takes 2^(score*c) as the weight with no maximum: a multiply and an
+//   exponential per score and nothing else.  A workgroup keeps its result
+//   when every row sum lies in a range that rules out overflow and harmful
+//   underflow; otherwise it runs the exact pass: the running maximum folded
+//   into the same FMA, moved (and O rescaled) only when a tile raises it by
+//   more than kRescaleLog2; weights are taken against the slightly stale
+//   maximum in between, which leaves the normalised result unchanged and
+//   bounds weights by 2^kRescaleLog2.  The row sum is taken over the weights
+//   as they enter the P V product (rounded to bf16).
 // * Masks (causal diagonal, ragged chunk end) are applied only to tiles that
 //   need them; tiles entirely in the future of the whole block are never
 //   fetched.
@@ -142,12 +143,16 @@ __device__ __forceinline__ float sum_half(float x) {
 template <typename T>
 __device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
 
-__device__ __forceinline__ u32x4_t lds_b128(uint32_t addr) {
-  return *reinterpret_cast<SQKV_LDS const u32x4_t*>((size_t)addr);
+// LDS reads take pointers derived from the LDS array by in-bounds offsets, so
+// that a constant part of the offset folds into the instruction's immediate.
+typedef SQKV_LDS unsigned char* lds_ptr;
+
+__device__ __forceinline__ u32x4_t lds_b128(lds_ptr p) {
+  return *reinterpret_cast<SQKV_LDS const u32x4_t*>(p);
 }
 
-__device__ __forceinline__ i16x4_t lds_tr16(uint32_t addr) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<SQKV_LDS i16x4_t*>((size_t)addr));
+__device__ __forceinline__ i16x4_t lds_tr16(lds_ptr p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<SQKV_LDS i16x4_t*>(p));
 }
 
 __device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t bytes) {
@@ -276,34 +281,24 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);   // Q is in registers before any DMA is counted
   };
-  // Q * scale*log2(e), rounded to bf16: the scores come out of the MFMA in
-  // base-2 units (the fast pass)
-  auto prescale_q = [&](float cs) {
-#pragma unroll
-    for (int kc = 0; kc < C::KC; ++kc)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t u = qf[kc][w];
-        qf[kc][w] = pack_bf16x2(__uint_as_float(u << 16) * cs, __uint_as_float(u & 0xffff0000u) * cs);
-      }
-  };
   load_q();
 
   // ---- per-lane LDS offsets ---------------------------------------------------
   // K fragment (A operand of S^T): row l32, 16-byte chunk 2*kc + hi
-  uint32_t kofs[C::KC];
+  const lds_ptr lds = (lds_ptr)smem;
+  lds_ptr kofs[C::KC];
 #pragma unroll
   for (int kc = 0; kc < C::KC; ++kc)
-    kofs[kc] = lds0 + C::K_LDS + l32 * C::ROWB + (((2 * kc + hi) ^ swz_k<D>(l32)) * 16);
+    kofs[kc] = lds + C::K_LDS + l32 * C::ROWB + (((2 * kc + hi) ^ swz_k<D>(l32)) * 16);
   // V^T fragment via transpose reads: the 16-lane group g = lane/16 reads key
   // rows 16*cc + 4*hi + {0..3} (and +8) at d columns 32*md + 16*(g&1) + {0..15};
   // group lane a16 supplies row a16/4, columns 4*(a16%4) .. +3
-  uint32_t vofs[C::MD];
+  lds_ptr vofs[C::MD];
 #pragma unroll
   for (int md = 0; md < C::MD; ++md) {
     const int r = 4 * hi + (a16 >> 2);
     const int c = 4 * md + 2 * ((lane >> 4) & 1) + ((a16 & 3) >> 1);
-    vofs[md] = lds0 + C::V_LDS + r * C::ROWB + ((c ^ swz_v<D>(r)) * 16) + (a16 & 1) * 8;
+    vofs[md] = lds + C::V_LDS + r * C::ROWB + ((c ^ swz_v<D>(r)) * 16) + (a16 & 1) * 8;
   }
   // DMA: wave-wide load i of a tile fills rows r0 = (i*kWaves + wave)*RPW ..
   // r0 + RPW - 1; the lane fills row r0 + lane/NCH at chunk position lane%NCH,
@@ -450,18 +445,17 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   // P columns cc (16 keys of the P V contraction step cc) are x(8*cc) ..
   // x(8*cc + 7).  The groups are spread over the MFMAs of the next tiles;
   // none is a long dependency chain (the wave issues in order).
-  // The fast pass (FAST) takes the scores as base-2 exponents directly: no
-  // maximum, no subtraction; only the exponential groups remain.
-  auto sm_group = [&](STile& v, int g, auto fast) {
+  // The fast pass (FAST) takes 2^(score * c) with no maximum and no
+  // subtraction; only the exponential groups remain.
+  // Fast pass: score e of the lane's 32 gets its multiply and exponential on
+  // its own, so that they spread one per MFMA slot (measured: 1.5% faster
+  // than groups of four).
+  constexpr int kFastGroups = kNB * 16;
+  auto sm_fast = [&](STile& v, int e) {
+    v.b[e >> 4][e & 15] = __builtin_amdgcn_exp2f(v.b[e >> 4][e & 15] * c);
+  };
+  auto sm_group = [&](STile& v, int g) {
     auto x = [&](int e) { return v.b[e >> 4][e & 15]; };
-    if constexpr (decltype(fast)::value) {
-      if (g >= 6) {
-        const int e0 = 4 * (g - 6);
-#pragma unroll
-        for (int e = e0; e < e0 + 4; ++e) v.b[e >> 4][e & 15] = __builtin_amdgcn_exp2f(x(e));
-      }
-      return;
-    }
     if (g == 0) {                      // partial maxima over x(0..11)
 #pragma unroll
       for (int k = 0; k < 4; ++k) mpart[k] = __builtin_fmaxf(__builtin_fmaxf(x(3 * k), x(3 * k + 1)), x(3 * k + 2));
@@ -526,7 +520,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   // O^T[d][query] += V^T[d][key] P^T[key][query]; contraction step cc covers
   // keys 16*cc + {4*hi .. 4*hi+3} and 16*cc + 8 + {4*hi .. 4*hi+3}
   auto vfrag = [&](int cc, int md, auto stage) {
-    const uint32_t a = vofs[md] + decltype(stage)::value * C::TILE + (16 * cc) * C::ROWB;
+    const lds_ptr a = vofs[md] + decltype(stage)::value * C::TILE + (16 * cc) * C::ROWB;
     const i16x4_t lo = lds_tr16(a);
     const i16x4_t up = lds_tr16(a + 8 * C::ROWB);
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -636,15 +630,14 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   // of columns cc, so it comes after the exponentials of those columns (groups
   // 6 + 2*cc, 7 + 2*cc) and after the last P V MFMA of this iteration that
   // reads them (slot 2*MD*(cc+1) - 1); a pack that falls past the last slot
-  // runs after the slot loop.  The fast pass has only the exponential groups:
-  // they are spread evenly over the slots.
-  constexpr int kFastLead = 2;
-  constexpr auto kSlotOfGroup = [](int g, bool fast) {
-    if (fast) return g < 6 ? -1 : kFastLead + ((g - 6) * kSlots) / 8;
-    return (g * kSlots) / (kGroups + kNCC);
-  };
+  // runs after the slot loop.  The fast pass has only the exponentials: one
+  // score per slot, in order.
+  constexpr auto kSlotOfGroup = [](int g) { return (g * kSlots) / (kGroups + kNCC); };
+  constexpr auto kSlotOfFast = [](int e) { return (e * kSlots) / kFastGroups; };
+  static_assert(kSlotOfFast(kFastGroups - 1) < kSlots && kSlotOfGroup(kGroups - 1) < kSlots,
+                "every softmax group must fall inside the slot loop");
   constexpr auto kSlotOfPack = [=](int cc, bool fast) {
-    const int after_exp = kSlotOfGroup(7 + 2 * cc, fast) + 1;
+    const int after_exp = fast ? kSlotOfFast(8 * cc + 7) + 1 : kSlotOfGroup(7 + 2 * cc) + 1;
     const int after_pv = 2 * C::MD * (cc + 1);
     return after_exp > after_pv ? after_exp : after_pv;
   };
@@ -676,8 +669,13 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     scores(sb, Step<1>{});
     mask(sa, 0, nv0, kp0);
     mask(sb, 1, nv1, kp1);
+    if constexpr (FAST) {
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) sm_group(sa, g, fast);   // O is still zero: no rescale
+      for (int j = 0; j < kFastGroups; ++j) sm_fast(sa, j);
+    } else {
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) sm_group(sa, g);     // O is still zero: no rescale
+    }
 #pragma unroll
     for (int cc = 0; cc < kNCC; ++cc) pack(sa, cc);
     pin(l_run);
@@ -729,9 +727,15 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
         constexpr int m = i >> 1;
         if constexpr ((i & 1) == 0) mfma_s(nx, kfr[m], m);
         else mfma_pv(vfr[m], m / C::MD, m % C::MD);
-        static_for<kGroups>([&](auto G) {
-          if constexpr (kSlotOfGroup(decltype(G)::value, FAST) == i) sm_group(cu, decltype(G)::value, fast);
-        });
+        if constexpr (FAST) {
+          static_for<kFastGroups>([&](auto J) {
+            if constexpr (kSlotOfFast(decltype(J)::value) == i) sm_fast(cu, decltype(J)::value);
+          });
+        } else {
+          static_for<kGroups>([&](auto G) {
+            if constexpr (kSlotOfGroup(decltype(G)::value) == i) sm_group(cu, decltype(G)::value);
+          });
+        }
         static_for<kNCC>([&](auto Q) {
           if constexpr (kSlotOfPack(decltype(Q)::value, FAST) == i) pack(cu, decltype(Q)::value);
         });
@@ -758,18 +762,16 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
     pv(Step<0>{});                       // V of the last (padded) tile landed above
     };
 
-  // The fast pass (Q pre-scaled by scale*log2(e) and rounded to bf16, weights
-  // 2^score with no maximum subtracted) is kept when every row's sum lies in
-  // [2^-24, 2^40] and every accumulator is finite: then no weight overflowed,
-  // the ones that underflowed are below 2^-100 of the sum, and no row's
-  // scores sit far from zero, where the rounding of the pre-scaled Q (half a
-  // bf16 unit per element, the size of Q's own rounding to bf16) moves a
-  // score furthest.  Otherwise the whole workgroup (its waves share the LDS
-  // pipeline) runs the exact pass with the running maximum.
+  // The fast pass (weights 2^(score * c) with no maximum subtracted) is kept
+  // when every row's sum lies in [2^-24, 2^40] and every accumulator is
+  // finite: then no weight overflowed (each is at most the sum) and the ones
+  // that underflowed (below 2^-126) are under 2^-100 of the sum.  Its weights
+  // are then the exact pass's up to the fp32 rounding of the exponent and a
+  // factor 2^m common to a row, which the normalisation cancels.  Otherwise the whole workgroup (its waves
+  // share the LDS pipeline) runs the exact pass with the running maximum.
   volatile int* redo_flag = reinterpret_cast<volatile int*>(smem + C::LDS_BYTES);
   if (threadIdx.x == 0) *redo_flag = 0;
   if (T > 0) {
-    prescale_q(c);
     run_pass(std::true_type{});
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     const float lt = sum_half(l_run);
@@ -780,10 +782,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
       for (int j = 0; j < 16; ++j) ok &= __builtin_isfinite(oacc[md][j]);
     if (__any(!ok) && lane == 0) *redo_flag = 1;
     lds_reads_done_sync();   // (the first barrier of the pass ordered the clearing before this)
-    if (*redo_flag != 0) {
-      load_q();
-      run_pass(std::false_type{});
-    }
+    if (*redo_flag != 0) run_pass(std::false_type{});
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no DMA may outlive the workgroup's LDS
 

@@ -235,6 +235,52 @@ def ulysses_input(w: UlyssesWorkload, *, L: int | None = None, H: int | None = N
     return f32_to_bf16_bits(x)
 
 
+# --------------------------------------------------------------------------
+# scores far from zero with every key aligned to its query
+# --------------------------------------------------------------------------
+LOG2E_F32 = np.float32(1.4426950408889634)
+
+
+def bf16_values_rounding_down_under_log2e(count: int = 8):
+    """The `count` bf16 values in [0.25, 0.5) whose product with log2(e),
+    taken in float32 and rounded to bf16, lands furthest below the exact
+    product.  Returns (uint16 patterns, relative shift of that product)."""
+    bits = (0x3E80 + np.arange(128)).astype(np.uint16)          # 0.25 * (1 + m/128)
+    x = bf16_bits_to_f64(bits)
+    scaled = bf16_bits_to_f64(f32_to_bf16_bits(bf16_bits_to_f32(bits) * LOG2E_F32))
+    rel = (scaled - x * float(LOG2E_F32)) / (x * float(LOG2E_F32))
+    order = np.argsort(rel, kind="stable")[:count]
+    return bits[order], rel[order]
+
+
+def aligned_score_inputs(B: int, H: int, nq: int, nk: int, d: int, seed: int,
+                         top_nats=(10.0, 18.0)):
+    """bf16 Q, K, V (uint16 patterns) whose scores (scale 1) all lie far above
+    zero and move together under any per-element rescaling of Q.
+
+    Every query element is one of the bf16 values in [0.25, 0.5) whose copy
+    scaled by log2(e) and re-rounded to bf16 falls furthest below the exact
+    product, so a computation that rescales Q and rounds it again shifts every
+    score of a row in the same direction.  Keys are positive and aligned with
+    the queries: key u of head h has elements a_h * s_u * (1 + 0.2 z), z ~
+    N(0, 1) clipped to [-2, 2], with s_u = 1 for half the keys and 0.97 for
+    the other half, and a_h chosen so that a row's largest score is about
+    top_nats[0] .. top_nats[1] nats (spread over the heads).  The row sums of
+    exp(score) then lie far above 1 but well inside float range.  V is
+    N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    vals, _ = bf16_values_rounding_down_under_log2e()
+    q = vals[rng.integers(0, len(vals), size=(B, H, nq, d))]
+    qmean = float(np.mean(bf16_bits_to_f64(vals)))
+    tops = np.linspace(top_nats[0], top_nats[1], H) if H > 1 else np.array([top_nats[1]])
+    a = (tops / (d * qmean * 1.2)).astype(np.float32)           # 1.2: the largest keys' noise gain
+    z = np.clip(rng.standard_normal((B, H, nk, d), dtype=np.float32), -2.0, 2.0)
+    s = np.where(np.arange(nk) % 2 == 0, np.float32(1.0), np.float32(0.97)).astype(np.float32)
+    k = a[None, :, None, None] * s[None, None, :, None] * (np.float32(1.0) + np.float32(0.2) * z)
+    v = rng.standard_normal((B, H, nk, d), dtype=np.float32)
+    return q, f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
 # 16-bit patterns that a value-based copy would not preserve:
 # quiet NaN with payload, signalling NaN, +inf, -inf, -0, smallest subnormal,
 # largest subnormal, negative NaN.

@@ -115,6 +115,29 @@ def test_ring_bwd_end_to_end(api, P, n, Hq, Hkv, d, causal):
     kb = _bits((P, B, Hkv, n, d), rng)
     vb = _bits((P, B, Hkv, n, d), rng)
     ob = _bits((P, B, Hq, n, d), rng)
+    _ring_bwd_check(api, qb, kb, vb, ob, causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rounding_edge_ring_bwd(api, causal):
+    """The ring backward fed by the GPU forward's lse on inputs whose scores
+    all sit at 9-17 nats, aligned with their queries (row sums 2^20-2^36, the
+    range where the forward keeps its fast pass): P = exp(S - lse) scales
+    every gradient by any error in lse."""
+    from sequence_kv_chunk_amd.synth import aligned_score_inputs
+    P, B, H, n, d = 4, 1, 2, 256, 128
+    say(f"ring bwd, rounding edge inputs, causal={causal}")
+    qb, kb, vb = aligned_score_inputs(B, H, P * n, P * n, d, seed=80 + int(causal))
+    pool = lambda x: np.ascontiguousarray(x.reshape(B, H, P, n, d).transpose(2, 0, 1, 3, 4))
+    ob = _bits((P, B, H, n, d), np.random.default_rng(81))
+    _ring_bwd_check(api, pool(qb), pool(kb), pool(vb), ob, causal)
+
+
+def _ring_bwd_check(api, qb, kb, vb, ob, causal):
+    """GPU ring forward, D and backward of every rank of pools [P, B, H, n, d]
+    against the gradients of one softmax over the whole sequence."""
+    P, B, Hq, n, d = qb.shape
+    Hkv = kb.shape[2]
     full = lambda x: bf16_bits_to_f64(x).transpose(1, 2, 0, 3, 4).reshape(B, x.shape[2], P * n, d)
     ref = oracle.attention_bwd_fp64(full(qb), full(kb), full(vb), full(ob), causal=causal)
     kd, vd = dev_bf16(kb), dev_bf16(vb)
