@@ -267,6 +267,37 @@ sqkv_status ra_zigzag_attention(sqkv_view q, sqkv_view k, sqkv_view v,
                                 float scale, void* stream);
 
 /*
+ * ra_zigzag_attention_noalloc -- ra_zigzag_attention for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same three launches, with the late
+ * piece's fp32 partial (what work_o / work_lse hold above) kept in a
+ * file-scope device array of the library instead of caller buffers.  It calls
+ * no hipMalloc, hipFree or allocating routine.
+ *
+ * Arguments, layouts, support and status codes as ra_zigzag_attention
+ * without work_o / work_lse.  Limit: the partial needs 4*(d+1) bytes per row
+ * of B*Hq*n/2 rows, plus up to 255 bytes of alignment, within
+ * ra_zigzag_attention_noalloc_max_bytes() (64 MiB); larger calls return
+ * SQKV_EUNSUPPORTED before any HIP call.  Each GPU holds its own copy of the
+ * array from the library's first use on it until the process ends (looked up
+ * once per device with hipGetSymbolAddress on the device current at the
+ * call, which must be the one `stream` and the buffers belong to).  Every
+ * call on a GPU shares that GPU's array, so calls that overlap on one GPU
+ * (other streams, other threads) race; calls on one stream are ordered.
+ * Nothing in the array needs to start at zero: launch 2 writes the whole
+ * partial before launch 3 reads it.
+ */
+sqkv_status ra_zigzag_attention_noalloc(sqkv_view q, sqkv_view k, sqkv_view v,
+                                        int64_t k_chunk_stride, int64_t v_chunk_stride,
+                                        sqkv_view o, float* lse,
+                                        int B, int Hq, int Hkv, int n, int d, int P, int rank,
+                                        sqkv_dtype in_dtype, sqkv_dtype out_dtype,
+                                        float scale, void* stream);
+
+/* Size in bytes of the array ra_zigzag_attention_noalloc works in. */
+size_t ra_zigzag_attention_noalloc_max_bytes(void);
+
+/*
  * ra_lse_merge -- the online-softmax merge of two partial attentions over
  * disjoint key sets ([RA] section 5, the rescale of the running output and
  * normaliser by the exponent of the change in the running maximum), in the

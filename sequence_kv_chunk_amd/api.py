@@ -53,6 +53,11 @@ _lib.ra_ring_attention.argtypes = [_V, _V, _V, _c_i64, _c_i64, _V, _vp, _c_int, 
 _lib.ra_zigzag_attention.restype = _c_int
 _lib.ra_zigzag_attention.argtypes = [_V, _V, _V, _c_i64, _c_i64, _V, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                      _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_f, _vp]
+_lib.ra_zigzag_attention_noalloc.restype = _c_int
+_lib.ra_zigzag_attention_noalloc.argtypes = [_V, _V, _V, _c_i64, _c_i64, _V, _vp, _c_int, _c_int, _c_int, _c_int,
+                                             _c_int, _c_int, _c_int, _c_int, _c_int, _c_f, _vp]
+_lib.ra_zigzag_attention_noalloc_max_bytes.restype = ctypes.c_size_t
+_lib.ra_zigzag_attention_noalloc_max_bytes.argtypes = []
 _lib.ra_attention_bwd_preprocess.restype = _c_int
 _lib.ra_attention_bwd_preprocess.argtypes = [_V, _V, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]
 _lib.ra_chunk_attention_bwd.restype = _c_int
@@ -76,7 +81,7 @@ _lib.ulysses_head_to_seq.restype = _c_int
 _lib.ulysses_head_to_seq.argtypes = [_vp, _vp, _c_int, _c_i64, _c_int, _c_int, _c_int, _vp]
 
 EXPORTED = ("ra_chunk_attention", "ra_ring_attention", "ra_ring_attention_packed", "ra_zigzag_attention",
-            "ra_lse_merge",
+            "ra_zigzag_attention_noalloc", "ra_zigzag_attention_noalloc_max_bytes", "ra_lse_merge",
             "ra_attention_bwd_preprocess", "ra_chunk_attention_bwd", "ra_ring_attention_bwd",
             "ulysses_seq_to_head", "ulysses_head_to_seq", "usp_attention", "sqkv_last_error")
 
@@ -222,6 +227,31 @@ def ra_zigzag_attention(q, k_pool, v_pool, o, lse, *, rank: int, scale: float = 
                                       wl.data_ptr(), B, Hq, k_pool.shape[2], n, d, P, int(rank), _dtype_code(q),
                                       _dtype_code(o), float(scale), _stream(q))
     _check(st)
+
+
+def ra_zigzag_attention_noalloc(q, k_pool, v_pool, o, lse, *, rank: int, scale: float = 1.0):
+    """ra_zigzag_attention with the late piece's partial in the library's own
+    per-GPU scratch array instead of caller work buffers: allocates nothing,
+    for callers that cannot.  Calls that overlap on one GPU race on that
+    scratch.  B*Hq*n/2 rows must fit zigzag_noalloc_max_bytes()."""
+    if k_pool.dim() != 5 or v_pool.shape != k_pool.shape:
+        raise SqkvError(SQKV_EINVAL, "k_pool, v_pool must be [P, B, Hkv, n, d]")
+    _same_device(q, k_pool, v_pool, o, lse)
+    P = k_pool.shape[0]
+    B, Hq, n, d = q.shape
+    if tuple(o.shape) != (B, Hq, n, d) or k_pool.shape[3] != n or k_pool.shape[1] != B:
+        raise SqkvError(SQKV_EINVAL, "shapes disagree")
+    with torch.cuda.device(q.device):
+        st = _lib.ra_zigzag_attention_noalloc(_view(q), _view(k_pool[0]), _view(v_pool[0]), k_pool.stride(0),
+                                              v_pool.stride(0), _view(o), _lse_ptr(lse, B * Hq * n), B, Hq,
+                                              k_pool.shape[2], n, d, P, int(rank), _dtype_code(q), _dtype_code(o),
+                                              float(scale), _stream(q))
+    _check(st)
+
+
+def zigzag_noalloc_max_bytes() -> int:
+    """Size of the scratch array ra_zigzag_attention_noalloc works in."""
+    return int(_lib.ra_zigzag_attention_noalloc_max_bytes())
 
 
 def ra_attention_bwd_preprocess(o, dout, D):

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/sqkv.h"
@@ -266,11 +267,14 @@ SQKV_EXPORT sqkv_status ra_ring_attention_packed(sqkv_view q, sqkv_view k, sqkv_
   return hip_status(launch_attention(p, d, in_dtype, (hipStream_t)stream), "ra_ring_attention_packed launch");
 }
 
-SQKV_EXPORT sqkv_status ra_zigzag_attention(sqkv_view q, sqkv_view k, sqkv_view v, int64_t k_chunk_stride,
-                                            int64_t v_chunk_stride, sqkv_view o, float* lse, float* work_o,
-                                            float* work_lse, int B, int Hq, int Hkv, int n, int d, int P,
-                                            int rank, sqkv_dtype in_dtype, sqkv_dtype out_dtype, float scale,
-                                            void* stream) {
+namespace {
+
+// Validation of a zigzag call.  The work buffers are checked only when
+// `work_given` (the no-allocation variant brings its own).
+sqkv_status check_zigzag(sqkv_view q, sqkv_view k, sqkv_view v, int64_t k_chunk_stride, int64_t v_chunk_stride,
+                         sqkv_view o, float* lse, float* work_o, float* work_lse, bool work_given, int B, int Hq,
+                         int Hkv, int n, int d, int P, int rank, sqkv_dtype in_dtype, sqkv_dtype out_dtype,
+                         float scale) {
   if (P < 1 || rank < 0 || rank >= P) return fail(SQKV_EINVAL, "need P >= 1 and 0 <= rank < P (P=%d rank=%d)", P, rank);
   if (n % 2) return fail(SQKV_EINVAL, "the local shard length n=%d must be even (two pieces)", n);
   if (k_chunk_stride < 0 || v_chunk_stride < 0) return fail(SQKV_EINVAL, "negative chunk stride");
@@ -281,23 +285,31 @@ SQKV_EXPORT sqkv_status ra_zigzag_attention(sqkv_view q, sqkv_view k, sqkv_view 
               (int64_t)(P - 1) * std::max(k_chunk_stride, v_chunk_stride) * ieb, d,
               in_dtype, SQKV_F32, out_dtype, scale};
   sqkv_status st = check_attention(a);
-  if (st != SQKV_OK || n == 0) return st;
+  if (st != SQKV_OK || n == 0 || !work_given) return st;
   const int c = n / 2;
   if (!work_o || !work_lse) return fail(SQKV_EINVAL, "null work_o or work_lse");
   if (((uintptr_t)work_o) % 16 || ((uintptr_t)work_lse) % 4)
     return fail(SQKV_EUNSUPPORTED, "work_o must be 16-byte and work_lse 4-byte aligned");
-  {
-    const int64_t rows = (int64_t)B * Hq * c;
-    Range rw = dense_range(work_o, rows * d, 4), rwl = dense_range(work_lse, rows, 4);
-    Range rq = view_range(q, B, Hq, n, d, ieb), ro = view_range(o, B, Hq, n, d, dtype_bytes(out_dtype));
-    Range rl = dense_range(lse, (int64_t)B * Hq * n, 4);
-    Range rk = view_range(k, B, Hkv, n, d, ieb), rv = view_range(v, B, Hkv, n, d, ieb);
-    rk.hi += a.kv_extent_extra_bytes;
-    rv.hi += a.kv_extent_extra_bytes;
-    for (const Range* r : {&rq, &ro, &rl, &rk, &rv})
-      if (overlap(rw, *r) || overlap(rwl, *r)) return fail(SQKV_EINVAL, "work buffers overlap q, k, v, o or lse");
-    if (overlap(rw, rwl)) return fail(SQKV_EINVAL, "work_o overlaps work_lse");
-  }
+  const int64_t rows = (int64_t)B * Hq * c;
+  Range rw = dense_range(work_o, rows * d, 4), rwl = dense_range(work_lse, rows, 4);
+  Range rq = view_range(q, B, Hq, n, d, ieb), ro = view_range(o, B, Hq, n, d, dtype_bytes(out_dtype));
+  Range rl = dense_range(lse, (int64_t)B * Hq * n, 4);
+  Range rk = view_range(k, B, Hkv, n, d, ieb), rv = view_range(v, B, Hkv, n, d, ieb);
+  rk.hi += a.kv_extent_extra_bytes;
+  rv.hi += a.kv_extent_extra_bytes;
+  for (const Range* r : {&rq, &ro, &rl, &rk, &rv})
+    if (overlap(rw, *r) || overlap(rwl, *r)) return fail(SQKV_EINVAL, "work buffers overlap q, k, v, o or lse");
+  if (overlap(rw, rwl)) return fail(SQKV_EINVAL, "work_o overlaps work_lse");
+  return ok();
+}
+
+// The three launches of a validated zigzag call (n > 0).
+sqkv_status launch_zigzag(sqkv_view q, sqkv_view k, sqkv_view v, int64_t k_chunk_stride, int64_t v_chunk_stride,
+                          sqkv_view o, float* lse, float* work_o, float* work_lse, int B, int Hq, int Hkv, int n,
+                          int d, int P, int rank, sqkv_dtype in_dtype, sqkv_dtype out_dtype, float scale,
+                          void* stream) {
+  const int ieb = dtype_bytes(in_dtype);
+  const int c = n / 2;
   auto rows_from = [](sqkv_view x, int64_t t0, int eb) {
     x.ptr = static_cast<char*>(x.ptr) + t0 * x.sn * eb;
     return x;
@@ -357,6 +369,84 @@ SQKV_EXPORT sqkv_status ra_zigzag_attention(sqkv_view q, sqkv_view k, sqkv_view 
   p3.lse_in_hs = c;
   p3.lse_out_hs = n;
   return hip_status(launch_attention(p3, d, in_dtype, hs), "ra_zigzag_attention launch 3");
+}
+
+}  // namespace
+
+namespace {
+
+// Scratch of the no-allocation zigzag entry point: the late piece's fp32
+// partial (O, then lse).  A file-scope device array, so each GPU the library
+// runs on holds its own copy from module load until the process ends, at the
+// address hipGetSymbolAddress gives on that device.  In host code the array's
+// name is a host-side stand-in, never a device address: only the per-device
+// pointers below reach kernels.
+constexpr size_t kZigzagScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kZigzagScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's address on the current device, looked up once per device.
+sqkv_status scratch_on_current_device(unsigned char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SQKV_EUNSUPPORTED, "device index %d above %d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(SQKV_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = static_cast<unsigned char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return SQKV_OK;
+}
+
+}  // namespace
+
+SQKV_EXPORT size_t ra_zigzag_attention_noalloc_max_bytes(void) { return kZigzagScratchBytes; }
+
+SQKV_EXPORT sqkv_status ra_zigzag_attention_noalloc(sqkv_view q, sqkv_view k, sqkv_view v,
+                                                    int64_t k_chunk_stride, int64_t v_chunk_stride, sqkv_view o,
+                                                    float* lse, int B, int Hq, int Hkv, int n, int d, int P,
+                                                    int rank, sqkv_dtype in_dtype, sqkv_dtype out_dtype,
+                                                    float scale, void* stream) {
+  sqkv_status st = check_zigzag(q, k, v, k_chunk_stride, v_chunk_stride, o, lse, nullptr, nullptr, false, B, Hq,
+                                Hkv, n, d, P, rank, in_dtype, out_dtype, scale);
+  if (st != SQKV_OK || n == 0) return st;
+  // work_o [B, Hq, n/2, d] fp32, then work_lse [B, Hq, n/2] fp32 at the next
+  // 256-byte boundary
+  const uint64_t rows = (uint64_t)B * (uint64_t)Hq * (uint64_t)(n / 2);
+  const uint64_t cap_rows = (kZigzagScratchBytes - 256) / (4 * (uint64_t)(d + 1));
+  if (rows > cap_rows)
+    return fail(SQKV_EUNSUPPORTED,
+                "ra_zigzag_attention_noalloc: B*Hq*n/2 = %llu rows need %llu bytes of scratch, above its "
+                "%llu-byte maximum; use ra_zigzag_attention with caller-owned work buffers",
+                (unsigned long long)rows, (unsigned long long)(rows * 4 * (uint64_t)(d + 1)),
+                (unsigned long long)kZigzagScratchBytes);
+  const uint64_t o_bytes = (rows * 4 * (uint64_t)d + 255) & ~(uint64_t)255;
+  unsigned char* base = nullptr;
+  st = scratch_on_current_device(&base);
+  if (st != SQKV_OK) return st;
+  return launch_zigzag(q, k, v, k_chunk_stride, v_chunk_stride, o, lse, reinterpret_cast<float*>(base),
+                       reinterpret_cast<float*>(base + o_bytes), B, Hq, Hkv, n, d, P, rank, in_dtype, out_dtype,
+                       scale, stream);
+}
+
+SQKV_EXPORT sqkv_status ra_zigzag_attention(sqkv_view q, sqkv_view k, sqkv_view v, int64_t k_chunk_stride,
+                                            int64_t v_chunk_stride, sqkv_view o, float* lse, float* work_o,
+                                            float* work_lse, int B, int Hq, int Hkv, int n, int d, int P,
+                                            int rank, sqkv_dtype in_dtype, sqkv_dtype out_dtype, float scale,
+                                            void* stream) {
+  sqkv_status st = check_zigzag(q, k, v, k_chunk_stride, v_chunk_stride, o, lse, work_o, work_lse, true, B, Hq,
+                                Hkv, n, d, P, rank, in_dtype, out_dtype, scale);
+  if (st != SQKV_OK || n == 0) return st;
+  return launch_zigzag(q, k, v, k_chunk_stride, v_chunk_stride, o, lse, work_o, work_lse, B, Hq, Hkv, n, d, P,
+                       rank, in_dtype, out_dtype, scale, stream);
 }
 
 namespace {

@@ -269,3 +269,26 @@ def check_empty(lib):
     assert _call_attn(lib, _attn_args(n_q=0)) == 0
     assert lib.ulysses_seq_to_head(at(1 * GB), at(2 * GB), 4, 0, 8, 8, 2, 2, None) == 0
     assert lib.sqkv_last_error().decode() == ""
+
+
+@no_gpu
+def test_zigzag_noalloc_refuses_on_the_host(lib):
+    """The no-allocation zigzag variant validates like ra_zigzag_attention and
+    refuses partials larger than its scratch array before any HIP call."""
+    _setup(lib)
+    i, i64, f, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+    V = View
+    lib.ra_zigzag_attention_noalloc.argtypes = [V, V, V, i64, i64, V, vp, i, i, i, i, i, i, i, i, i, f, vp]
+    lib.ra_zigzag_attention_noalloc_max_bytes.restype = ctypes.c_size_t
+    assert lib.ra_zigzag_attention_noalloc_max_bytes() == 64 << 20
+    H, n, d = 32, 8192, 128          # 131072 rows of 129 fp32 values: above 64 MiB
+    q, k, v = _dense(1 * GB, H, n, d), _dense(2 * GB, H, n, d), _dense(3 * GB, H, n, d)
+    o, lse = _dense(4 * GB, H, n, d), at(5 * GB)
+
+    def call(n=n, rank=0):
+        return lib.ra_zigzag_attention_noalloc(q, k, v, 0, 0, o, lse, 1, H, H, n, d, 1, rank, BF16, BF16, 1.0,
+                                               None)
+
+    assert call() == EUNSUP and b"scratch" in lib.sqkv_last_error()
+    assert call(n=n - 1) == EINVAL           # odd shard: refused before the size check
+    assert call(rank=1) == EINVAL
