@@ -2,24 +2,32 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-One step = the whole 32k-token ring on one GPU: 8 virtual ranks, each
-attending with its 4096-row query chunk to all 8 resident key/value chunks in
-ring order (one launch per rank, the online-softmax merge carried across the
-chunks in registers; bf16 in, fp32 accumulation, bf16 out), B=1, 32 heads,
-d=128, non-causal.  Inputs are drawn on the device
-from a seeded generator and are resident in HBM before timing starts.
+One step = one GPU's share of the causal 128k ring: rank 7 of P = 8 (its
+16384-row query chunk, the last of the sequence) attending to all 8 resident
+key/value chunks of 16384 tokens in ring order, its own (diagonal) chunk
+first, in one launch that carries the online-softmax merge across the chunks
+in registers; B=1, 32 heads, d=128, bf16 in, fp32 accumulation, bf16 out.
+Inputs are drawn on the device from a seeded generator and are resident in
+HBM before timing starts.  W untimed warm-up steps, then exactly K timed
+steps between synchronisations; every launch is also bracketed by HIP events
+on the stream it runs on, which give the kernel's mean and median launch
+time for the roofline.
 
 Printed: ONE JSON line on stdout with the metric, the roofline of the
-chunk-attention kernel (MFMA-bound) and the CPU oracle timed on a bounded
-sample of the same workload.  Extra figures on the other workloads (Ulysses
-permute GB/s on 8 x [16384, 32, 128] bf16 with its own HBM roofline and a
-device copy of the same bytes, the causal 128k rank-7 ring share, the causal
-128k GQA Ulysses share, the whole causal 128k ring under the contiguous and
-the zigzag split, the backward of the 32k ring, the USP hybrid at 128k, the
-32k ring packing 2k-token samples, the standalone lse merge of a 128k ring
-step, the tiny fp32 ring, causal attention over 1,048,576 tokens, and with
-the CPU baseline the oracle's Ulysses copies) go in "extras".  Logs go to
-stderr.
+chunk-attention kernel (MFMA-bound) on that launch, and the CPU oracle timed
+on a seeded sample of the same workload (16384 query rows across all heads,
+extrapolated to the full share by visible pairs, with the GPU's error on
+those rows).  Extra figures on the other workloads go in "extras": the whole
+32k ring (8 ranks x 8 chunks of 4096, non-causal) and the causal GQA Ulysses
+share at 128k (4 query heads, 1 key/value head), each with its own roofline
+object; the Ulysses permutes on 8 x [16384, 32, 128] bf16 with their HBM
+roofline beside the same kernel run as a plain copy of the same bytes; the
+GQA key/value replication of the Ulysses exchange at 128k (1 and 2 key/value
+heads copied up to 8 ranks); the whole causal 128k ring under the contiguous
+and the zigzag split; the backward of the 32k ring; the USP hybrid at 128k;
+the 32k ring packing 2k-token samples; the standalone lse merge of a 128k
+ring step; the tiny fp32 ring; causal attention over 1,048,576 tokens; and,
+with the CPU baseline, the oracle's Ulysses copies.  Logs go to stderr.
 """
 from __future__ import annotations
 
@@ -27,6 +35,8 @@ import argparse
 import hashlib
 import json
 import os
+import platform
+import statistics
 import sys
 import time
 
@@ -38,13 +48,20 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 METRIC = "chunked-attention TFLOP/s (% bf16 MFMA peak); Ulysses permute GB/s (% HBM)"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_ring32k_traffic.json")
+HEADLINE = "ring_bf16_128k_rank7_causal"
 ATTN_SRC = os.path.join(ROOT, "sequence_kv_chunk_amd", "csrc", "attn_bf16.hip")
-MFMA_FILE = os.path.join(ROOT, "profiles", "attn_bf16_ring32k_mfma.json")
 PERMUTE_SRC = os.path.join(ROOT, "sequence_kv_chunk_amd", "csrc", "ulysses.hip")
-PERMUTE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ulysses_permute_131k_traffic.json")
-EXTRAS = ("packed", "backward", "ulysses", "rank7", "ulysses_share", "causal_split", "usp", "lse_merge",
-          "f32_tiny", "capacity_1m")
+PROFILES = os.path.join(ROOT, "profiles")
+# committed rocprofv3 counter summaries, per workload (used while the kernel source is unchanged)
+ATTN_COUNTERS = {
+    "ring_bf16_128k_rank7_causal": ("attn_bf16_rank7_128k_traffic.json", "attn_bf16_rank7_128k_mfma.json"),
+    "ring_bf16_32k": ("attn_bf16_ring32k_traffic.json", "attn_bf16_ring32k_mfma.json"),
+    "ulysses_share_gqa_128k_causal": ("attn_bf16_gqa_share_128k_traffic.json", "attn_bf16_gqa_share_128k_mfma.json"),
+}
+PERMUTE_TRAFFIC_FILE = os.path.join(PROFILES, "ulysses_permute_131k_traffic.json")
+REPLICATION_TRAFFIC_FILE = os.path.join(PROFILES, "ulysses_gqa_replication_131k_traffic.json")
+EXTRAS = ("ring32k", "ulysses_share", "ulysses", "gqa_replication", "packed", "backward", "causal_split", "usp",
+          "lse_merge", "f32_tiny", "capacity_1m")
 
 
 def log(*a):
@@ -63,11 +80,11 @@ def kernel_source_hash(path: str = ATTN_SRC) -> str:
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
-def load_profile(path: str, src: str):
+def load_profile(name: str, src: str):
     """A committed rocprofv3 counter summary, if it was taken on the current
     kernel source (else None: the counters describe older code)."""
     try:
-        with open(path) as f:
+        with open(os.path.join(PROFILES, name)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -76,98 +93,301 @@ def load_profile(path: str, src: str):
     return t
 
 
-def load_traffic():
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    passes, if they were taken on the current kernel source."""
-    t = load_profile(TRAFFIC_FILE, ATTN_SRC)
-    return None if t is None else t.get("bytes_per_launch")
+def timed_launches(torch, fn, warmup, iters, flush=None):
+    """Runs fn `warmup` times, then `iters` times, each bracketed by HIP events
+    on the current stream (the one the library enqueues on).  With `flush`, a
+    cache-evicting fill runs before every timed launch (outside its events).
+    Returns (per-launch ms list, wall ms of the timed region without flushes
+    or None)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * iters)]
+    t0 = time.perf_counter()
+    for i in range(iters):
+        if flush is not None:
+            flush()
+        evs[2 * i].record()
+        fn()
+        evs[2 * i + 1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 if flush is None else None
+    return [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(iters)], wall
 
 
-def time_ring(api, torch, w, x, steps, warmup):
-    """Times `steps` ring passes over all query ranks; returns (ms_per_step, launches/step)."""
-    P = w.P
-    qs, kp, vp = x["q"], x["k"], x["v"]
-    B, H, n, d = qs.shape[1:]
-    o = torch.empty((B, H, n, d), dtype=qs.dtype, device="cuda")     # bf16 in -> bf16 out, fp32 -> fp32
+def ms_stats(ts):
+    return {"ms_mean": round(sum(ts) / len(ts), 4), "ms_median": round(statistics.median(ts), 4),
+            "ms_min": round(min(ts), 4), "launches_timed": len(ts)}
+
+
+def attn_roofline(name, flops_per_launch, ts, kernel="attn_bf16_kernel<128, false>"):
+    """Roofline object of one attention launch: algorithmic FLOPs over the mean
+    launch time (events), with HBM traffic and MFMA-busy counters from the
+    committed rocprofv3 summaries when they match the current kernel code."""
+    mean = sum(ts) / len(ts)
+    achieved = flops_per_launch / (mean * 1e-3) / 1e12
+    tr_file, mf_file = ATTN_COUNTERS.get(name, (None, None))
+    traffic = load_profile(tr_file, ATTN_SRC) if tr_file else None
+    mfma = load_profile(mf_file, ATTN_SRC) if mf_file else None
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None if traffic is None else traffic.get("bytes_per_launch"),
+            "traffic_algorithmic": None if traffic is None else traffic.get("algorithmic_bytes_per_launch"),
+            "kernel": kernel, "flops_per_launch": flops_per_launch,
+            "launch_ms": round(mean, 4), "launch_ms_median": round(statistics.median(ts), 4),
+            "mfma_busy_pct_counters": None if mfma is None else mfma.get("MfmaUtil_pct")}
+
+
+# ---------------------------------------------------------------------------
+# headline: rank 7's share of the causal 128k ring
+# ---------------------------------------------------------------------------
+def headline(api, torch, args):
+    from sequence_kv_chunk_amd.synth import WORKLOADS, device_attention_inputs
+    w = WORKLOADS[HEADLINE]
+    x = device_attention_inputs(w)
+    rank = w.query_ranks[0]
+    q, kp, vp = x["q"][0], x["k"], x["v"]
+    B, H, n, d = q.shape
+    o = torch.empty((B, H, n, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(B * H * n, dtype=torch.float32, device="cuda")
-    ranks = w.query_ranks
+    torch.cuda.synchronize()
+    log(f"workload {w.name}: inputs resident ({sum(t.numel() * 2 for t in x.values()) / 2**30:.2f} GiB)")
 
     def step():
-        for idx, i in enumerate(ranks):
-            api.ra_ring_attention(qs[idx], kp, vp, o, lse, rank=i, scale=1.0, causal=w.causal)
+        api.ra_ring_attention(q, kp, vp, o, lse, rank=rank, scale=1.0, causal=True)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
-    gpu = ev0.elapsed_time(ev1) / steps
-    launches = len(ranks)           # one ra_ring_attention launch per virtual rank
-    return wall, gpu, launches
+    ts, wall = timed_launches(torch, step, args.warmup, args.steps)
+    ms_step = wall / args.steps
+    flops = w.flops()
+    value = flops / (ms_step * 1e-3) / 1e12
+    roof = attn_roofline(w.name, flops, ts)
+    log(f"{w.name}: step {ms_step:.3f} ms (wall), launches mean {roof['launch_ms']:.3f} / median "
+        f"{roof['launch_ms_median']:.3f} ms, {value:.1f} TFLOP/s, roofline frac {roof['frac']}")
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) on device; Q scaled by d^-0.5)",
+        "config": {"workload": "ring_bf16_128k_rank7_causal: one GPU's share of the causal 131072-token ring, "
+                               "rank 7 of 8 (query chunk of 16384 tokens, positions 114688..131071) against the "
+                               "8 resident KV chunks of 16384 in ring order (1 diagonal + 7 full blocks), B=1, "
+                               "32 heads, d=128, one launch per step",
+                   "global_batch": 1, "seq_len": w.L, "heads": w.Hq, "head_dim": w.d, "chunks": w.P,
+                   "query_rank": rank, "causal": True, "parallelism": "single GPU; one virtual rank's share"},
+        "roofline": roof,
+    }
+    return result, (w, x, o, lse)
+
+
+def host_facts():
+    """CPU model, BLAS library and the cores this process may run on."""
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:
+        pass
+    return model, cores, blas
+
+
+def cpu_baseline(w, x, o, lse, torch, rows_per_head=512):
+    """The fp64 oracle on a seeded sample of the headline workload: in every
+    head, `rows_per_head` query rows evenly spaced over the chunk (the first
+    and the last included) against every key each row sees.  Its time is
+    extrapolated to the whole share by the count of visible (query, key)
+    pairs; the GPU output on the sampled rows is compared with it."""
+    import oracle
+    from sequence_kv_chunk_amd.synth import bf16_bits_to_f64
+    from threadpoolctl import threadpool_limits
+
+    def bits(t):
+        return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    model, cores, blas = host_facts()
+    rank, n, P, H, d = w.query_ranks[0], w.n, w.P, w.Hq, w.d
+    rows = np.unique(np.linspace(0, n - 1, rows_per_head).round().astype(np.int64))
+    q_pos = rank * n + rows
+    k_pos = np.arange(w.L)
+    o_rows = o[0][:, rows].float().cpu().numpy().astype(np.float64)            # [H, r, d]
+    l_rows = lse.view(H, n)[:, rows].cpu().numpy().astype(np.float64)          # [H, r]
+    secs, err_o, err_l = 0.0, 0.0, 0.0
+    with threadpool_limits(limits=cores):
+        for h in range(H):
+            qh = bf16_bits_to_f64(bits(x["q"][0][:, h:h + 1, rows]))                     # [1, 1, r, d]
+            kf = bf16_bits_to_f64(bits(x["k"][:, :, h])).reshape(1, 1, P * n, d)         # chunks in order
+            vf = bf16_bits_to_f64(bits(x["v"][:, :, h])).reshape(1, 1, P * n, d)
+            t0 = time.perf_counter()
+            ref_o, ref_l = oracle.attention_at_positions_fp64(qh, kf, vf, q_pos, k_pos)
+            secs += time.perf_counter() - t0
+            err_o = max(err_o, float(np.max(np.abs(ref_o[0, 0] - o_rows[h]))))
+            err_l = max(err_l, float(np.max(np.abs(ref_l[0, 0] - l_rows[h]))))
+    pairs_sample = int(np.sum(q_pos + 1)) * H
+    full_pairs = w.unmasked_pairs()
+    flops_sample = 4 * d * pairs_sample
+    return {"value": round(flops_sample / secs / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows.size} query rows per head (evenly spaced over rank 7's chunk, first and last "
+                      f"included) x {H} heads = {rows.size * H} rows, each against all of its visible keys "
+                      f"(up to {w.L}); fp64 numpy oracle",
+            "sample_seconds": round(secs, 2),
+            "full_share_seconds_extrapolated": round(secs * full_pairs / pairs_sample, 1),
+            "extrapolation": "sample time x visible pairs of the whole share / visible pairs of the sample",
+            "cpu_model": model, "blas": blas, "threads": cores,
+            "gpu_max_abs_err_on_sample": {"O": float(f"{err_o:.3e}"), "lse": float(f"{err_l:.3e}")}}
+
+
+# ---------------------------------------------------------------------------
+# extras
+# ---------------------------------------------------------------------------
+def bench_ring32k(api, torch, warmup=3, iters=10):
+    """The whole 32k ring: 8 virtual ranks, each a 4096-row query chunk against
+    all 8 resident KV chunks (one launch per rank), 32 heads, non-causal."""
+    from sequence_kv_chunk_amd.synth import WORKLOADS, device_attention_inputs
+    w = WORKLOADS["ring_bf16_32k"]
+    x = device_attention_inputs(w)
+    qs, kp, vp = x["q"], x["k"], x["v"]
+    B, H, n, d = qs.shape[1:]
+    o = torch.empty((B, H, n, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B * H * n, dtype=torch.float32, device="cuda")
+    launches = []
+    for r in range(w.P):
+        ts, _ = timed_launches(torch, lambda: api.ra_ring_attention(qs[r], kp, vp, o, lse, rank=r, scale=1.0),
+                               warmup if r == 0 else 1, iters)
+        launches += ts
+    ring_ms = sum(launches) / len(launches) * w.P
+    res = {"ring_ms": round(ring_ms, 4), "TFLOP/s": round(w.flops() / (ring_ms * 1e-3) / 1e12, 1),
+           "flops": w.flops(), "roofline": attn_roofline(w.name, w.flops() // w.P, launches),
+           "workload": "ring_bf16_32k: 32768 tokens as 8 chunks of 4096, all 8 query chunks x 8 resident KV "
+                       "chunks, B=1, 32 heads, d=128, non-causal (one launch per rank)"}
+    del x, o, lse
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_ulysses_share(api, torch, warmup=3, iters=10):
+    """One Ulysses share: causal attention over 131072 tokens, 4 query heads
+    on 1 key/value head, [S, H, d] layout, fp32 lse; one launch."""
+    from sequence_kv_chunk_amd.synth import WORKLOADS, device_attention_inputs
+    w = WORKLOADS["ulysses_share_gqa_128k_causal"]
+    x = device_attention_inputs(w)
+    o = torch.empty((w.L, w.Hq, w.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(w.Hq * w.L, dtype=torch.float32, device="cuda")
+    ts, _ = timed_launches(torch, lambda: api.ra_chunk_attention(x["q"], x["k"], x["v"], o, lse, scale=1.0,
+                                                                 causal=True), warmup, iters)
+    res = dict(ms_stats(ts))
+    res.update({"TFLOP/s": round(w.flops() / (res["ms_mean"] * 1e-3) / 1e12, 1), "flops": w.flops(),
+                "roofline": attn_roofline(w.name, w.flops(), ts),
+                "workload": "ulysses_share_gqa_128k_causal: L=131072, 4 query heads, 1 KV head, d=128, causal, "
+                            "[S, H, d] layout, one launch"})
+    del x, o, lse
+    torch.cuda.empty_cache()
+    return res
+
+
+def _flush_fill(torch):
+    buf = torch.empty(768 << 20, dtype=torch.uint8, device="cuda")     # > 256 MiB last-level cache
+    return buf, (lambda: buf.fill_(1))
 
 
 def bench_ulysses(api, torch, iters=10):
     """Ulysses seq->head and head->seq on 8 shards of [16384, 32, 128] bf16.
-    Every launch is timed on its own with HIP events on the stream it runs on,
-    after a 768 MiB fill that evicts the 256 MiB last-level cache, so each
-    launch reads from HBM.  A plain device copy of the same bytes, timed the
-    same way, gives the streaming ceiling the permute is held against."""
+    Every launch is timed on its own with HIP events on the stream it runs
+    on, after a 768 MiB fill that evicts the 256 MiB last-level cache, so each
+    launch reads from HBM.  The same kernel run as a plain copy of the same
+    bytes (P = 1: every token's 32 heads are one contiguous 8 KiB run, so the
+    permutation is the identity) is the streaming ceiling it is held
+    against; torch's copy_ is shown beside it."""
     from sequence_kv_chunk_amd.synth import ULYSSES_WORKLOADS, device_ulysses_input
     w = ULYSSES_WORKLOADS["ulysses_131k_32h"]
     src = device_ulysses_input(w)
     mid = torch.empty((w.P, w.L, w.H // w.P, w.d), dtype=torch.bfloat16, device="cuda")
     back = torch.empty_like(src)
-    flush = torch.empty(768 << 20, dtype=torch.uint8, device="cuda")   # > 256 MiB MALL
+    buf, flush = _flush_fill(torch)
     nbytes = w.bytes_per_direction()
-
-    def timed(fn):
-        fn()
-        ts = []
-        for _ in range(iters):
-            flush.zero_()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return ts
-
+    gbs = lambda ms: nbytes / (ms * 1e-3) / 1e9
     res = {}
     for name, fn in (("seq_to_head", lambda: api.ulysses_seq_to_head(src, mid)),
                      ("head_to_seq", lambda: api.ulysses_head_to_seq(mid, back))):
-        ts = timed(fn)
-        avg = sum(ts) / len(ts)
-        ts.sort()
-        res[name] = {"ms_avg": round(avg, 4), "ms_median": round(ts[len(ts) // 2], 4), "ms_min": round(ts[0], 4),
-                     "GB/s": round(nbytes / (avg * 1e-3) / 1e9, 1),
-                     "frac_hbm": round(nbytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        ts, _ = timed_launches(torch, fn, 1, iters, flush)
+        st = ms_stats(ts)
+        res[name] = {**st, "GB/s": round(gbs(st["ms_mean"]), 1), "frac_hbm": round(gbs(st["ms_mean"]) / PEAK_HBM_GBS, 4)}
     torch.cuda.synchronize()
     ok = bool(torch.equal(back.view(torch.int16), src.view(torch.int16)))
-    copy_ts = timed(lambda: back.copy_(src))
-    copy_avg = sum(copy_ts) / len(copy_ts)
-    res["plain_copy_same_bytes"] = {"ms_avg": round(copy_avg, 4),
-                                    "GB/s": round(nbytes / (copy_avg * 1e-3) / 1e9, 1),
-                                    "kernel": "torch copy_ of 1 GiB (read 1 GiB + write 1 GiB)"}
+    one = src.view(1, w.L, w.H, w.d)
+    dst1 = back.view(1, w.L, w.H, w.d)
+    ts, _ = timed_launches(torch, lambda: api.ulysses_seq_to_head(one, dst1), 1, iters, flush)
+    st = ms_stats(ts)
+    res["plain_copy_same_kernel"] = {**st, "GB/s": round(gbs(st["ms_mean"]), 1),
+                                     "kernel": "permute_kernel<16, 0> with P=1 (identity): a linear copy of 1 GiB "
+                                               "in the permute's launch shape"}
+    ts, _ = timed_launches(torch, lambda: back.copy_(src), 1, iters, flush)
+    st = ms_stats(ts)
+    res["torch_copy_same_bytes"] = {**st, "GB/s": round(gbs(st["ms_mean"]), 1)}
     res["round_trip_bit_exact"] = ok
     res["workload"] = "ulysses_131k_32h: 8 shards [16384, 32, 128] bf16 <-> [131072, 4, 128]"
     res["bytes_per_direction"] = nbytes
-    prof = load_profile(PERMUTE_TRAFFIC_FILE, PERMUTE_SRC)
-    both_ms = (res["seq_to_head"]["ms_avg"] + res["head_to_seq"]["ms_avg"]) / 2
-    achieved = nbytes / (both_ms * 1e-3) / 1e9
+    prof = load_profile(os.path.basename(PERMUTE_TRAFFIC_FILE), PERMUTE_SRC)
+    both_ms = (res["seq_to_head"]["ms_mean"] + res["head_to_seq"]["ms_mean"]) / 2
+    achieved = gbs(both_ms)
     res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                        "frac": round(achieved / PEAK_HBM_GBS, 4),
                        "traffic": None if prof is None else prof.get("bytes_per_launch"),
                        "kernel": "permute_kernel<16, *> (seq->head and head->seq, mean of the two)",
-                       "bytes_per_launch": nbytes, "launch_ms": round(both_ms, 4)}
-    del src, mid, back, flush
+                       "bytes_per_launch": nbytes, "launch_ms": round(both_ms, 4),
+                       "frac_of_same_kernel_copy": round(achieved / res["plain_copy_same_kernel"]["GB/s"], 4)}
+    del src, mid, back, buf
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_gqa_replication(api, torch, iters=10):
+    """The Ulysses exchange of the key/value heads with GQA: [8][16384][H_kv][128]
+    bf16 shards become [8][131072][1][128] (every key/value head copied up to
+    the 8 ranks), H_kv in {1, 2}.  Bytes = read once + written 8/H_kv times;
+    each launch after a cache-evicting fill."""
+    P, L, d = 8, 131072, 128
+    buf, flush = _flush_fill(torch)
+    res = {}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    for H_kv in (1, 2):
+        src = torch.randn((P, L // P, H_kv, d), generator=g, device="cuda").to(torch.bfloat16)
+        dst = torch.empty((P, L, 1, d), dtype=torch.bfloat16, device="cuda")
+        fn = lambda: api.ulysses_seq_to_head(src, dst, H_dst=P)
+        ts, _ = timed_launches(torch, fn, 1, iters, flush)
+        nbytes = src.numel() * 2 + dst.numel() * 2
+        st = ms_stats(ts)
+        achieved = nbytes / (st["ms_mean"] * 1e-3) / 1e9
+        prof = load_profile(os.path.basename(REPLICATION_TRAFFIC_FILE), PERMUTE_SRC)
+        tr = None if prof is None else prof.get("bytes_per_launch", {}).get(f"H_kv={H_kv}")
+        res[f"H_kv={H_kv}"] = {**st, "copies_per_head": P // H_kv, "bytes_per_launch": nbytes,
+                               "GB/s": round(achieved, 1),
+                               "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                                            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                                            "traffic": tr, "kernel": "replicate_kernel<16>"}}
+        del src, dst
+    res["workload"] = ("GQA key/value exchange: 8 shards [16384, H_kv, 128] bf16 -> [131072, 1, 128] per rank "
+                       "(H_dst = 8), L = 131072")
+    del buf
     torch.cuda.empty_cache()
     return res
 
@@ -187,34 +407,33 @@ def bench_lse_merge(api, torch, iters=10):
     lb = torch.randn((B * H * n,), generator=g, device="cuda")
     oo = torch.empty_like(oa)
     lo = torch.empty_like(la)
-    flush = torch.empty(768 << 20, dtype=torch.uint8, device="cuda")
-    api.ra_lse_merge(oa, la, ob, lb, oo, lo)
-    ts = []
-    for _ in range(iters):
-        flush.zero_()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        api.ra_lse_merge(oa, la, ob, lb, oo, lo)
-        e1.record()
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1))
-    avg = sum(ts) / len(ts)
+    buf, flush = _flush_fill(torch)
+    ts, _ = timed_launches(torch, lambda: api.ra_lse_merge(oa, la, ob, lb, oo, lo), 1, iters, flush)
+    st = ms_stats(ts)
     nbytes = 3 * (B * H * n * d * 4 + B * H * n * 4)
-    gbs = nbytes / (avg * 1e-3) / 1e9
-    del oa, ob, la, lb, oo, lo, flush
+    gbs = nbytes / (st["ms_mean"] * 1e-3) / 1e9
+    del oa, ob, la, lb, oo, lo, buf
     torch.cuda.empty_cache()
-    return {"ms_avg": round(avg, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
-            "bytes": nbytes, "workload": "lse merge of two fp32 partials [1, 32, 16384, 128] + lse (one 128k ring step)"}
+    return {**st, "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes,
+            "workload": "lse merge of two fp32 partials [1, 32, 16384, 128] + lse (one 128k ring step)"}
 
 
-def bench_f32_tiny(api, torch, steps=20):
+def bench_f32_tiny(api, torch, iters=20):
     """The tiny fp32 ring (4 virtual ranks x 4 chunks of 256, 4 heads, d=64):
     a correctness workload; its time is reported, not held against a roofline."""
     from sequence_kv_chunk_amd.synth import WORKLOADS, device_attention_inputs
     w = WORKLOADS["ring_f32_tiny"]
     x = device_attention_inputs(w)
-    _, ms, launches = time_ring(api, torch, w, x, steps, 2)
-    return {"ms": round(ms, 4), "launches": launches, "flops": w.flops(),
+    qs, kp, vp = x["q"], x["k"], x["v"]
+    o = torch.empty(qs.shape[1:], dtype=torch.float32, device="cuda")
+    lse = torch.empty(o.numel() // o.shape[-1], dtype=torch.float32, device="cuda")
+
+    def step():
+        for r in range(w.P):
+            api.ra_ring_attention(qs[r], kp, vp, o, lse, rank=r)
+
+    ts, _ = timed_launches(torch, step, 2, iters)
+    return {"ms": round(sum(ts) / len(ts), 4), "launches": w.P, "flops": w.flops(),
             "workload": "ring_f32_tiny: fp32, B=1, 4 heads, d=64, L=1024 as 4 chunks of 256, all 4 ranks"}
 
 
@@ -236,12 +455,8 @@ def bench_capacity_1m(api, torch):
     api.ra_chunk_attention(q, k, v, o, lse, scale=1.0, causal=True)
     torch.cuda.synchronize()
     extra = free0 - torch.cuda.mem_get_info()[0]
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    api.ra_chunk_attention(q, k, v, o, lse, scale=1.0, causal=True)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
+    ts, _ = timed_launches(torch, lambda: api.ra_chunk_attention(q, k, v, o, lse, scale=1.0, causal=True), 0, 1)
+    ms = ts[0]
     flops = 4 * d * Hq * (L * (L + 1) // 2)
     io_bytes = sum(t.numel() * t.element_size() for t in (q, k, v, o, lse))
     del q, k, v, o, lse
@@ -253,33 +468,7 @@ def bench_capacity_1m(api, torch):
             "workload": "causal attention, 1048576 tokens, 4 q heads, 1 kv head, d=128, bf16, one call"}
 
 
-def bench_attention_extra(api, torch, name, steps=3):
-    from sequence_kv_chunk_amd.synth import WORKLOADS, device_attention_inputs
-    w = WORKLOADS[name]
-    x = device_attention_inputs(w)
-    if w.layout == "shd":
-        o = torch.empty((w.L, w.Hq, w.d), dtype=torch.bfloat16, device="cuda")
-        lse = torch.empty(w.Hq * w.L, dtype=torch.float32, device="cuda")
-        fn = lambda: api.ra_chunk_attention(x["q"], x["k"], x["v"], o, lse, scale=1.0, causal=w.causal)
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
-    else:
-        _, ms, _ = time_ring(api, torch, w, x, steps, 1)
-    tf = w.flops() / (ms * 1e-3) / 1e12
-    del x
-    torch.cuda.empty_cache()
-    return {"ms": round(ms, 3), "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4),
-            "flops": w.flops()}
-
-
-def bench_causal_split(api, torch, steps=2):
+def bench_causal_split(api, torch, iters=2):
     """The whole causal 128k ring (8 ranks x chunks of 16384, 32 heads) under the
     contiguous split and under the zigzag split: per-rank launch time, the sum
     (the ring on one GPU) and the slowest rank (what bounds a step when every
@@ -300,14 +489,8 @@ def bench_causal_split(api, torch, steps=2):
                 fn = lambda: api.ra_zigzag_attention(x["q"][r], x["k"], x["v"], o, lse, rank=r, work=work)
             else:
                 fn = lambda: api.ra_ring_attention(x["q"][r], x["k"], x["v"], o, lse, rank=r, causal=True)
-            fn()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(steps):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            rank_ms.append(e0.elapsed_time(e1) / steps)
+            ts, _ = timed_launches(torch, fn, 1, iters)
+            rank_ms.append(sum(ts) / len(ts))
         tot = sum(rank_ms)
         res[split] = {"rank_ms": [round(t, 3) for t in rank_ms], "ring_ms_one_gpu": round(tot, 3),
                       "slowest_rank_ms": round(max(rank_ms), 3),
@@ -322,11 +505,14 @@ def bench_causal_split(api, torch, steps=2):
     return res
 
 
-def bench_backward(api, torch, x, w, steps=2):
+def bench_backward(api, torch, iters=2):
     """Backward of the 32k ring: for every rank the D preprocess and the ring
     backward (dQ of the rank, its share of every chunk's dK, dV).  TFLOP/s
     counts 10*d per visible pair (scores recomputed, dV, dP, dQ, dK); the
     kernels do 14*d (the dK/dV kernel recomputes the scores and dP)."""
+    from sequence_kv_chunk_amd.synth import WORKLOADS, device_attention_inputs
+    w = WORKLOADS["ring_bf16_32k"]
+    x = device_attention_inputs(w)
     qs, kp, vp = x["q"], x["k"], x["v"]
     P = w.P
     B, H, n, d = qs.shape[1:]
@@ -347,25 +533,18 @@ def bench_backward(api, torch, x, w, steps=2):
             api.ra_attention_bwd_preprocess(o[r], dout[r], D[r])
             api.ra_ring_attention_bwd(qs[r], kp, vp, dout[r], lse[r], D[r], dq, dk, dv, rank=r, causal=w.causal)
 
-    step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ts, _ = timed_launches(torch, step, 1, iters)
+    ms = sum(ts) / len(ts)
     flops = w.flops() // 4 * 10
     res = {"ms": round(ms, 3), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1),
            "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "flops_10d": flops,
            "workload": "backward of ring_bf16_32k (all 8 ranks: D preprocess + ring backward)"}
-    del dout, o, lse, D, dq, dk, dv
+    del x, dout, o, lse, D, dq, dk, dv
     torch.cuda.empty_cache()
     return res
 
 
-def bench_usp(api, torch, steps=2):
+def bench_usp(api, torch, iters=2):
     """USP hybrid at 128k: 8 virtual ranks as Ulysses groups of P_u inside a
     ring of P_r = 8 / P_u groups; B=1, 32 query heads, 8 key/value heads,
     d=128, causal, bf16.  One call runs all 8 ranks' work (permutes in,
@@ -381,25 +560,21 @@ def bench_usp(api, torch, steps=2):
     flops = 4 * d * H * (L * (L + 1) // 2)
     res = {"workload": "USP causal, L=131072, 32 q heads, 8 kv heads, d=128, 8 virtual ranks", "flops": flops}
     for P_u in (4, 2):
-        api.usp_attention(q, k, v, o, P_u=P_u, causal=True)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            api.usp_attention(q, k, v, o, P_u=P_u, causal=True)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
+        ts, _ = timed_launches(torch, lambda: api.usp_attention(q, k, v, o, P_u=P_u, causal=True), 1, iters)
+        ms = sum(ts) / len(ts)
         res[f"P_u={P_u},P_r={P // P_u}"] = {"ms": round(ms, 3), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)}
     del q, k, v, o
     torch.cuda.empty_cache()
     return res
 
 
-def bench_packed(api, torch, x, w, sample_len=2048, steps=2):
+def bench_packed(api, torch, sample_len=2048, iters=3):
     """The 32k ring with the sequence packing samples of `sample_len` tokens
     (causal inside each sample, samples blind to each other).  TFLOP/s counts
     the visible pairs only."""
+    from sequence_kv_chunk_amd.synth import WORKLOADS, device_attention_inputs
+    w = WORKLOADS["ring_bf16_32k"]
+    x = device_attention_inputs(w)
     qs, kp, vp = x["q"], x["k"], x["v"]
     P = w.P
     B, H, n, d = qs.shape[1:]
@@ -412,18 +587,14 @@ def bench_packed(api, torch, x, w, sample_len=2048, steps=2):
         for r in range(P):
             api.ra_ring_attention_packed(qs[r], kp, vp, o, lse, starts, rank=r)
 
-    step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ts, _ = timed_launches(torch, step, 1, iters)
+    ms = sum(ts) / len(ts)
     pairs = (L // sample_len) * sample_len * (sample_len + 1) // 2
     flops = 4 * d * pairs * B * H
-    return {"ms": round(ms, 3), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1), "flops": flops,
+    del x, o, lse
+    torch.cuda.empty_cache()
+    return {"ms": round(ms, 3), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "flops": flops,
             "workload": f"ring_bf16_32k packing {L // sample_len} causal samples of {sample_len} tokens"}
 
 
@@ -449,46 +620,43 @@ def cpu_baseline_ulysses(torch):
     return res
 
 
-def cpu_baseline(x_dev, w, torch, budget_rows=4096, heads=16):
-    """The fp64 oracle on a bounded sample of the workload: query chunk 0
-    (4096 rows) of the first `heads` heads against all 32768 keys."""
-    import oracle
-    from sequence_kv_chunk_amd.synth import bf16_bits_to_f64
-
-    def bits(t):
-        return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
-
-    q = bf16_bits_to_f64(bits(x_dev["q"][0][:, :heads, :budget_rows]))          # [B, h, rows, d]
-    kp = bf16_bits_to_f64(bits(x_dev["k"][:, :, :heads]))                          # [P, B, h, n, d]
-    vp = bf16_bits_to_f64(bits(x_dev["v"][:, :, :heads]))
-    P, B, h, n, d = kp.shape
-    k = kp.transpose(1, 2, 0, 3, 4).reshape(B, h, P * n, d)
-    v = vp.transpose(1, 2, 0, 3, 4).reshape(B, h, P * n, d)
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    t0 = time.perf_counter()
-    oracle.attention_fp64(q, k, v, scale=1.0, causal=False)
-    dt = time.perf_counter() - t0
-    flops = 4 * d * (P * n) * budget_rows * heads * B
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"query rows 0..{budget_rows - 1} (chunk 0) of heads 0..{heads - 1} against all "
-                      f"{P * n} keys, fp64 numpy oracle, {dt:.1f} s",
-            "seconds": round(dt, 2)}
+def run_extras(api, torch, chosen):
+    """The other workloads' figures; a failure here never hides the main line."""
+    extras = {}
+    runs = (("ring32k", "ring_bf16_32k", lambda: bench_ring32k(api, torch)),
+            ("ulysses_share", "ulysses_share_gqa_128k_causal", lambda: bench_ulysses_share(api, torch)),
+            ("ulysses", "ulysses", lambda: bench_ulysses(api, torch)),
+            ("gqa_replication", "ulysses_gqa_replication_128k", lambda: bench_gqa_replication(api, torch)),
+            ("packed", "ring_bf16_32k_packed_2k", lambda: bench_packed(api, torch)),
+            ("backward", "ring_bf16_32k_backward", lambda: bench_backward(api, torch)),
+            ("causal_split", "causal_128k_ring_split", lambda: bench_causal_split(api, torch)),
+            ("usp", "usp_128k_causal", lambda: bench_usp(api, torch)),
+            ("lse_merge", "lse_merge_128k_step", lambda: bench_lse_merge(api, torch)),
+            ("f32_tiny", "ring_f32_tiny", lambda: bench_f32_tiny(api, torch)),
+            ("capacity_1m", "capacity_1m_causal", lambda: bench_capacity_1m(api, torch)))
+    for key, name, fn in runs:
+        if key not in chosen:
+            continue
+        try:
+            extras[name] = fn()
+            log(f"{name}: {extras[name]}")
+        except Exception as e:        # report and go on: the headline is already measured
+            extras[name] = {"error": repr(e)}
+            log(f"{name}: error {e!r}")
+            torch.cuda.empty_cache()
+    return extras
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads' figures")
     ap.add_argument("--extras", default="all",
                     help="comma-separated subset of " + ",".join(EXTRAS) + " (default: all)")
     ap.add_argument("--only-extras", action="store_true",
-                    help="skip the ring and the CPU baseline; print the chosen extras only (for profiling)")
+                    help="skip the headline and the CPU baseline; print the chosen extras only (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
@@ -500,7 +668,6 @@ def main():
 
     import torch
     from sequence_kv_chunk_amd import api
-    from sequence_kv_chunk_amd.synth import WORKLOADS, device_attention_inputs
 
     chosen = () if args.no_extras else (EXTRAS if args.extras == "all" else tuple(args.extras.split(",")))
     unknown = [e for e in chosen if e not in EXTRAS]
@@ -515,88 +682,23 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    w = WORKLOADS["ring_bf16_32k"]
-    x = device_attention_inputs(w)
-    torch.cuda.synchronize()
-    log(f"workload {w.name}: inputs resident ({sum(t.numel() * 2 for t in x.values()) / 2**30:.2f} GiB)")
-
     result = {}
     if not args.only_extras:
-        result = ring_result(api, torch, w, x, args)
-    extras = run_extras(api, torch, w, x, chosen)
-    if not args.no_cpu and not args.only_extras:
-        result["cpu_baseline"] = cpu_baseline(x, w, torch)
-        log(f"cpu baseline: {result['cpu_baseline']}")
+        result, kept = headline(api, torch, args)
+        if not args.no_cpu:
+            result["cpu_baseline"] = cpu_baseline(*kept, torch)
+            log(f"cpu baseline: {result['cpu_baseline']}")
+        else:
+            result["cpu_baseline"] = None
+        del kept
+        torch.cuda.empty_cache()
+    extras = run_extras(api, torch, chosen)
+    if not args.no_cpu and not args.only_extras and "ulysses" in chosen:
         extras["cpu_oracle_ulysses"] = cpu_baseline_ulysses(torch)
         log(f"cpu oracle ulysses: {extras['cpu_oracle_ulysses']}")
-    elif not args.only_extras:
-        result["cpu_baseline"] = None
     if extras:
         result["extras"] = extras
     print(json.dumps(result), flush=True)
-
-
-def ring_result(api, torch, w, x, args):
-    """The headline line: the 32k ring step, its throughput and the roofline
-    of the chunk-attention kernel."""
-    wall_ms, gpu_ms, launches = time_ring(api, torch, w, x, args.steps, args.warmup)
-    flops = w.flops()
-    value = flops / (wall_ms * 1e-3) / 1e12
-    per_launch_flops = flops // launches
-    launch_ms = gpu_ms / launches      # the timed region holds only chunk-attention launches
-    achieved = per_launch_flops / (launch_ms * 1e-3) / 1e12
-    traffic = load_traffic()
-    mfma = load_profile(MFMA_FILE, ATTN_SRC)
-    log(f"ring step {wall_ms:.3f} ms (events {gpu_ms:.3f} ms), {value:.1f} TFLOP/s, "
-        f"{launches} launches of {launch_ms:.4f} ms")
-    return {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(wall_ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) on device; Q scaled by d^-0.5)",
-        "config": {"workload": "ring_bf16_32k: 32768 tokens as 8 chunks of 4096, all 8 query chunks x 8 "
-                               "resident KV chunks, B=1, 32 heads, d=128, non-causal",
-                   "global_batch": 1, "seq_len": w.L, "heads": w.Hq, "head_dim": w.d, "chunks": w.P,
-                   "parallelism": "single GPU; 8 virtual ranks"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "attn_bf16_kernel<128, false>", "flops_per_launch": per_launch_flops,
-                     "launch_ms": round(launch_ms, 4),
-                     "mfma_busy_pct_counters": None if mfma is None else mfma.get("MfmaUtil_pct")},
-    }
-
-
-def run_extras(api, torch, w, x, chosen):
-    """The other workloads' figures; a failure here never hides the main line."""
-    extras = {}
-    runs = (("packed", "ring_bf16_32k_packed_2k", lambda: bench_packed(api, torch, x, w)),
-            ("backward", "ring_bf16_32k_backward", lambda: bench_backward(api, torch, x, w)),
-            ("ulysses", "ulysses", lambda: bench_ulysses(api, torch)),
-            ("rank7", "ring_bf16_128k_rank7_causal",
-             lambda: bench_attention_extra(api, torch, "ring_bf16_128k_rank7_causal")),
-            ("ulysses_share", "ulysses_share_gqa_128k_causal",
-             lambda: bench_attention_extra(api, torch, "ulysses_share_gqa_128k_causal")),
-            ("causal_split", "causal_128k_ring_split", lambda: bench_causal_split(api, torch)),
-            ("usp", "usp_128k_causal", lambda: bench_usp(api, torch)),
-            ("lse_merge", "lse_merge_128k_step", lambda: bench_lse_merge(api, torch)),
-            ("f32_tiny", "ring_f32_tiny", lambda: bench_f32_tiny(api, torch)),
-            ("capacity_1m", "capacity_1m_causal", lambda: bench_capacity_1m(api, torch)))
-    try:
-        for key, name, fn in runs:
-            if key in chosen:
-                extras[name] = fn()
-                log(f"{name}: {extras[name]}")
-    except Exception as e:
-        extras["error"] = repr(e)
-    return extras
 
 
 if __name__ == "__main__":

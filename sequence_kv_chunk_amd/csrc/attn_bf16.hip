@@ -71,6 +71,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
@@ -99,7 +100,14 @@ struct Cfg {
   static constexpr int K_LDS = 0;                        // kStages K tiles
   static constexpr int V_LDS = kStages * TILE;           // kStages V tiles
   static constexpr int LDS_BYTES = 2 * kStages * TILE;
-  static constexpr int LDS_ALLOC = LDS_BYTES + 16;      // + the workgroup's redo flag
+  // epilogue staging, one region per wave: its 32 output rows as fp32 at a
+  // padded pitch (rows 16 bytes apart in bank terms), then the rows' merge
+  // weights; it reuses the K/V stages once the visit's last LDS read is done
+  static constexpr int STAGE_PITCH = D * 4 + 16;
+  static constexpr int STAGE_WAVE = kQW * STAGE_PITCH + kQW * 4;
+  static constexpr int STAGE_BYTES = kWaves * STAGE_WAVE;
+  static constexpr int FLAG_OFS = LDS_BYTES > STAGE_BYTES ? LDS_BYTES : STAGE_BYTES;
+  static constexpr int LDS_ALLOC = FLAG_OFS + 16;       // + the workgroup's redo flag
   // every wave issues the same number of loads per tile, so that its vmcnt
   // bookkeeping is uniform
   static_assert(NL >= 1 && NLT % kWaves == 0, "tile loads must spread evenly over the waves");
@@ -215,20 +223,43 @@ __device__ __forceinline__ void static_for(F&& f) {
 template <int D, bool PACKED>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_bf16_kernel(AttnParams p, int n_qtiles) {
+attn_bf16_kernel(AttnParams params, int n_qtiles, int n_items) {
   using C = Cfg<D>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   // LDS offset of the dynamic allocation (no static LDS in this kernel)
   const uint32_t lds0 = (uint32_t)(size_t)(SQKV_LDS unsigned char*)smem;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // The grid holds one workgroup per CU and each workgroup walks its items
+  // (one (b, h, q-tile) visit each) in turn: workgroup g takes items g,
+  // 2G-1-g, 2G+g, 4G-1-g, ... of the G-wide rounds, so that in a list issued
+  // heaviest first a heavy item pairs with a light one.  A visit's output
+  // stores then drain while the next visit loads its Q and first tiles
+  // (measured: a visit of one 64-key tile took 20 us as a workgroup of its
+  // own, 8.5 us of it in the output stores).
+  const int G = gridDim.x;
+  for (int round = 0;; ++round) {
+  const int item = round * G + ((round & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+  if (item >= n_items) break;
+  // The parameters are read from the kernel argument segment through a
+  // pointer the compiler cannot see through, once per visit: otherwise it
+  // keeps every one of them in registers across all visits and spills.
+  typedef const __attribute__((address_space(4))) AttnParams KernArgParams;   // scalar-loadable
+  KernArgParams* pk_visit = (KernArgParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(pk_visit));
+  KernArgParams& p = *pk_visit;
+  // (likewise the lane's constants, recomputed per visit rather than held)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const int a16 = lane & 15;
 
-  // Workgroup -> (b, h, q-tile).  Workgroups are dealt round-robin to the 8
-  // XCDs, each with its own L2.  When every workgroup has about the same work
+  // Item -> (b, h, q-tile).  Item i runs on XCD i % 8 in even rounds and on
+  // XCD 7 - i % 8 in odd ones (workgroups are dealt round-robin to the 8
+  // XCDs, each with its own L2); the grouping below only needs the items of
+  // one round that share i % 8 to share an XCD.  When every workgroup has about the same work
   // (no mask, or a causal visit of several chunks, where the diagonal chunk
   // is a small part) the linear id is remapped so that each XCD walks a
   // contiguous range of (b, h, q-tile) with the q-tiles of one head adjacent,
@@ -236,18 +267,28 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   // share its L2 (causal: heaviest q-tile of the head first).  A causal visit
   // of one chunk grows with the q-tile: heads vary fastest (every XCD gets a
   // mix) and the q-tiles are issued heaviest first.  Packed samples keep that
-  // order too (measured: the remap is ~20% slower with 2k-token samples).
+  // order too (measured: the remap is ~20% slower with 2k-token samples).  In
+  // that order the `group` query heads that share a key/value head (GQA) are
+  // dealt to one XCD at consecutive slots, so that they stream the same key /
+  // value tiles through its L2 together: ids are permuted inside every run of
+  // 8*group (a tail shorter than that keeps its order).
   const int BH = p.B * p.Hq;
   int bh, qt;
   if (p.causal && (p.nseg < 2 || PACKED)) {
-    const int qt_rank = blockIdx.x / BH;
-    bh = blockIdx.x - qt_rank * BH;
+    const int span = 8 * p.group;
+    int lid = item;
+    if (lid < (n_items / span) * span) {
+      const int unit = (lid / span) * 8 + (lid & 7);   // (q-tile, key/value head), on XCD lid % 8
+      lid = unit * p.group + (lid >> 3) % p.group;
+    }
+    const int qt_rank = lid / BH;
+    bh = lid - qt_rank * BH;
     qt = n_qtiles - 1 - qt_rank;
   } else {
     constexpr int kXcds = 8;
-    const int per = gridDim.x / kXcds, rem = gridDim.x % kXcds;
-    const int xcd = blockIdx.x % kXcds;
-    const int logical = xcd * per + min(xcd, rem) + blockIdx.x / kXcds;
+    const int per = n_items / kXcds, rem = n_items % kXcds;
+    const int xcd = item % kXcds;
+    const int logical = xcd * per + min(xcd, rem) + item / kXcds;
     bh = logical / n_qtiles;
     qt = logical - bh * n_qtiles;
     if (p.causal) qt = n_qtiles - 1 - qt;
@@ -769,7 +810,7 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
   // are then the exact pass's up to the fp32 rounding of the exponent and a
   // factor 2^m common to a row, which the normalisation cancels.  Otherwise the whole workgroup (its waves
   // share the LDS pipeline) runs the exact pass with the running maximum.
-  volatile int* redo_flag = reinterpret_cast<volatile int*>(smem + C::LDS_BYTES);
+  volatile int* redo_flag = reinterpret_cast<volatile int*>(smem + C::FLAG_OFS);
   if (threadIdx.x == 0) *redo_flag = 0;
   if (T > 0) {
     run_pass(std::true_type{});
@@ -782,48 +823,101 @@ attn_bf16_kernel(AttnParams p, int n_qtiles) {
       for (int j = 0; j < 16; ++j) ok &= __builtin_isfinite(oacc[md][j]);
     if (__any(!ok) && lane == 0) *redo_flag = 1;
     lds_reads_done_sync();   // (the first barrier of the pass ordered the clearing before this)
-    if (*redo_flag != 0) run_pass(std::false_type{});
+    if (*redo_flag != 0) {
+      run_pass(std::false_type{});
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      lds_reads_done_sync();
+    }
   }
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no DMA may outlive the workgroup's LDS
+  // No DMA is in flight and no wave reads the K/V stages any more: the
+  // epilogue may stage its rows there.
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
   // ---- epilogue: normalise, merge into the running (O, lse), store ------------
   // The output parameters are read from the kernel argument segment here,
   // through a pointer the compiler cannot see through: otherwise it loads
-  // them at kernel entry and keeps ~20 scalar registers live across the loop.
+  // them early and keeps ~20 scalar registers live across the loop.
+  // A lane holds 64 of its row's d values in groups of four, so storing from
+  // the accumulators writes 8 or 16 bytes at a time scattered over 32 rows
+  // (measured: ~8 us per visit for a 256-row bf16 tile).  Instead each wave
+  // writes its rows, normalised, as fp32 into its own LDS region, reads them
+  // back in row order and stores whole rows: 32 lanes per row, 4 values each,
+  // merged there with the running (o_in) rows when present.
   {
     const AttnParams* pk = (const AttnParams*)__builtin_amdgcn_kernarg_segment_ptr();
     asm volatile("" : "+s"(pk));
     const AttnParams& pe = *pk;
     const int row = qw0 + l32;
     const float lt = sum_half(l_run);
+    const int64_t bh_row = (int64_t)b * pe.Hq + h;
+    float wi = 0.f, f = 0.f;
     if (row < pe.n_q) {
       const float lse_j = (lt > 0.f) ? (m_run + log2f(lt)) * kLn2 : kNegInf;
       const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
-      const int64_t bh_row = (int64_t)b * pe.Hq + h;
-      float wi = 0.f, wj = 1.f, lse = lse_j;
+      float wj = 1.f, lse = lse_j;
       if (pe.o_in != nullptr) lse = lse_merge_weights(pe.lse_in[bh_row * pe.lse_in_hs + row], lse_j, wi, wj);
-      const float f = wj * inv;
-      const int64_t ooff = b * pe.oo_sb + h * pe.oo_sh + (int64_t)row * pe.oo_sn;
-      const int64_t ioff = b * pe.oi_sb + h * pe.oi_sh + (int64_t)row * pe.oi_sn;
-#pragma unroll
-      for (int md = 0; md < C::MD; ++md)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = 32 * md + 8 * g + 4 * hi;
-          float y[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) y[r] = oacc[md][4 * g + r] * f;
-          if (pe.o_in != nullptr && wi != 0.f) {
-            float x[4];
-            load4(pe.o_in, ioff + d0, pe.acc_dtype, x);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) y[r] = fmaf(wi, x[r], y[r]);
-          }
-          store4(pe.o_out, ooff + d0, pe.out_dtype, y);
-        }
+      f = wj * inv;
       if (hi == 0) pe.lse_out[bh_row * pe.lse_out_hs + row] = lse;
     }
+    const lds_ptr stage = lds + wave * C::STAGE_WAVE;
+#pragma unroll
+    for (int md = 0; md < C::MD; ++md)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * md + 8 * g + 4 * hi;
+        const f32x4_t y = {oacc[md][4 * g] * f, oacc[md][4 * g + 1] * f, oacc[md][4 * g + 2] * f,
+                           oacc[md][4 * g + 3] * f};
+        *reinterpret_cast<SQKV_LDS f32x4_t*>(stage + l32 * C::STAGE_PITCH + d0 * 4) = y;
+      }
+    if (hi == 0) *reinterpret_cast<SQKV_LDS float*>(stage + kQW * C::STAGE_PITCH + l32 * 4) = wi;
+    // the wave's own LDS writes, complete before its lanes read each other's
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // D/4 lanes per row, 256/D rows per pass
+    constexpr int kLanesPerRow = D / 4, kRowsPerPass = 64 / kLanesPerRow;
+    static_assert(kQW % kRowsPerPass == 0, "whole passes over the wave's rows");
+    const int c = 4 * (lane % kLanesPerRow);    // this lane's 4 values of a row
+#pragma unroll 4
+    for (int it = 0; it < kQW / kRowsPerPass; ++it) {
+      const int r = kRowsPerPass * it + lane / kLanesPerRow;   // row of the wave
+      const int grow = qw0 + r;
+      if (grow < pe.n_q) {
+        const f32x4_t v = *reinterpret_cast<SQKV_LDS const f32x4_t*>(stage + r * C::STAGE_PITCH + c * 4);
+        float y[4] = {v[0], v[1], v[2], v[3]};
+        if (pe.o_in != nullptr) {
+          const float w = *reinterpret_cast<SQKV_LDS const float*>(stage + kQW * C::STAGE_PITCH + r * 4);
+          if (w != 0.f) {
+            float x[4];
+            load4(pe.o_in, b * pe.oi_sb + h * pe.oi_sh + (int64_t)grow * pe.oi_sn + c, pe.acc_dtype, x);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) y[k] = fmaf(w, x[k], y[k]);
+          }
+        }
+        store4(pe.o_out, b * pe.oo_sb + h * pe.oo_sh + (int64_t)grow * pe.oo_sn + c, pe.out_dtype, y);
+      }
+    }
   }
+  // every wave is done with this visit's LDS (fragments, flag) before the
+  // next one's DMA and flag clearing
+  lds_reads_done_sync();
+  }
+}
+
+// Compute units of the current device (one persistent workgroup each).
+hipError_t cu_count(int* n) {
+  constexpr int kMaxDev = 64;
+  static int cache[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDev && cache[dev] > 0) {
+    *n = cache[dev];
+    return hipSuccess;
+  }
+  e = hipDeviceGetAttribute(n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (*n < 1) *n = 1;
+  if (dev >= 0 && dev < kMaxDev) cache[dev] = *n;
+  return hipSuccess;
 }
 
 template <int D, bool PACKED>
@@ -832,6 +926,10 @@ hipError_t launch_d(const AttnParams& p, hipStream_t s) {
   const int n_qtiles = (p.n_q + kBM - 1) / kBM;
   const int64_t blocks = (int64_t)n_qtiles * p.B * p.Hq;
   if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;   // the host validation keeps items below 2^31
+  int ncu = 0;
+  hipError_t ec = cu_count(&ncu);
+  if (ec != hipSuccess) return ec;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_kernel<D, PACKED>),
@@ -839,8 +937,9 @@ hipError_t launch_d(const AttnParams& p, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((attn_bf16_kernel<D, PACKED>), dim3((unsigned)blocks), dim3(kThreads), C::LDS_ALLOC, s, p,
-                     n_qtiles);
+  const unsigned grid = (unsigned)(blocks < ncu ? blocks : ncu);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, PACKED>), dim3(grid), dim3(kThreads), C::LDS_ALLOC, s, p, n_qtiles,
+                     (int)blocks);
   return hipGetLastError();
 }
 
