@@ -320,7 +320,9 @@ attn_bf16_kernel(AttnParams params, int n_qtiles, int n_items) {
       const u32x4_t z = {0u, 0u, 0u, 0u};
       qf[kc] = ok ? *reinterpret_cast<const u32x4_t*>(src + 16 * kc) : z;
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // Q is in registers before any DMA is counted
+    // No wait here: the Q loads are older than the visit's first K/V DMA,
+    // so the first DMA wait (vector memory completes in order) also covers
+    // them, and the two latencies overlap (measured: ~2 us per visit).
   };
   load_q();
 
@@ -844,9 +846,12 @@ attn_bf16_kernel(AttnParams params, int n_qtiles, int n_items) {
   // back in row order and stores whole rows: 32 lanes per row, 4 values each,
   // merged there with the running (o_in) rows when present.
   {
-    const AttnParams* pk = (const AttnParams*)__builtin_amdgcn_kernarg_segment_ptr();
+    // (in the constant address space: a generic pointer would let every
+    // output store alias the parameters, and the compiler then waits for each
+    // store to complete before reading them again)
+    KernArgParams* pk = (KernArgParams*)__builtin_amdgcn_kernarg_segment_ptr();
     asm volatile("" : "+s"(pk));
-    const AttnParams& pe = *pk;
+    KernArgParams& pe = *pk;
     const int row = qw0 + l32;
     const float lt = sum_half(l_run);
     const int64_t bh_row = (int64_t)b * pe.Hq + h;
@@ -876,23 +881,36 @@ attn_bf16_kernel(AttnParams params, int n_qtiles, int n_items) {
     constexpr int kLanesPerRow = D / 4, kRowsPerPass = 64 / kLanesPerRow;
     static_assert(kQW % kRowsPerPass == 0, "whole passes over the wave's rows");
     const int c = 4 * (lane % kLanesPerRow);    // this lane's 4 values of a row
+    const int r0 = lane / kLanesPerRow;
+    // element offsets of (row qw0 + r0, column c) and the step to the next pass
+    const int64_t obase = b * pe.oo_sb + h * pe.oo_sh + (int64_t)(qw0 + r0) * pe.oo_sn + c;
+    const int64_t ibase = b * pe.oi_sb + h * pe.oi_sh + (int64_t)(qw0 + r0) * pe.oi_sn + c;
+    const int64_t ostep = kRowsPerPass * pe.oo_sn, istep = kRowsPerPass * pe.oi_sn;
+    const bool bf16_out = pe.out_dtype == kBF16;
+    const int n_q = pe.n_q, acc_dtype = pe.acc_dtype;
+    const void* const o_in = pe.o_in;
+    void* const o_out = pe.o_out;
 #pragma unroll 4
     for (int it = 0; it < kQW / kRowsPerPass; ++it) {
-      const int r = kRowsPerPass * it + lane / kLanesPerRow;   // row of the wave
-      const int grow = qw0 + r;
-      if (grow < pe.n_q) {
-        const f32x4_t v = *reinterpret_cast<SQKV_LDS const f32x4_t*>(stage + r * C::STAGE_PITCH + c * 4);
-        float y[4] = {v[0], v[1], v[2], v[3]};
-        if (pe.o_in != nullptr) {
+      const int r = kRowsPerPass * it + r0;     // row of the wave
+      if (qw0 + r < n_q) {
+        f32x4_t y = *reinterpret_cast<SQKV_LDS const f32x4_t*>(stage + r * C::STAGE_PITCH + c * 4);
+        if (o_in != nullptr) {
           const float w = *reinterpret_cast<SQKV_LDS const float*>(stage + kQW * C::STAGE_PITCH + r * 4);
           if (w != 0.f) {
             float x[4];
-            load4(pe.o_in, b * pe.oi_sb + h * pe.oi_sh + (int64_t)grow * pe.oi_sn + c, pe.acc_dtype, x);
+            load4(o_in, ibase + it * istep, acc_dtype, x);
 #pragma unroll
             for (int k = 0; k < 4; ++k) y[k] = fmaf(w, x[k], y[k]);
           }
         }
-        store4(pe.o_out, b * pe.oo_sb + h * pe.oo_sh + (int64_t)grow * pe.oo_sn + c, pe.out_dtype, y);
+        const int64_t off = obase + it * ostep;
+        if (bf16_out) {   // round to nearest even in hardware, two values per instruction
+          const uint2 v = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(o_out) + off) = v;
+        } else {
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(o_out) + off) = y;
+        }
       }
     }
   }
