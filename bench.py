@@ -25,7 +25,8 @@ roofline beside the same kernel run as a plain copy of the same bytes; the
 GQA key/value replication of the Ulysses exchange at 128k (1 and 2 key/value
 heads copied up to 8 ranks); the whole causal 128k ring under the contiguous
 and the zigzag split; the backward of the 32k ring; the USP hybrid at 128k;
-the 32k ring packing 2k-token samples; the standalone lse merge of a 128k
+the 32k ring packing 2k-token samples; the fixed cost of an attention visit
+(query tiles against 1..64 key tiles); the standalone lse merge of a 128k
 ring step; the tiny fp32 ring; causal attention over 1,048,576 tokens; and,
 with the CPU baseline, the oracle's Ulysses copies.  Logs go to stderr.
 """
@@ -60,8 +61,8 @@ ATTN_COUNTERS = {
 }
 PERMUTE_TRAFFIC_FILE = os.path.join(PROFILES, "ulysses_permute_131k_traffic.json")
 REPLICATION_TRAFFIC_FILE = os.path.join(PROFILES, "ulysses_gqa_replication_131k_traffic.json")
-EXTRAS = ("ring32k", "ulysses_share", "ulysses", "gqa_replication", "packed", "backward", "causal_split", "usp",
-          "lse_merge", "f32_tiny", "capacity_1m")
+EXTRAS = ("ring32k", "ulysses_share", "ulysses", "gqa_replication", "packed", "visit_lengths", "backward",
+          "causal_split", "usp", "lse_merge", "f32_tiny", "capacity_1m")
 
 
 def log(*a):
@@ -384,12 +385,45 @@ def bench_gqa_replication(api, torch, iters=10):
                                "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                                             "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                                             "traffic": tr, "kernel": "replicate_kernel<16>"}}
+        if H_kv == 1:   # write ceiling: a linear fill of the same destination bytes, timed the same way
+            ts, _ = timed_launches(torch, lambda: dst.fill_(1), 1, iters, flush)
+            st = ms_stats(ts)
+            res["linear_fill_same_dst_bytes"] = {**st, "GB/s": round(dst.numel() * 2 / (st["ms_mean"] * 1e-3) / 1e9, 1),
+                                                 "kernel": "torch fill_ of the 256 MiB destination"}
         del src, dst
     res["workload"] = ("GQA key/value exchange: 8 shards [16384, H_kv, 128] bf16 -> [131072, 1, 128] per rank "
                        "(H_dst = 8), L = 131072")
     del buf
     torch.cuda.empty_cache()
     return res
+
+
+def bench_visit_lengths(api, torch, iters=5):
+    """Fixed cost of one attention visit: 4096 query tiles of 256 rows (16 per
+    CU, non-causal, d=128), each against T key tiles of 64 for T in 1..64;
+    per-workgroup time per visit and a straight-line fit over T >= 8 (the
+    slope is the steady cost of a tile, the intercept the cost of a visit's
+    start and end)."""
+    H, n, d = 4096, 256, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12)
+    q = (torch.randn((1, H, n, d), generator=g, device="cuda") * d ** -0.5).to(torch.bfloat16)
+    o = torch.empty_like(q)
+    lse = torch.empty(H * n, dtype=torch.float32, device="cuda")
+    pts = {}
+    for T in (1, 4, 8, 16, 32, 64):
+        kv = torch.randn((1, H, 64 * T, d), generator=g, device="cuda").to(torch.bfloat16)
+        ts, _ = timed_launches(torch, lambda: api.ra_chunk_attention(q, kv, kv, o, lse), 1, iters)
+        pts[T] = round(statistics.median(ts) * 1e3 / (H / 256), 2)      # us per workgroup visit (16 per CU)
+        del kv
+    xs = [t for t in pts if t >= 8]
+    mx, my = sum(xs) / len(xs), sum(pts[t] for t in xs) / len(xs)
+    slope = sum((t - mx) * (pts[t] - my) for t in xs) / sum((t - mx) ** 2 for t in xs)
+    del q, o, lse
+    torch.cuda.empty_cache()
+    return {"us_per_visit_by_key_tiles": pts, "fit_us_per_tile": round(slope, 3),
+            "fit_us_per_visit": round(my - slope * mx, 2),
+            "workload": "4096 query tiles of 256 rows x T key tiles of 64, d=128, non-causal, 16 visits per CU"}
 
 
 def bench_lse_merge(api, torch, iters=10):
@@ -628,6 +662,7 @@ def run_extras(api, torch, chosen):
             ("ulysses", "ulysses", lambda: bench_ulysses(api, torch)),
             ("gqa_replication", "ulysses_gqa_replication_128k", lambda: bench_gqa_replication(api, torch)),
             ("packed", "ring_bf16_32k_packed_2k", lambda: bench_packed(api, torch)),
+            ("visit_lengths", "attention_visit_lengths", lambda: bench_visit_lengths(api, torch)),
             ("backward", "ring_bf16_32k_backward", lambda: bench_backward(api, torch)),
             ("causal_split", "causal_128k_ring_split", lambda: bench_causal_split(api, torch)),
             ("usp", "usp_128k_causal", lambda: bench_usp(api, torch)),
