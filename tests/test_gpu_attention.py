@@ -517,9 +517,9 @@ def test_causal_1m_tokens_sampled(api):
     free0 = torch.cuda.mem_get_info()[0]
     api.ra_chunk_attention(qd, kd, vd, o, lse, causal=True)
     torch.cuda.synchronize()
-    # no L x L buffer (2 TiB per head here): the only device memory the call
-    # can take is what the HIP runtime reserves on a kernel's first launch
-    # (per-queue scratch for its spilled registers, tens of MiB)
+    # no L x L buffer (2 TiB per head here): the library allocates nothing, and
+    # the bound leaves room for what the HIP runtime itself may reserve on a
+    # kernel's first launch
     assert free0 - torch.cuda.mem_get_info()[0] < oracle.attn_matrix_bytes(L) // 4096
     # every element written (the output starts as NaN) and finite
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
