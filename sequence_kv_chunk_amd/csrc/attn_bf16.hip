@@ -41,8 +41,9 @@
 //   instruction immediate.  The DMA loads are inline assembly, their
 //   completion counted with explicit s_waitcnt vmcnt, because the compiler
 //   would otherwise wait for every in-flight LDS DMA before each LDS read.
-//   The tile count is padded to 4k+1 with empty tiles (fully masked,
-//   zero-filled), which contribute nothing.
+//   The loop runs 4k iterations for a visit of T <= 4k+1 tiles: the tiles
+//   past T are empty (fully masked, zero-filled) and contribute nothing, and
+//   the P V of tile 4k after the loop runs only when T = 4k+1.
 // * Softmax runs in base 2, in up to two passes over the visit.  Both take
 //   the fp32 score of the bf16 Q and K and multiply it by scale*log2(e) in
 //   fp32 right before the exponential, so the exponent carries only fp32
@@ -794,7 +795,9 @@ attn_bf16_kernel(AttnParams params, int n_qtiles, int n_items) {
       g += 1;
       wait_dma_and_sync<2 * C::NL, kPreLds>();   // K(t+4), V(t+2) landed
     };
-    // T - 1 iterations, padded to a multiple of 4 with empty tiles
+    // T - 1 iterations, padded to a multiple of 4 with empty tiles; iteration
+    // t adds tile t's P V, so the last tile's P V after the loop is needed
+    // only when no padding was added (otherwise it adds zeros)
     const int iters = (T - 1 + 3) & ~3;
     for (int t = 0; t < iters; t += 4) {
       body(Step<0>{}, sa, sb);
@@ -802,7 +805,7 @@ attn_bf16_kernel(AttnParams params, int n_qtiles, int n_items) {
       body(Step<2>{}, sa, sb);
       body(Step<3>{}, sb, sa);
     }
-    pv(Step<0>{});                       // V of the last (padded) tile landed above
+    if (iters == T - 1) pv(Step<0>{});   // V of the last tile landed above
     };
 
   // The fast pass (weights 2^(score * c) with no maximum subtracted) is kept
@@ -923,18 +926,16 @@ attn_bf16_kernel(AttnParams params, int n_qtiles, int n_items) {
 // Compute units of the current device (one persistent workgroup each).
 hipError_t cu_count(int* n) {
   constexpr int kMaxDev = 64;
-  static int cache[kMaxDev] = {};
+  static std::atomic<int> cache[kMaxDev] = {};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < kMaxDev && cache[dev] > 0) {
-    *n = cache[dev];
-    return hipSuccess;
-  }
+  const bool cached = dev >= 0 && dev < kMaxDev;
+  if (cached && (*n = cache[dev].load(std::memory_order_relaxed)) > 0) return hipSuccess;
   e = hipDeviceGetAttribute(n, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   if (*n < 1) *n = 1;
-  if (dev >= 0 && dev < kMaxDev) cache[dev] = *n;
+  if (cached) cache[dev].store(*n, std::memory_order_relaxed);
   return hipSuccess;
 }
 
@@ -948,13 +949,9 @@ hipError_t launch_d(const AttnParams& p, hipStream_t s) {
   int ncu = 0;
   hipError_t ec = cu_count(&ncu);
   if (ec != hipSuccess) return ec;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_kernel<D, PACKED>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_ALLOC);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = allow_dyn_lds(reinterpret_cast<const void*>(&attn_bf16_kernel<D, PACKED>), C::LDS_ALLOC, lds_set);
+  if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)(blocks < ncu ? blocks : ncu);
   hipLaunchKernelGGL((attn_bf16_kernel<D, PACKED>), dim3(grid), dim3(kThreads), C::LDS_ALLOC, s, p, n_qtiles,
                      (int)blocks);

@@ -829,16 +829,11 @@ template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t s) {
   using Cq = BCfg<D, kDqWaves>;
   using Ck = BCfg<D, kKvWaves>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 4 * Cq::TILE);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kKvLds<D>);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> dq_set{0}, kv_set{0};
+  hipError_t e = allow_dyn_lds(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D>), 4 * Cq::TILE, dq_set);
+  if (e != hipSuccess) return e;
+  e = allow_dyn_lds(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D>), kKvLds<D>, kv_set);
+  if (e != hipSuccess) return e;
   const int n_qtiles = (p.n_q + kDqRows - 1) / kDqRows;
   const int64_t bq = (int64_t)n_qtiles * p.B * p.Hq;
   if (bq > 0)
