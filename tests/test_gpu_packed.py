@@ -82,6 +82,38 @@ def test_packed_fast_pass_fallback(api):
         check_close(host_f64(lse).reshape(1, H, n), ref_l[:, :, r * n:(r + 1) * n], "bf16", f"lse rank {r}")
 
 
+@pytest.mark.parametrize("Hq,Hkv,d,starts", [
+    (1024, 128, 128, [0, 37, 250, 251, 333, 512, 600, 639]),
+    (512, 512, 64, [0, 31, 64, 256, 257, 300, 320, 321, 480]),
+], ids=["h1024_d128", "h512_d64"])
+def test_packed_many_visits_per_workgroup(api, Hq, Hkv, d, starts):
+    """Enough heads that every workgroup makes several visits in turn (each
+    visit loads the next one's first tiles before its own stores): every
+    output finite, and sampled heads against the oracle in full."""
+    P, n = 2, 320
+    L = P * n
+    say(f"packed, {Hq} heads, d={d}: several visits per workgroup")
+    rng = np.random.default_rng(5100 + Hq + d)
+    qb = f32_to_bf16_bits(rng.standard_normal((P, 1, Hq, n, d), dtype=np.float32) * np.float32(d ** -0.5))
+    kb = f32_to_bf16_bits(rng.standard_normal((P, 1, Hkv, n, d), dtype=np.float32))
+    vb = f32_to_bf16_bits(rng.standard_normal((P, 1, Hkv, n, d), dtype=np.float32))
+    heads = np.unique(np.concatenate([[0, 1, Hq - 1], rng.integers(0, Hq, size=45)]))
+    kv = heads // (Hq // Hkv)
+    full = lambda x, sel: bf16_bits_to_f64(x[:, :, sel]).transpose(1, 2, 0, 3, 4).reshape(1, len(sel), L, d)
+    ref_o, ref_l = oracle.attention_packed_fp64(full(qb, heads), full(kb, kv), full(vb, kv), starts)
+    kd, vd = dev_bf16(kb), dev_bf16(vb)
+    seg = torch.tensor(starts, dtype=torch.int64, device="cuda")
+    for r in range(P):
+        o = torch.full((1, Hq, n, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((Hq * n,), float("nan"), dtype=torch.float32, device="cuda")
+        api.ra_ring_attention_packed(dev_bf16(qb[r]), kd, vd, o, lse, seg, rank=r)
+        torch.cuda.synchronize()
+        go, gl = host_f64(o), host_f64(lse).reshape(1, Hq, n)
+        assert np.isfinite(go).all() and np.isfinite(gl).all(), f"rank {r}: unwritten or non-finite outputs"
+        check_close(go[:, heads], ref_o[:, :, r * n:(r + 1) * n], "bf16", f"O rank {r}")
+        check_close(gl[:, heads], ref_l[:, :, r * n:(r + 1) * n], "bf16", f"lse rank {r}")
+
+
 @pytest.mark.slow
 def test_packed_32k_full_sampled(api):
     """The 32k ring packing 16 samples of 2048 tokens, the shape bench.py
