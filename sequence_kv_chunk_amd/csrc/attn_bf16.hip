@@ -234,9 +234,9 @@ attn_bf16_kernel(AttnParams params, int n_qtiles, int n_items) {
   // (one (b, h, q-tile) visit each) in turn: workgroup g takes items g,
   // 2G-1-g, 2G+g, 4G-1-g, ... of the G-wide rounds, so that in a list issued
   // heaviest first a heavy item pairs with a light one.  A visit's output
-  // stores then drain while the next visit loads its Q and first tiles
-  // (measured: a visit of one 64-key tile took 20 us as a workgroup of its
-  // own, 8.5 us of it in the output stores).
+  // stores then drain while the next visit sets up and loads its Q and
+  // first tiles, and the launch pays for one workgroup start per CU rather
+  // than one per item.
   const int G = gridDim.x;
   for (int round = 0;; ++round) {
   const int item = round * G + ((round & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
@@ -844,10 +844,10 @@ attn_bf16_kernel(AttnParams params, int n_qtiles, int n_items) {
   // them early and keeps ~20 scalar registers live across the loop.
   // A lane holds 64 of its row's d values in groups of four, so storing from
   // the accumulators writes 8 or 16 bytes at a time scattered over 32 rows
-  // (measured: ~8 us per visit for a 256-row bf16 tile).  Instead each wave
-  // writes its rows, normalised, as fp32 into its own LDS region, reads them
-  // back in row order and stores whole rows: 32 lanes per row, 4 values each,
-  // merged there with the running (o_in) rows when present.
+  // (measured: ~1 us per visit slower than the staging below).  Instead
+  // each wave writes its rows, normalised, as fp32 into its own LDS region,
+  // reads them back in row order and stores whole rows: D/4 lanes per row,
+  // 4 values each, merged there with the running (o_in) rows when present.
   {
     // (in the constant address space: a generic pointer would let every
     // output store alias the parameters, and the compiler then waits for each
