@@ -284,9 +284,52 @@ def bench_ring32k(api, torch, warmup=3, iters=10):
     return res
 
 
-def bench_ulysses_share(api, torch, warmup=3, iters=10):
+def cpu_oracle_share(w, x, o, lse, torch, rows_per_head=512):
+    """The fp64 oracle on a seeded sample of the GQA share: in every query
+    head, `rows_per_head` query rows evenly spaced over the sequence (the
+    first and the last included) against every key each row sees; the time
+    is extrapolated to the whole share by visible (query, key) pairs, and the
+    GPU output on the sampled rows is compared with it."""
+    import oracle
+    from sequence_kv_chunk_amd.synth import bf16_bits_to_f64
+    from threadpoolctl import threadpool_limits
+
+    def bits(t):
+        return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    model, cores, blas = host_facts()
+    L, Hq, Hkv, d = w.L, w.Hq, w.Hkv, w.d
+    rows = np.unique(np.linspace(0, L - 1, rows_per_head).round().astype(np.int64))
+    o_rows = o[rows].float().cpu().numpy().astype(np.float64)                   # [r, Hq, d]
+    l_rows = lse.view(Hq, L)[:, rows].cpu().numpy().astype(np.float64)          # [Hq, r]
+    secs, err_o, err_l = 0.0, 0.0, 0.0
+    with threadpool_limits(limits=cores):
+        for hk in range(Hkv):
+            kf = bf16_bits_to_f64(bits(x["k"][:, hk])).reshape(1, 1, L, d)
+            vf = bf16_bits_to_f64(bits(x["v"][:, hk])).reshape(1, 1, L, d)
+            for h in range(hk * (Hq // Hkv), (hk + 1) * (Hq // Hkv)):
+                qh = bf16_bits_to_f64(bits(x["q"][rows, h])).reshape(1, 1, rows.size, d)
+                t0 = time.perf_counter()
+                ref_o, ref_l = oracle.attention_at_positions_fp64(qh, kf, vf, rows, np.arange(L))
+                secs += time.perf_counter() - t0
+                err_o = max(err_o, float(np.max(np.abs(ref_o[0, 0] - o_rows[:, h]))))
+                err_l = max(err_l, float(np.max(np.abs(ref_l[0, 0] - l_rows[h]))))
+    pairs_sample = int(np.sum(rows + 1)) * Hq
+    full_pairs = Hq * L * (L + 1) // 2
+    return {"value": round(4 * d * pairs_sample / secs / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{rows.size} query rows per head (evenly spaced over the {L} tokens, first and last "
+                      f"included) x {Hq} heads, each against all of its visible keys; fp64 numpy oracle",
+            "sample_seconds": round(secs, 2),
+            "full_share_seconds_extrapolated": round(secs * full_pairs / pairs_sample, 1),
+            "cpu_model": model, "blas": blas, "threads": cores,
+            "gpu_max_abs_err_on_sample": {"O": float(f"{err_o:.3e}"), "lse": float(f"{err_l:.3e}")}}
+
+
+def bench_ulysses_share(api, torch, warmup=3, iters=10, cpu=False):
     """One Ulysses share: causal attention over 131072 tokens, 4 query heads
-    on 1 key/value head, [S, H, d] layout, fp32 lse; one launch."""
+    on 1 key/value head, [S, H, d] layout, fp32 lse; one launch.  With `cpu`,
+    also the fp64 oracle on a sample of it."""
     from sequence_kv_chunk_amd.synth import WORKLOADS, device_attention_inputs
     w = WORKLOADS["ulysses_share_gqa_128k_causal"]
     x = device_attention_inputs(w)
@@ -299,6 +342,8 @@ def bench_ulysses_share(api, torch, warmup=3, iters=10):
                 "roofline": attn_roofline(w.name, w.flops(), ts),
                 "workload": "ulysses_share_gqa_128k_causal: L=131072, 4 query heads, 1 KV head, d=128, causal, "
                             "[S, H, d] layout, one launch"})
+    if cpu:
+        res["cpu_oracle"] = cpu_oracle_share(w, x, o, lse, torch)
     del x, o, lse
     torch.cuda.empty_cache()
     return res
@@ -452,9 +497,10 @@ def bench_lse_merge(api, torch, iters=10):
             "workload": "lse merge of two fp32 partials [1, 32, 16384, 128] + lse (one 128k ring step)"}
 
 
-def bench_f32_tiny(api, torch, iters=20):
+def bench_f32_tiny(api, torch, iters=20, cpu=False):
     """The tiny fp32 ring (4 virtual ranks x 4 chunks of 256, 4 heads, d=64):
-    a correctness workload; its time is reported, not held against a roofline."""
+    a correctness workload; its time is reported, not held against a roofline.
+    With `cpu`, also the fp64 oracle on the whole workload."""
     from sequence_kv_chunk_amd.synth import WORKLOADS, device_attention_inputs
     w = WORKLOADS["ring_f32_tiny"]
     x = device_attention_inputs(w)
@@ -467,8 +513,24 @@ def bench_f32_tiny(api, torch, iters=20):
             api.ra_ring_attention(qs[r], kp, vp, o, lse, rank=r)
 
     ts, _ = timed_launches(torch, step, 2, iters)
-    return {"ms": round(sum(ts) / len(ts), 4), "launches": w.P, "flops": w.flops(),
-            "workload": "ring_f32_tiny: fp32, B=1, 4 heads, d=64, L=1024 as 4 chunks of 256, all 4 ranks"}
+    res = {"ms": round(sum(ts) / len(ts), 4), "launches": w.P, "flops": w.flops(),
+           "workload": "ring_f32_tiny: fp32, B=1, 4 heads, d=64, L=1024 as 4 chunks of 256, all 4 ranks"}
+    if cpu:
+        import oracle
+        full = lambda t: t.permute(1, 2, 0, 3, 4).reshape(t.shape[1], t.shape[2], -1, t.shape[-1]).double().cpu().numpy()
+        qf, kf, vf = full(qs), full(kp), full(vp)
+        t0 = time.perf_counter()
+        ref_o, _ = oracle.attention_fp64(qf, kf, vf)
+        secs = time.perf_counter() - t0
+        step()
+        torch.cuda.synchronize()
+        last = o.double().cpu().numpy()                        # rank P-1's chunk
+        n = qs.shape[3]
+        err = float(np.max(np.abs(last - ref_o[:, :, (w.P - 1) * n:])) / np.max(np.abs(ref_o)))
+        res["cpu_oracle"] = {"ms": round(secs * 1e3, 2), "kind": "oracle", "cores": host_facts()[1],
+                             "sample": "the whole workload (fp64 numpy oracle, one softmax per query row)",
+                             "gpu_normwise_rel_err_last_rank": float(f"{err:.3e}")}
+    return res
 
 
 def bench_capacity_1m(api, torch):
@@ -654,11 +716,12 @@ def cpu_baseline_ulysses(torch):
     return res
 
 
-def run_extras(api, torch, chosen):
-    """The other workloads' figures; a failure here never hides the main line."""
+def run_extras(api, torch, chosen, cpu=False):
+    """The other workloads' figures; a failure here never hides the main line.
+    With `cpu`, the extras that carry an oracle figure time it too."""
     extras = {}
     runs = (("ring32k", "ring_bf16_32k", lambda: bench_ring32k(api, torch)),
-            ("ulysses_share", "ulysses_share_gqa_128k_causal", lambda: bench_ulysses_share(api, torch)),
+            ("ulysses_share", "ulysses_share_gqa_128k_causal", lambda: bench_ulysses_share(api, torch, cpu=cpu)),
             ("ulysses", "ulysses", lambda: bench_ulysses(api, torch)),
             ("gqa_replication", "ulysses_gqa_replication_128k", lambda: bench_gqa_replication(api, torch)),
             ("packed", "ring_bf16_32k_packed_2k", lambda: bench_packed(api, torch)),
@@ -667,7 +730,7 @@ def run_extras(api, torch, chosen):
             ("causal_split", "causal_128k_ring_split", lambda: bench_causal_split(api, torch)),
             ("usp", "usp_128k_causal", lambda: bench_usp(api, torch)),
             ("lse_merge", "lse_merge_128k_step", lambda: bench_lse_merge(api, torch)),
-            ("f32_tiny", "ring_f32_tiny", lambda: bench_f32_tiny(api, torch)),
+            ("f32_tiny", "ring_f32_tiny", lambda: bench_f32_tiny(api, torch, cpu=cpu)),
             ("capacity_1m", "capacity_1m_causal", lambda: bench_capacity_1m(api, torch)))
     for key, name, fn in runs:
         if key not in chosen:
@@ -727,7 +790,7 @@ def main():
             result["cpu_baseline"] = None
         del kept
         torch.cuda.empty_cache()
-    extras = run_extras(api, torch, chosen)
+    extras = run_extras(api, torch, chosen, cpu=not args.no_cpu and not args.only_extras)
     if not args.no_cpu and not args.only_extras and "ulysses" in chosen:
         extras["cpu_oracle_ulysses"] = cpu_baseline_ulysses(torch)
         log(f"cpu oracle ulysses: {extras['cpu_oracle_ulysses']}")
