@@ -92,6 +92,26 @@ def test_chunk_partial(api, case, in_dt):
         check_close(host_f64(lse).reshape(ref_l.shape), ref_l, tol, "lse")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_chunk_many_items_ragged_gqa(api, causal, d):
+    """More (b, h, q-tile) items than CUs (several visits per workgroup) with
+    item counts that fill neither the 8 XCDs evenly nor whole GQA groups of
+    8*group, a ragged last q-tile and 5:1 GQA: every output written once
+    (NaN-initialised, all finite) and equal to the oracle."""
+    B, Hq, Hkv, nq, nk = 1, 150, 30, 520, 390
+    say(f"chunk, {Hq} heads x 3 q-tiles, causal={causal}, d={d}")
+    (q, k, v), (qd, kd, vd) = _inputs("bf16", B, Hq, Hkv, nq, nk, d, seed=900 + d + causal)
+    ref_o, ref_l = oracle.attention_fp64(q, k, v, causal=causal, q_pos0=130 if causal else 0)
+    o, lse = _out(B, Hq, nq, d, torch.bfloat16)
+    api.ra_chunk_attention(qd, kd, vd, o, lse, causal=causal, q_pos0=130 if causal else 0)
+    torch.cuda.synchronize()
+    go, gl = host_f64(o), host_f64(lse).reshape(ref_l.shape)
+    assert np.isfinite(go).all() and np.isfinite(gl).all(), "unwritten or non-finite outputs"
+    check_close(go, ref_o, "bf16", "O")
+    check_close(gl, ref_l, "bf16", "lse")
+
+
 @pytest.mark.parametrize("in_dt", ["f32", "bf16"])
 @pytest.mark.parametrize("inplace", [True, False])
 def test_chunk_accumulate(api, in_dt, inplace):
