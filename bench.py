@@ -764,14 +764,14 @@ def main():
               "pool); --gpus N with N > 1 is not supported.", file=sys.stderr)
         sys.exit(2)
 
-    import torch
-    from sequence_kv_chunk_amd import api
-
     chosen = () if args.no_extras else (EXTRAS if args.extras == "all" else tuple(args.extras.split(",")))
     unknown = [e for e in chosen if e not in EXTRAS]
     if unknown:
         print(f"bench.py: unknown extras {unknown}; choose from {','.join(EXTRAS)}", file=sys.stderr)
         sys.exit(2)
+
+    import torch
+    from sequence_kv_chunk_amd import api
 
     if args.calibrate_copy:
         a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
