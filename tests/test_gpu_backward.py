@@ -55,6 +55,9 @@ CASES = [
     (1, 4, 2, 3, 200, 64, False, 0, 0, 0.7),         # three queries, ragged keys
     (1, 2, 1, 70, 40, 128, True, 0, 100, 1.0),       # every key after every query: no contribution
     (2, 2, 2, 200, 1, 128, True, 50, 0, 1.0),        # one key, seen by every row
+    (1, 2, 2, 600, 600, 64, True, 0, 0, 1.0),        # diagonal over several query and key workgroups
+    (1, 4, 2, 700, 450, 128, True, 0, 200, 1.0),     # key workgroups whose walks start at different tiles
+    (2, 4, 1, 520, 260, 128, False, 0, 0, 0.9),      # GQA 4:1, B=2, ragged query and key tails
 ]
 
 
@@ -104,7 +107,8 @@ def test_bwd_preprocess(api):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("P,n,Hq,Hkv,d", [(4, 128, 4, 2, 128), (3, 100, 2, 2, 64), (1, 200, 2, 1, 128)])
+@pytest.mark.parametrize("P,n,Hq,Hkv,d", [(4, 128, 4, 2, 128), (3, 100, 2, 2, 64), (1, 200, 2, 1, 128),
+                                          (3, 300, 2, 1, 128)])
 def test_ring_bwd_end_to_end(api, P, n, Hq, Hkv, d, causal):
     """GPU ring forward, GPU D, every rank's GPU backward; against the
     gradients of one softmax over the whole sequence."""
