@@ -20,14 +20,14 @@
 //   ds_read_b64_tr_b16 and dS^T rounded to bf16 as the B operand.  The two
 //   32-key blocks of a tile are staggered so that one block's VALU work runs
 //   between the other block's MFMAs.
-// * attn_bwd_dkdv: parallel over keys (4 waves x 32 keys per workgroup, one
-//   wave per SIMD: K and -V rows of the wave's keys in registers, dK^T and
-//   dV^T accumulators alongside).  Per 32-query block it forms S = Q K^T and
-//   D - dP (queries on M: a lane holds 16 queries of ONE key), P and dS, and
-//   dV^T += dO^T P, dK^T += Q^T dS with transposed reads of the dO and Q
-//   tiles, three blocks in flight at once.  The query heads of a GQA group
-//   are walked inside the workgroup so that a key/value head's gradients sum
-//   over them without atomics.
+// * attn_bwd_dkdv: parallel over keys (128 keys per workgroup, 8 waves, two
+//   per SIMD).  The two waves of a SIMD share 32 keys: one holds their K
+//   rows and forms S = Q K^T and P, the other holds -V and forms D - dP and
+//   dS (queries on M: a lane holds 16 queries of ONE key); P and dS cross
+//   between them through LDS, and each accumulates dV^T += dO^T P and
+//   dK^T += Q^T dS (transposed reads of the dO and Q tiles) for its half of
+//   d.  The query heads of a GQA group are walked inside the workgroup so
+//   that a key/value head's gradients sum over them without atomics.
 // Tiles (64 rows) are copied global -> LDS by buffer_load ... lds, two
 // (dQ) or three (dK/dV) stages deep.  Every tile is read both as rows
 // (ds_read_b128) and transposed (ds_read_b64_tr_b16); the 16-byte chunk
@@ -430,58 +430,63 @@ attn_bwd_dq_kernel(BwdParams p, int n_qtiles) {
 // ============================================================================
 // dK, dV: key rows in registers, Q/dO tiles streamed
 // ============================================================================
-constexpr int kKvWaves = 4;
-constexpr int kKvRows = 32 * kKvWaves;
-constexpr int kKvStages = 3;   // LDS stages of (Q tile, dO tile, lse, D)
+constexpr int kKvRows = 128;    // keys per workgroup
+constexpr int kKvStages = 3;    // LDS stages of (Q tile, dO tile, lse, D)
 
+// Two waves per SIMD, a pair of waves per 32 keys.  Waves w and w + 4 (one SIMD) take the same 32 keys.  Wave w (role 0)
+// holds the K rows of the keys and forms S = Q K^T and P; wave w + 4 (role 1)
+// holds the -V rows and forms D - dP and dS = P (dP - D).  Each accumulates
+// dV^T and dK^T for its own half of d, so a wave holds half the accumulators
+// of the one-wave kernel and the pair issues the same MFMAs as one wave
+// there.  P goes from role 0 to role 1, and dS back, through LDS (bf16, lane
+// to lane in the B-operand layout), with one barrier per 32-query block.
+// Step u (blocks u = 0, 1, ... of the walk; the step after the last block
+// only finishes dK):
+//   role 0: S of block u+1 and its P (written out), dV^T += dO^T P of block
+//           u, dK^T += Q^T dS of block u-1 (dS written by role 1 in step u-1);
+//   role 1: D - dP of block u+1, dS of block u (P written by role 0 in step
+//           u-1, D - dP from its own step u-1, written out), dV^T of block u,
+//           dK^T of block u-1.
+// A step issues its LDS reads ahead of its MFMAs (those of dK after the
+// S or D - dP products are under way), so that the two waves of a SIMD see
+// the read latency about once per step.  Tiles sit in three
+// LDS stages (the three Q tiles, then the three dO tiles, so that every
+// fragment offset fits a read's immediate field); the copy of tile tau+2 is
+// issued after the barrier that ends block 2tau, the last one to read tile
+// tau-1, and waited for at the barrier that ends block 2tau+2.  The loop
+// runs three tiles (six steps) per iteration so that every stage index and
+// every register of the two-block rotation is a constant.
+constexpr int kKvWaves = 8;
+constexpr uint32_t kXchg = 2 * 1024;   // one block's P or dS: two 1 KiB halves of 64 lanes x 16 bytes
 
-// S and dP of one 32-query block for the wave's 32 keys: element j holds
-// query 8*(j/4) + 4*hi + j%4 of the block, key `key` (lane % 32).
-struct SdBlock {
-  f32x16_t s, dp;
-};
+template <int D>
+constexpr uint32_t kKvMainLds = kKvStages * (2 * BCfg<D, kKvWaves>::TILE + 512);
+// LDS: Q tiles of the three stages, dO tiles, (lse, D) of the three stages,
+// then per pair two P and two dS buffers.
+template <int D>
+constexpr int kKvLds = (int)(kKvMainLds<D> + 4 * 4 * kXchg);
 
-// The weights P and dS of one block rounded to bf16, as B operands of the
-// dV and dK products: half h covers queries 16*h .. 16*h + 15 of the block.
-struct PdsBlock {
-  u32x4_t pf[2], df[2];
-};
-
-// Walks 32-query blocks u = 0, 1, ... over the (query head of the GQA group,
-// 64-query tile) sequence, two blocks per tile.  Step u is a software
-// pipeline of three blocks: the S and dP products of block u+2, the
-// softmax-gradient VALU work of block u+1 and the dV, dK products of block u
-// share one slot schedule (one MFMA per slot, S/dP and dV/dK alternating,
-// the VALU work spread over the slots), so the VALU work of one block runs
-// under the MFMAs of the others.  Tiles sit in three LDS stages: at the top
-// of tile tau (blocks 2tau, 2tau+1) tiles tau and tau+1 have landed, and the
-// copy of tile tau+2 goes into the stage of tile tau-1, which every wave has
-// finished reading.
 template <int D>
 __global__ void __launch_bounds__(64 * kKvWaves)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv_kernel(BwdParams p) {
   using C = BCfg<D, kKvWaves>;
-  constexpr int NSD = 2 * C::KC;      // S and dP MFMAs per block
-  constexpr int NKV = 4 * C::MD;      // dV and dK MFMAs per block
-  static_assert(NSD == NKV, "one S/dP MFMA per dV/dK MFMA");
-  constexpr int kSlots = NSD + NKV;
-  constexpr int kLead = 4;            // fragments are read this many slots ahead
-  constexpr int kItems = 24;          // softmax-gradient work items per block (6 per 4 queries)
-  constexpr uint32_t kStage = 2 * C::TILE;                 // Q tile, then dO tile
-  constexpr uint32_t kStats = kKvStages * kStage;          // per stage: lse (256 B), D (256 B)
+  constexpr int MH = C::MD / 2;                     // 32-row blocks of d per half
+  constexpr uint32_t kQ0 = 0, kO0 = kKvStages * C::TILE;   // first Q tile, first dO tile
+  constexpr uint32_t kStats = 2 * kKvStages * C::TILE;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const uint32_t lds0 = (uint32_t)(size_t)(SQKV_LDS unsigned char*)smem;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
+  const int pr = wave & 3, role = wave >> 2;
 
   const int BH = p.B * p.Hkv;
   const int kt = blockIdx.x / BH;
   const int bh = blockIdx.x - kt * BH;
   const int b = bh / p.Hkv, hk = bh - (bh / p.Hkv) * p.Hkv;
-  const int k0 = kt * kKvRows, kw0 = k0 + wave * 32;
+  const int k0 = kt * kKvRows, kw0 = k0 + pr * 32;
   const int key = kw0 + l32;
   const bool key_ok = key < p.n_k;
 
@@ -490,24 +495,20 @@ attn_bwd_dkdv_kernel(BwdParams p) {
   if (p.causal) qstart = (int)min((int64_t)p.n_q, max((int64_t)0, p.k_pos0 + k0 - p.q_pos0));
   const int t0 = qstart / kTR;
   const int T = (p.n_q + kTR - 1) / kTR;
-  const int Tq = T - t0;                      // tiles per query head
-  const int NT = p.group * Tq;                // tiles of the whole walk
+  const int NT = p.group * (T - t0);          // tiles of the whole walk
   if (NT <= 0) return;                        // no query sees these keys: nothing to add
+  const int NB = 2 * NT;                      // 32-query blocks
 
-  // K and V rows of the lane's key (B operands of S and dP); a key past the
-  // chunk end reads zeros and only ever touches its own (unstored) column
-  const uint16_t* krow = static_cast<const uint16_t*>(p.k) + b * p.k_sb + hk * p.k_sh + (int64_t)(key_ok ? key : 0) * p.k_sn;
-  const uint16_t* vrow = static_cast<const uint16_t*>(p.v) + b * p.v_sb + hk * p.v_sh + (int64_t)(key_ok ? key : 0) * p.v_sn;
-  u32x4_t kf[C::KC], vf[C::KC];
+  // K (role 0) or -V (role 1) rows of the lane's key: B operands of S and of
+  // D - dP; a key past the chunk end reads zeros and only ever touches its
+  // own (unstored) column
+  const uint16_t* brow =
+      role == 0 ? static_cast<const uint16_t*>(p.k) + b * p.k_sb + hk * p.k_sh + (int64_t)(key_ok ? key : 0) * p.k_sn
+                : static_cast<const uint16_t*>(p.v) + b * p.v_sb + hk * p.v_sh + (int64_t)(key_ok ? key : 0) * p.v_sn;
+  const uint32_t sgn = role == 0 ? 0u : 0x80008000u;
+  u32x4_t bfr[C::KC];
 #pragma unroll
-  for (int kc = 0; kc < C::KC; ++kc) {
-    kf[kc] = load_row8(krow, key_ok, 16 * kc + 8 * hi);
-    vf[kc] = load_row8(vrow, key_ok, 16 * kc + 8 * hi);
-  }
-  // -V: the dP product of a block starts from the rows' D and ends at
-  // D - dO V^T = -(dP - D)
-#pragma unroll
-  for (int kc = 0; kc < C::KC; ++kc) vf[kc] ^= (u32x4_t){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  for (int kc = 0; kc < C::KC; ++kc) bfr[kc] = load_row8(brow, key_ok, 16 * kc + 8 * hi) ^ (u32x4_t){sgn, sgn, sgn, sgn};
   const int64_t kpos = p.k_pos0 + key;
   const int64_t kpos_wave_last = p.k_pos0 + kw0 + 31;
   const float c = p.scale_log2;
@@ -516,26 +517,14 @@ attn_bwd_dkdv_kernel(BwdParams p) {
   TileDma<D, kKvWaves> q_dma, o_dma;
   q_dma.init(lane, wave, q_snb);
   o_dma.init(lane, wave, o_snb);
-
-  f32x16_t dka[C::MD], dva[C::MD];
-#pragma unroll
-  for (int md = 0; md < C::MD; ++md) {
-    dka[md] = (f32x16_t){};
-    dva[md] = (f32x16_t){};
-  }
-
-  // Q, dO rows [t*64, t*64 + 64) of query head hk*group + gi, and their lse
-  // and D (wave 0: one 64-lane dword load each), into LDS stage `stage`;
-  // rows past the chunk end arrive as zeros.
   auto issue_tile = [&](int gi, int t, int stage) {
     const int h = hk * p.group + gi;
     const unsigned char* qg = reinterpret_cast<const unsigned char*>(
         static_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh);
     const unsigned char* og = reinterpret_cast<const unsigned char*>(
         static_cast<const uint16_t*>(p.dout) + b * p.do_sb + h * p.do_sh);
-    const uint32_t base = lds0 + (uint32_t)stage * kStage;
-    q_dma.issue(qg, q_snb, t * kTR, p.n_q, base);
-    o_dma.issue(og, o_snb, t * kTR, p.n_q, base + C::TILE);
+    q_dma.issue(qg, q_snb, t * kTR, p.n_q, lds0 + kQ0 + (uint32_t)stage * C::TILE);
+    o_dma.issue(og, o_snb, t * kTR, p.n_q, lds0 + kO0 + (uint32_t)stage * C::TILE);
     if (wave == 0) {
       const int nv = __builtin_amdgcn_readfirstlane(min(max(p.n_q - t * kTR, 0), kTR));
       const int64_t row = ((int64_t)b * p.Hq + h) * p.n_q + (int64_t)t * kTR;
@@ -545,173 +534,133 @@ attn_bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  // ---- one block's pieces -------------------------------------------------
-  // S/dP MFMA m: m < KC, S from the Q tile (kc = m); m >= KC, D - dP from the
-  // dO tile (kc = m - KC), starting from the block's D values `dinit`.  Each
-  // reads a row fragment at ra[kc] + qb*32 rows.
-  auto sd_read = [&](auto M, const uint32_t (&ra)[C::KC], auto QB) -> u32x4_t {
-    constexpr int m = decltype(M)::value, qb = decltype(QB)::value;
-    constexpr int kc = m % C::KC;
-    return lds_b128(ra[kc] + (uint32_t)(qb * 32 * C::ROWB + (m / C::KC) * C::TILE));
+  f32x16_t dka[MH], dva[MH];
+#pragma unroll
+  for (int mh = 0; mh < MH; ++mh) {
+    dka[mh] = (f32x16_t){};
+    dva[mh] = (f32x16_t){};
+  }
+
+  // Lane addresses in stage 0: row fragments of the Q (role 0) or dO (role
+  // 1) tile, row l32 of the first half; transposed fragments of the Q tile
+  // for the wave's half of d (the dO tiles are kO0 further); the lse (role
+  // 0) or D (role 1) of the lane's first four queries; the pair's exchange
+  // buffers at the lane's 16-byte slot of each half.
+  uint32_t ra[C::KC], ta[MH][2];
+#pragma unroll
+  for (int kc = 0; kc < C::KC; ++kc) ra[kc] = lds0 + (role == 0 ? kQ0 : kO0) + row_ofs<D>(l32, kc, hi);
+#pragma unroll
+  for (int mh = 0; mh < MH; ++mh) {
+    ta[mh][0] = lds0 + tr_ofs<D>(lane, role * MH + mh, 0);
+    ta[mh][1] = lds0 + tr_ofs<D>(lane, role * MH + mh, 1);
+  }
+  const uint32_t sa = lds0 + kStats + (uint32_t)(16 * hi + 256 * role);
+  const uint32_t xa = lds0 + kKvMainLds<D> + (uint32_t)pr * 4 * kXchg + (uint32_t)lane * 16;
+
+  // ---- pieces of a block (tile stage S, half QB of the tile) ---------------
+  // Row fragments of S (role 0) or D - dP (role 1) of a block.
+  auto sd_frags = [&](auto S, auto QB, u32x4_t (&fr)[C::KC]) {
+    constexpr uint32_t so = (uint32_t)(decltype(S)::value * C::TILE + decltype(QB)::value * 32 * C::ROWB);
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc) fr[kc] = lds_b128(ra[kc] + so);
   };
-  auto sd_mfma = [&](auto M, SdBlock& o, const u32x4_t& fr, const f32x16_t& dinit) {
-    constexpr int m = decltype(M)::value, kc = m % C::KC;
-    if constexpr (m < C::KC)
-      o.s = mfma(as_bf16x8(fr), as_bf16x8(kf[kc]), kc == 0 ? (f32x16_t){} : o.s);
-    else
-      o.dp = mfma(as_bf16x8(fr), as_bf16x8(vf[kc]), kc == 0 ? dinit : o.dp);
+  // The block's lse (role 0) or D (role 1) as the accumulator layout:
+  // element j holds query 8*(j/4) + 4*hi + j%4 of the block.
+  auto stats = [&](auto S, auto QB, u32x4_t (&st)[4]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      st[g] = lds_b128(sa + (uint32_t)(decltype(S)::value * 512 + (32 * decltype(QB)::value + 8 * g) * 4));
   };
-  // D of the 32 queries of half QB of a tile (stats at `sa`), laid out as
-  // the dP accumulator: element j holds query 8*(j/4) + 4*hi + j%4.
-  auto d_init = [&](uint32_t sa, auto QB) -> f32x16_t {
-    constexpr int qb = decltype(QB)::value;
-    f32x16_t r;
+  // S = Q K^T (role 0, from 0) or D - dP = D - dO V^T (role 1, from D).
+  auto sd_mfma = [&](auto R, const u32x4_t (&fr)[C::KC], const u32x4_t (&st)[4]) -> f32x16_t {
+    f32x16_t acc;
+    if constexpr (decltype(R)::value == 0) {
+      acc = (f32x16_t){};
+    } else {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) acc[4 * g + x] = __uint_as_float(st[g][x]);
+    }
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc) acc = mfma(as_bf16x8(fr[kc]), as_bf16x8(bfr[kc]), acc);
+    return acc;
+  };
+  // P of a block from its S and lse, masked causally (query tile t, half
+  // qb), rounded to bf16 in the B-operand layout: half h holds queries
+  // 16h + {4hi..4hi+3, 8+4hi..8+4hi+3}.  lse = -inf only for a row that sees
+  // no key anywhere, hence none of this pair: the mask (a select) zeroes its
+  // elements.
+  auto make_p = [&](const f32x16_t& s, const u32x4_t (&lr)[4], int t, int qb, u32x4_t (&pf)[2]) {
+    float pw[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        pw[4 * g + x] = __builtin_amdgcn_exp2f(fmaf(s[4 * g + x], c, -__uint_as_float(lr[g][x]) * kLog2e));
+    const int64_t q0pos = p.q_pos0 + (int64_t)t * kTR + 32 * qb;
+    if (p.causal && kpos_wave_last > q0pos) {
+      const int lo = (int)min(max(kpos - q0pos - 4 * hi, (int64_t)-1), (int64_t)33);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) pw[4 * g + x] = (8 * g + x >= lo) ? pw[4 * g + x] : 0.f;
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const u32x4_t v = lds_b128(sa + 256u + (uint32_t)((32 * qb + 8 * g) * 4));
-#pragma unroll
-      for (int x = 0; x < 4; ++x) r[4 * g + x] = __uint_as_float(v[x]);
+      const int half = g / 2, xx = 2 * (g & 1);
+      pf[half][xx] = pack_bf16x2(pw[4 * g], pw[4 * g + 1]);
+      pf[half][xx + 1] = pack_bf16x2(pw[4 * g + 2], pw[4 * g + 3]);
     }
-    return r;
   };
-  // dV/dK MFMA m: half = m / (2 MD), md = (m / 2) % MD; even: dV^T += dO^T P
-  // (transposed dO fragment), odd: dK^T += Q^T dS (transposed Q fragment).
-  auto kv_read = [&](auto M, const uint32_t (&ta)[C::MD][2], auto QB) -> bf16x8_t {
-    constexpr int m = decltype(M)::value, qb = decltype(QB)::value;
-    constexpr int half = m / (2 * C::MD), md = (m / 2) % C::MD;
-    constexpr uint32_t o = (uint32_t)((32 * qb + 16 * half) * C::ROWB + ((m & 1) ? 0 : C::TILE));
-    return tr_frag(ta[md][0] + o, ta[md][1] + o);
-  };
-  auto kv_mfma = [&](auto M, const PdsBlock& w, const bf16x8_t& fr) {
-    constexpr int m = decltype(M)::value;
-    constexpr int half = m / (2 * C::MD), md = (m / 2) % C::MD;
-    if constexpr ((m & 1) == 0) dva[md] = mfma(fr, as_bf16x8(w.pf[half]), dva[md]);
-    else dka[md] = mfma(fr, as_bf16x8(w.df[half]), dka[md]);
-  };
-
-  // Softmax-gradient work of a block: P = exp2(c*s - lse*log2e) and
-  // dS = P (dP - D) = -P (D - dP), masked causally, rounded to bf16.  Item k
-  // of the 24: for each 4-query group g = k / 6: the group's lse, its four
-  // elements, then the mask and the bf16 packs.  The group's lse is read
-  // from LDS a few slots before its first item.
-  struct SmState {
-    u32x4_t lr[4];
-    float nl[4];
-    float pw[16], dsw[16];
-    int lo;
-    bool msk;
-  };
-  auto sm_read = [&](SmState& st, uint32_t sa, auto QB, auto G) {
-    constexpr int qb = decltype(QB)::value, g = decltype(G)::value;
-    st.lr[g] = lds_b128(sa + (uint32_t)((32 * qb + 8 * g) * 4));
-  };
-  auto sm_setup = [&](SmState& st, int t, auto QB) {
-    constexpr int qb = decltype(QB)::value;
-    const int qb0 = t * kTR + 32 * qb;
-    const int64_t q0pos = p.q_pos0 + qb0;
-    st.msk = p.causal && kpos_wave_last > q0pos;
-    const int64_t lo = kpos - q0pos - 4 * hi;
-    st.lo = (int)min(max(lo, (int64_t)-1), (int64_t)33);
-  };
-  auto sm_item = [&](auto K, SmState& st, const SdBlock& sd, PdsBlock& w) {
-    constexpr int k = decltype(K)::value, g = k / 6, r = k % 6;
-    if constexpr (r == 0) {
-      // lse = -inf only for a row that sees no key anywhere, so none of
-      // this pair: the causal mask below (a select) zeroes its elements
+  // dS = P (dP - D) = -P (D - dP) of a block (role 1), from its bf16 P.
+  auto make_ds = [&](const u32x4_t (&pf)[2], const f32x16_t& dm, u32x4_t (&df)[2]) {
 #pragma unroll
-      for (int x = 0; x < 4; ++x) st.nl[x] = -__uint_as_float(st.lr[g][x]) * kLog2e;
-    } else if constexpr (r <= 4) {
-      constexpr int x = r - 1, j = 4 * g + x;
-      const float pr = __builtin_amdgcn_exp2f(fmaf(sd.s[j], c, st.nl[x]));
-      st.pw[j] = pr;
-      st.dsw[j] = -(pr * sd.dp[j]);
-    } else {
-      if (st.msk) {
+    for (int g = 0; g < 4; ++g) {
+      const int half = g / 2, xx = 2 * (g & 1);
+      float d4[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const bool vis = 8 * g + x >= st.lo;
-          st.pw[4 * g + x] = vis ? st.pw[4 * g + x] : 0.f;
-          st.dsw[4 * g + x] = vis ? st.dsw[4 * g + x] : 0.f;
-        }
+      for (int y = 0; y < 2; ++y) {
+        const uint32_t w = pf[half][xx + y];
+        d4[2 * y] = -(__uint_as_float(w << 16) * dm[4 * g + 2 * y]);
+        d4[2 * y + 1] = -(__uint_as_float(w & 0xffff0000u) * dm[4 * g + 2 * y + 1]);
       }
-      constexpr int half = g / 2, xx = 2 * (g & 1);
-      w.pf[half][xx] = pack_bf16x2(st.pw[4 * g], st.pw[4 * g + 1]);
-      w.pf[half][xx + 1] = pack_bf16x2(st.pw[4 * g + 2], st.pw[4 * g + 3]);
-      w.df[half][xx] = pack_bf16x2(st.dsw[4 * g], st.dsw[4 * g + 1]);
-      w.df[half][xx + 1] = pack_bf16x2(st.dsw[4 * g + 2], st.dsw[4 * g + 3]);
-      pin(w.pf[half]);
-      pin(w.df[half]);
+      df[half][xx] = pack_bf16x2(d4[0], d4[1]);
+      df[half][xx + 1] = pack_bf16x2(d4[2], d4[3]);
     }
   };
-  constexpr auto kSlotOfItem = [](int k) { return 1 + (k * (kSlots - 2)) / kItems; };
-
-  // Per-tile addresses: row fragments of tile tau+1 (ra), transposed
-  // fragments of tile tau (ta), statistics of tiles tau and tau+1.  Moving
-  // to the next tile adds the distance between the stages' bases.
-  uint32_t ra[C::KC], ta[C::MD][2], sa_cur, sa_nxt;
+  // Transposed fragments of a block for dV^T += dO^T P (DK = false, dO
+  // tile) or dK^T += Q^T dS (DK = true, Q tile), the wave's half of d;
+  // fragment 2*mh + hf covers 32-row block mh of the half, queries 16 hf ..
+  // of the block.
+  auto kv_frags = [&](auto S, auto QB, auto DK, bf16x8_t (&fr)[2 * MH]) {
+    constexpr uint32_t so = (uint32_t)(decltype(S)::value * C::TILE + (decltype(DK)::value ? kQ0 : kO0));
 #pragma unroll
-  for (int kc = 0; kc < C::KC; ++kc) ra[kc] = lds0 + row_ofs<D>(l32, kc, hi);                       // stage 0
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint32_t o = so + (uint32_t)((32 * decltype(QB)::value + 16 * hf) * C::ROWB);
 #pragma unroll
-  for (int md = 0; md < C::MD; ++md) {
-    ta[md][0] = lds0 + (uint32_t)(kKvStages - 1) * kStage + tr_ofs<D>(lane, md, 0);   // stage S-1
-    ta[md][1] = lds0 + (uint32_t)(kKvStages - 1) * kStage + tr_ofs<D>(lane, md, 1);
-  }
-  auto move_addr = [&](int s_cur, int s_nxt, uint32_t d_cur, uint32_t d_nxt) {
-#pragma unroll
-    for (int kc = 0; kc < C::KC; ++kc) {
-      ra[kc] += d_nxt;
-      pin(ra[kc]);
+      for (int mh = 0; mh < MH; ++mh) fr[2 * mh + hf] = tr_frag(ta[mh][0] + o, ta[mh][1] + o);
     }
-#pragma unroll
-    for (int md = 0; md < C::MD; ++md) {
-      ta[md][0] += d_cur;
-      ta[md][1] += d_cur;
-      pin(ta[md][0]);
-      pin(ta[md][1]);
-    }
-    sa_cur = lds0 + kStats + (uint32_t)s_cur * 512u + (uint32_t)(16 * hi);
-    sa_nxt = lds0 + kStats + (uint32_t)s_nxt * 512u + (uint32_t)(16 * hi);
   };
-
-  // One pipeline step: dV/dK of the block in `kvw` (tile tau, half QB of
-  // the tile), the softmax gradient of `smi` into `smo` (statistics at
-  // sa_sm, query tile t_sm, half 1 - QB) and S/dP of the block after it into
-  // `sdo` (tile tau+1, half QB, statistics at sa_sd).
-  auto step = [&](auto QB, const PdsBlock& kvw, const SdBlock& smi, PdsBlock& smo, SdBlock& sdo,
-                  uint32_t sa_sm, int t_sm, uint32_t sa_sd) {
-    constexpr int qb = decltype(QB)::value;
-    using SQB = Step<1 - qb>;
-    SmState st;
-    sm_read(st, sa_sm, SQB{}, Step<0>{});
-    const f32x16_t dinit = d_init(sa_sd, QB);
-    sm_setup(st, t_sm, SQB{});
-    bf16x8_t kvfr[NKV];
-    u32x4_t sdfr[NSD];
-    static_for<kLead>([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      if constexpr ((i & 1) == 0) kvfr[i / 2] = kv_read(Step<i / 2>{}, ta, QB);
-      else sdfr[i / 2] = sd_read(Step<i / 2>{}, ra, QB);
-    });
-    static_for<kSlots>([&](auto I) {
-      constexpr int i = decltype(I)::value, ia = i + kLead;
-      if constexpr (ia < kSlots) {
-        if constexpr ((ia & 1) == 0) kvfr[ia / 2] = kv_read(Step<ia / 2>{}, ta, QB);
-        else sdfr[ia / 2] = sd_read(Step<ia / 2>{}, ra, QB);
+  auto kv_mfma = [&](auto DK, const bf16x8_t (&fr)[2 * MH], const u32x4_t (&w)[2]) {
+#pragma unroll
+    for (int mh = 0; mh < MH; ++mh)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        if constexpr (decltype(DK)::value) dka[mh] = mfma(fr[2 * mh + hf], as_bf16x8(w[hf]), dka[mh]);
+        else dva[mh] = mfma(fr[2 * mh + hf], as_bf16x8(w[hf]), dva[mh]);
       }
-      static_for<3>([&](auto G) {
-        constexpr int g = decltype(G)::value + 1;
-        if constexpr (kSlotOfItem(6 * g) - 3 == i) sm_read(st, sa_sm, SQB{}, Step<g>{});
-      });
-      if constexpr ((i & 1) == 0) kv_mfma(Step<i / 2>{}, kvw, kvfr[i / 2]);
-      else sd_mfma(Step<i / 2>{}, sdo, sdfr[i / 2], dinit);
-      static_for<kItems>([&](auto K) {
-        if constexpr (kSlotOfItem(decltype(K)::value) == i) sm_item(K, st, smi, smo);
-      });
-      __builtin_amdgcn_sched_barrier(0);
-    });
+  };
+  auto x_write = [&](uint32_t buf, const u32x4_t (&v)[2]) {
+    *reinterpret_cast<SQKV_LDS u32x4_t*>((size_t)(xa + buf)) = v[0];
+    *reinterpret_cast<SQKV_LDS u32x4_t*>((size_t)(xa + buf + 1024)) = v[1];
+  };
+  auto x_read = [&](uint32_t buf, u32x4_t (&v)[2]) {
+    v[0] = lds_b128(xa + buf);
+    v[1] = lds_b128(xa + buf + 1024);
   };
 
-  // ---- prologue: tiles 0 and 1 in flight, S/dP of blocks 0 and 1, P/dS of block 0
+  // ---- the walk (one copy of the loop per role) ------------------------------
   int gi_d = 0, t_d = t0;                     // next tile to copy
   auto advance = [&](int& gi, int& t) {
     if (++t == T) {
@@ -727,62 +676,137 @@ attn_bwd_dkdv_kernel(BwdParams p) {
   }
   drain_and_sync();
 
-  SdBlock sA, sB;
-  PdsBlock wA, wB;
-  sa_nxt = lds0 + kStats + (uint32_t)(16 * hi);   // statistics of tile 0 (stage 0)
-  {
-    const f32x16_t d0 = d_init(sa_nxt, Step<0>{}), d1 = d_init(sa_nxt, Step<1>{});
-    static_for<NSD>([&](auto M) { sd_mfma(M, sA, sd_read(M, ra, Step<0>{}), d0); });
-    static_for<NSD>([&](auto M) { sd_mfma(M, sB, sd_read(M, ra, Step<1>{}), d1); });
-    SmState st;
-    static_for<4>([&](auto G) { sm_read(st, sa_nxt, Step<0>{}, G); });
-    sm_setup(st, t0, Step<0>{});
-    static_for<kItems>([&](auto K) { sm_item(K, st, sA, wA); });
-  }
-
-  int s_cur = 0;                              // stage of tile tau
-  int t_cur = t0, gi_cur = 0;                 // query tile of tau
-  for (int tau = 0; tau < NT; ++tau) {
-    if (tau > 0) drain_and_sync();            // tile tau+1 landed; tile tau-1 no longer read
-    const int s_nxt = s_cur == kKvStages - 1 ? 0 : s_cur + 1;
-    if (tau + 2 < NT) {
-      const int s_dma = s_nxt == kKvStages - 1 ? 0 : s_nxt + 1;   // the stage of tile tau-1
-      issue_tile(gi_d, t_d, s_dma);
-      advance(gi_d, t_d);
+  auto walk = [&](auto R) {
+    constexpr int r = decltype(R)::value;
+    // w[u & 1]: P of block u (role 0) or dS of block u (role 1); dm: role 1's
+    // D - dP of the block whose dS comes next.
+    u32x4_t w[2][2];
+    f32x16_t dm;
+    // The row fragments of an even step (and role 1's D of its block u+1)
+    // come from a tile landed before the barrier ahead of it, so they are
+    // read before that barrier.
+    u32x4_t pre_fr[C::KC], pre_st[4];
+    auto prefetch = [&](auto SU1) {
+      sd_frags(SU1, Step<1>{}, pre_fr);
+      if constexpr (r == 1) stats(SU1, Step<1>{}, pre_st);
+    };
+    {
+      u32x4_t fr[C::KC], st[4];
+      sd_frags(Step<0>{}, Step<0>{}, fr);
+      stats(Step<0>{}, Step<0>{}, st);
+      if constexpr (r == 0) {
+        make_p(sd_mfma(R, fr, st), st, t0, 0, w[0]);
+        x_write(0u, w[0]);
+      } else {
+        dm = sd_mfma(R, fr, st);
+      }
     }
-    int gi_n = gi_cur, t_nxt = t_cur;
+    prefetch(Step<0>{});
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    asm volatile("s_barrier" ::: "memory");
+
+    int t_cur = t0, t_nxt = t0, gi_n = 0;     // query tiles of tau and tau+1
     advance(gi_n, t_nxt);
-    // ra moves from tile tau's stage to tile tau+1's, ta from tau-1's to tau's
-    const uint32_t back = (uint32_t)(-(int)((kKvStages - 1) * kStage));
-    move_addr(s_cur, s_nxt, s_cur == 0 ? back : kStage, tau == 0 ? kStage : (s_nxt == 0 ? back : kStage));
-    step(Step<0>{}, wA, sB, wB, sA, sa_cur, t_cur, sa_nxt);   // dV/dK(2tau), P/dS(2tau+1), S/dP(2tau+2)
-    step(Step<1>{}, wB, sA, wA, sB, sa_nxt, t_nxt, sa_nxt);   // dV/dK(2tau+1), P/dS(2tau+2), S/dP(2tau+3)
-    s_cur = s_nxt;
-    t_cur = t_nxt;
-    gi_cur = gi_n;
-  }
+
+    // One step: block u = 2 tau + QB; SP, SC, SN are the stages of tiles
+    // tau-1, tau, tau+1.
+    auto step = [&](auto SP, auto SC, auto SN, auto QB, int tau) {
+      constexpr int qb = decltype(QB)::value;
+      using SU1 = std::conditional_t<qb == 0, decltype(SC), decltype(SN)>;   // stage of block u+1
+      using SM1 = std::conditional_t<qb == 0, decltype(SP), decltype(SC)>;  // stage of block u-1
+      using QO = Step<1 - qb>;                                               // half of blocks u+1, u-1
+      const int u = 2 * tau + qb;
+      const bool nxt = u + 1 < NB, cur = u < NB, prv = u >= 1 && u <= NB;
+      u32x4_t fr[C::KC], st[4], xw[2];
+      bf16x8_t fv[2 * MH], fk[2 * MH];
+      if constexpr (qb == 0) {
+#pragma unroll
+        for (int kc = 0; kc < C::KC; ++kc) fr[kc] = pre_fr[kc];
+        if constexpr (r == 0) kv_frags(SC, QB, Step<0>{}, fv);
+        if constexpr (r == 1) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) st[g] = pre_st[g];
+        }
+      } else {
+        sd_frags(SU1{}, QO{}, fr);
+        if constexpr (r == 1) stats(SU1{}, QO{}, st);   // D of block u+1
+        if constexpr (r == 0) kv_frags(SC, QB, Step<0>{}, fv);
+      }
+      if constexpr (r == 1) x_read((uint32_t)qb * kXchg, xw);   // P of block u
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (r == 0) {
+        const f32x16_t a = sd_mfma(R, fr, st);   // S of block u+1 (st unused: from 0)
+        // read while those run: the dK fragments, dS of block u-1, lse of block u+1
+        kv_frags(SM1{}, QO{}, Step<1>{}, fk);
+        x_read((uint32_t)(2 + ((u + 1) & 1)) * kXchg, xw);
+        stats(SU1{}, QO{}, st);
+        if (cur) kv_mfma(Step<0>{}, fv, w[qb]);
+        if (prv) kv_mfma(Step<1>{}, fk, xw);
+        if (nxt) {
+          make_p(a, st, qb == 0 ? t_cur : t_nxt, 1 - qb, w[1 - qb]);
+          x_write((uint32_t)(1 - qb) * kXchg, w[1 - qb]);
+        }
+      } else {
+        // dS of block u first (VALU while the partner wave's S products
+        // run), then D - dP of block u+1 into the same registers
+        if (cur) {
+          make_ds(xw, dm, w[qb]);
+          x_write((uint32_t)(2 + qb) * kXchg, w[qb]);
+        }
+        dm = sd_mfma(R, fr, st);
+        kv_frags(SC, QB, Step<0>{}, fv);
+        kv_frags(SM1{}, QO{}, Step<1>{}, fk);
+        if (cur) kv_mfma(Step<0>{}, fv, xw);
+        if (prv) kv_mfma(Step<1>{}, fk, w[1 - qb]);
+      }
+      if constexpr (qb == 0) {
+        // the next step reads tile tau+1
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        asm volatile("s_barrier" ::: "memory");
+        if (tau + 2 < NT) {
+          issue_tile(gi_d, t_d, decltype(SP)::value);   // tile tau+2 takes the stage of tile tau-1
+          advance(gi_d, t_d);
+        }
+      } else {
+        prefetch(SN);   // block u+2: tile tau+1, half 1
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+        asm volatile("s_barrier" ::: "memory");
+        t_cur = t_nxt;
+        advance(gi_n, t_nxt);
+      }
+    };
+    for (int tau = 0; 2 * tau <= NB; tau += 3) {
+      step(Step<2>{}, Step<0>{}, Step<1>{}, Step<0>{}, tau);
+      step(Step<2>{}, Step<0>{}, Step<1>{}, Step<1>{}, tau);
+      step(Step<0>{}, Step<1>{}, Step<2>{}, Step<0>{}, tau + 1);
+      step(Step<0>{}, Step<1>{}, Step<2>{}, Step<1>{}, tau + 1);
+      step(Step<1>{}, Step<2>{}, Step<0>{}, Step<0>{}, tau + 2);
+      step(Step<1>{}, Step<2>{}, Step<0>{}, Step<1>{}, tau + 2);
+    }
+  };
+  if (role == 0) walk(Step<0>{});
+  else walk(Step<1>{});
   __builtin_amdgcn_s_waitcnt(0);   // no DMA may outlive the workgroup's LDS
 
   if (key_ok) {
-
     float* dkr = p.dk + b * p.dk_sb + hk * p.dk_sh + (int64_t)key * p.dk_sn;
     float* dvr = p.dv + b * p.dv_sb + hk * p.dv_sh + (int64_t)key * p.dv_sn;
 #pragma unroll
-    for (int md = 0; md < C::MD; ++md)
+    for (int mh = 0; mh < MH; ++mh)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * md + 8 * g + 4 * hi;
+        const int d0 = 32 * (role * MH + mh) + 8 * g + 4 * hi;
         float4 x = *reinterpret_cast<float4*>(dkr + d0);
-        x.x = fmaf(p.scale, dka[md][4 * g + 0], x.x);
-        x.y = fmaf(p.scale, dka[md][4 * g + 1], x.y);
-        x.z = fmaf(p.scale, dka[md][4 * g + 2], x.z);
-        x.w = fmaf(p.scale, dka[md][4 * g + 3], x.w);
+        x.x = fmaf(p.scale, dka[mh][4 * g + 0], x.x);
+        x.y = fmaf(p.scale, dka[mh][4 * g + 1], x.y);
+        x.z = fmaf(p.scale, dka[mh][4 * g + 2], x.z);
+        x.w = fmaf(p.scale, dka[mh][4 * g + 3], x.w);
         *reinterpret_cast<float4*>(dkr + d0) = x;
         float4 y = *reinterpret_cast<float4*>(dvr + d0);
-        y.x += dva[md][4 * g + 0];
-        y.y += dva[md][4 * g + 1];
-        y.z += dva[md][4 * g + 2];
-        y.w += dva[md][4 * g + 3];
+        y.x += dva[mh][4 * g + 0];
+        y.y += dva[mh][4 * g + 1];
+        y.z += dva[mh][4 * g + 2];
+        y.w += dva[mh][4 * g + 3];
         *reinterpret_cast<float4*>(dvr + d0) = y;
       }
   }
@@ -820,15 +844,9 @@ __global__ void __launch_bounds__(256) bwd_rowdot_kernel(RowDotParams p) {
   if (r < rows && sub == 0) p.D[r] = acc;
 }
 
-// LDS of the dK/dV kernel: three stages of (Q tile, dO tile) and of the
-// tiles' lse and D.
-template <int D>
-constexpr int kKvLds = kKvStages * (2 * BCfg<D, kKvWaves>::TILE + 512);
-
 template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t s) {
   using Cq = BCfg<D, kDqWaves>;
-  using Ck = BCfg<D, kKvWaves>;
   static std::atomic<uint64_t> dq_set{0}, kv_set{0};
   hipError_t e = allow_dyn_lds(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D>), 4 * Cq::TILE, dq_set);
   if (e != hipSuccess) return e;
