@@ -5,66 +5,83 @@
 // sum (normaliser) and the weighted sum of values; the chunk's partial is
 // then merged into the running output (online softmax).
 //
-// This is the exact-precision variant (no reduced-precision products): one
-// lane owns one query row and keeps q and its output accumulator in
-// registers; the four wavefronts of a workgroup share its 64 rows and split
-// the visit's 32-key tiles between them (tile g goes to wave g mod 4), each
-// running its own online softmax over its tiles, staged in its own LDS
-// region (every lane reads the same K/V element at a time: an LDS
-// broadcast).  At the end the waves' partial states of a row are merged in
-// LDS (log-sum-exp weights), each wave finishing its share of the columns.
-// The key/value chunks of a ring visit are met in ring order within one
-// launch.  It is meant for correctness-critical fp32 use; the bf16 MFMA
-// kernel is the throughput path.
+// This is the exact-precision variant: the products run on the fp32 matrix
+// cores (v_mfma_f32_32x32x2_f32: fp32 operands, fp32 accumulation, no
+// reduced-precision rounding).  A workgroup takes 32 query rows; its four
+// wavefronts split the visit's 32-key tiles between them (tile g goes to
+// wave g mod 4), each running its own online softmax over its tiles, staged
+// in its own LDS region.  Per tile a wave forms S^T = K Q^T (keys on the
+// MFMA M axis, so a lane holds 16 keys of ONE query: the row maximum and sum
+// are lane-local plus one exchange with the lane holding the query's other
+// 16 keys) and O^T += V^T P^T, where P^T is the S^T registers themselves
+// (the k index of a step pairs key 8g + x of one lane half with key
+// 8g + 4 + x of the other).  Q^T stays in registers (lane half h holds
+// d = h*D/2 .. h*D/2 + D/2 - 1 of its query).  At the end the waves' partial
+// states of a row are merged in LDS (log-sum-exp weights).  The key/value
+// chunks of a ring visit are met in ring order within one launch.  It is
+// meant for correctness-critical fp32 use; the bf16 kernel is the
+// throughput path.
 #include "attn_common.h"
 
 namespace sqkv {
 namespace {
 
-constexpr int kRows = 64;    // query rows per workgroup (one per lane)
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kRows = 32;    // query rows per workgroup
 constexpr int kTile = 32;    // keys per LDS tile
+constexpr int kSplit = 4;    // wavefronts, each with every kSplit-th tile
 
 template <int D>
 struct F32Cfg {
-  static constexpr int SPLIT = 4;                              // wavefronts, each with every SPLIT-th tile
-  // per wave: its K and V tile; reused at the end for the partial states
-  static constexpr int TILES = SPLIT * 2 * kTile * D;         // floats
-  static constexpr int STATE = kRows * (D + 2) * SPLIT;       // (o[D], m, l) per row and wave
-  static constexpr int FLOATS = TILES > STATE ? TILES : STATE;
+  static constexpr int KROW = D + 4;                            // padded K row (floats): conflict-free b128 reads
+  static constexpr int WAVE = kTile * KROW + kTile * D;         // one wave's K and V tile (floats)
+  static constexpr int STATE = kSplit * kRows * (D + 2);        // (o[D], m, l) per wave and row
+  static constexpr int FLOATS = kSplit * WAVE > STATE ? kSplit * WAVE : STATE;
   static_assert(FLOATS * 4 <= 160 * 1024, "LDS");
-  static_assert(D % (4 * SPLIT) == 0, "whole float4 column groups per wave");
+  static_assert(D % 32 == 0, "whole 32-row blocks of d");
 };
 
+__device__ __forceinline__ f32x16_t mfma_f32(float a, float b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
 template <int D>
-__global__ void __launch_bounds__(kRows * F32Cfg<D>::SPLIT) attn_f32_kernel(AttnParams p) {
-  constexpr int kSplit = F32Cfg<D>::SPLIT;
+__global__ void __launch_bounds__(64 * kSplit) attn_f32_kernel(AttnParams p) {
+  using C = F32Cfg<D>;
+  constexpr int MB = D / 32;   // 32-row blocks of d in O^T
   extern __shared__ float lds_f[];
-  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kRows);
-  const int lane = threadIdx.x % kRows;
-  float* ks = lds_f + wave * 2 * kTile * D;    // [kTile][D]
-  float* vs = ks + kTile * D;                  // [kTile][D]
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / 64);
+  const int lane = threadIdx.x % 64;
+  const int l32 = lane & 31, hi = lane >> 5;
+  float* ks = lds_f + wave * C::WAVE;          // [kTile][KROW]
+  float* vs = ks + kTile * C::KROW;            // [kTile][D]
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int hk = h / p.group;
-  const int t = blockIdx.x * kRows + lane;
+  const int q0 = blockIdx.x * kRows;
+  const int t = q0 + l32;                      // this lane's query row
   const bool row_ok = t < p.n_q;
   const float* qrow = static_cast<const float*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)(row_ok ? t : 0) * p.q_sn;
   const float* kb0 = static_cast<const float*>(p.k) + b * p.k_sb + hk * p.k_sh;
   const float* vb0 = static_cast<const float*>(p.v) + b * p.v_sb + hk * p.v_sh;
 
-  float q[D];
-  float o[D];
+  // Q^T operand: d = hi * D/2 + s of the lane's query (zeros past n_q)
+  float q[D / 2];
 #pragma unroll
-  for (int e = 0; e < D; e += 4) {
-    float4 x = row_ok ? *reinterpret_cast<const float4*>(qrow + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int e = 0; e < D / 2; e += 4) {
+    const float4 x = row_ok ? *reinterpret_cast<const float4*>(qrow + hi * (D / 2) + e) : make_float4(0.f, 0.f, 0.f, 0.f);
     q[e] = x.x; q[e + 1] = x.y; q[e + 2] = x.z; q[e + 3] = x.w;
-    o[e] = o[e + 1] = o[e + 2] = o[e + 3] = 0.f;
   }
+  // O^T: element j of block mb holds d = 32 mb + 8 (j/4) + 4 hi + j%4 of the query
+  f32x16_t o[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) o[mb] = (f32x16_t){};
   const float c = p.scale_log2;
   const int64_t qpos = p.q_pos0 + t;
-  const int64_t tmax = min((int64_t)blockIdx.x * kRows + kRows - 1, (int64_t)p.n_q - 1);
-  float m = kNegInf;  // running max of logits, base-2 units
-  float l = 0.f;      // running normaliser
+  const int64_t tmax = min((int64_t)q0 + kRows - 1, (int64_t)p.n_q - 1);
+  float m = kNegInf;  // running max of logits, base-2 units (same in both lane halves)
+  float l = 0.f;      // this lane's part of the running normaliser (its 16 keys of each tile)
   int g = 0;          // tile number within the visit
   // chunks in ring order: visit s reads chunk j = (rank - s) mod P
   for (int s = 0; s < p.nseg; ++s) {
@@ -80,88 +97,118 @@ __global__ void __launch_bounds__(kRows * F32Cfg<D>::SPLIT) attn_f32_kernel(Attn
       // this wave's region only: the wave's own LDS accesses complete in
       // order, so no workgroup barrier is needed (and the waves may make
       // different numbers of tiles)
-      for (int i = lane; i < kTile * D / 4; i += kRows) {
-        int r = i / (D / 4), e = (i % (D / 4)) * 4;
-        int64_t u = k0 + r;
+      for (int i = lane; i < kTile * D / 4; i += 64) {
+        const int r = i / (D / 4), e = (i % (D / 4)) * 4;
+        const int64_t u = k0 + r;
         float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
         if (u < n_keys) {
           kx = *reinterpret_cast<const float4*>(kb + u * p.k_sn + e);
           vx = *reinterpret_cast<const float4*>(vb + u * p.v_sn + e);
         }
-        *reinterpret_cast<float4*>(ks + r * D + e) = kx;
+        *reinterpret_cast<float4*>(ks + r * C::KROW + e) = kx;
         *reinterpret_cast<float4*>(vs + r * D + e) = vx;
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      float sc[kTile];
+      // S^T = K Q^T: step e pairs d = e (lane half 0) with d = D/2 + e (half 1)
+      f32x16_t st = (f32x16_t){};
+      const float* krow = ks + l32 * C::KROW + hi * (D / 2);
+#pragma unroll
+      for (int e = 0; e < D / 2; e += 4) {
+        const float4 kx = *reinterpret_cast<const float4*>(krow + e);
+        st = mfma_f32(kx.x, q[e], st);
+        st = mfma_f32(kx.y, q[e + 1], st);
+        st = mfma_f32(kx.z, q[e + 2], st);
+        st = mfma_f32(kx.w, q[e + 3], st);
+      }
+      // element jj: key 8 (jj/4) + 4 hi + jj%4 of the tile, masked past the
+      // chunk's visible keys and (causal) after the query
       float tmx = kNegInf;
 #pragma unroll
-      for (int jj = 0; jj < kTile; ++jj) {
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < D; ++e) acc = fmaf(q[e], ks[jj * D + e], acc);
-        int64_t u = k0 + jj;
-        bool vis = u < n_keys && (!p.causal || kpos0 + u <= qpos);
-        sc[jj] = vis ? acc * c : kNegInf;
-        tmx = fmaxf(tmx, sc[jj]);
+      for (int jj = 0; jj < 16; ++jj) {
+        const int64_t u = k0 + 8 * (jj / 4) + 4 * hi + (jj % 4);
+        const bool vis = u < n_keys && (!p.causal || kpos0 + u <= qpos);
+        st[jj] = vis ? st[jj] * c : kNegInf;
+        tmx = fmaxf(tmx, st[jj]);
       }
-      float mn = fmaxf(m, tmx);
-      if (mn != kNegInf) {
-        float alpha = (m == mn) ? 1.f : exp2f(m - mn);
-        l *= alpha;
+      tmx = fmaxf(tmx, __shfl_xor(tmx, 32));   // the query's other 16 keys
+      // no branch on the row's state: the matrix products below run for the
+      // whole wave whatever the lane mask, so a row that has seen no key yet
+      // keeps alpha = 1 and gets weights 0
+      const float mn = fmaxf(m, tmx);
+      const float alpha = (mn == kNegInf || m == mn) ? 1.f : exp2f(m - mn);
+      l *= alpha;
 #pragma unroll
-        for (int e = 0; e < D; ++e) o[e] *= alpha;
-        m = mn;
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int jj = 0; jj < kTile; ++jj) {
-          float pj = exp2f(sc[jj] - m);
-          l += pj;
+        for (int jj = 0; jj < 16; ++jj) o[mb][jj] *= alpha;
+      m = mn;
 #pragma unroll
-          for (int e = 0; e < D; ++e) o[e] = fmaf(pj, vs[jj * D + e], o[e]);
+      for (int jj = 0; jj < 16; ++jj) {
+        st[jj] = (st[jj] == kNegInf) ? 0.f : exp2f(st[jj] - m);
+        l += st[jj];
+      }
+      // O^T += V^T P^T: step (gg, x) pairs key 8gg + x (half 0) with key
+      // 8gg + 4 + x (half 1), i.e. element 4gg + x of each lane
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          const float vx = vs[(8 * (jj / 4) + 4 * hi + (jj % 4)) * D + 32 * mb + l32];
+          o[mb] = mfma_f32(vx, st[jj], o[mb]);
         }
-      }
       // every lane's reads of this tile are done before the next one is staged
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
-  // Merge the waves' partial states of each row: state (o, m, l) of wave w
-  // for row `lane` sits at st + (w * kRows + lane) * (D + 2).
+  // Merge the waves' partial states of each row: state (o[D], m, l) of wave
+  // w for row n sits at stt + (w * kRows + n) * (D + 2).
   __syncthreads();   // every wave is done with its tiles
-  float* st = lds_f;
+  float* stt = lds_f;
   {
-    float* mine = st + (wave * kRows + lane) * (D + 2);
+    float* mine = stt + (wave * kRows + l32) * (D + 2);
 #pragma unroll
-    for (int e = 0; e < D; ++e) mine[e] = o[e];
-    mine[D] = m;
-    mine[D + 1] = l;
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) mine[32 * mb + 8 * gg + 4 * hi + x] = o[mb][4 * gg + x];
+    const float lsum = l + __shfl_xor(l, 32);
+    if (hi == 0) {
+      mine[D] = m;
+      mine[D + 1] = lsum;
+    }
   }
   __syncthreads();
+  // thread -> (row n, column slice): 8 threads per row, D/8 columns each
+  const int n = threadIdx.x / 8;
+  const int t_out = q0 + n;
+  if (t_out >= p.n_q) return;
   float M = kNegInf;
 #pragma unroll
-  for (int w = 0; w < kSplit; ++w) M = fmaxf(M, st[(w * kRows + lane) * (D + 2) + D]);
+  for (int w = 0; w < kSplit; ++w) M = fmaxf(M, stt[(w * kRows + n) * (D + 2) + D]);
   float a[kSplit];
   float L = 0.f;
 #pragma unroll
   for (int w = 0; w < kSplit; ++w) {
-    const float mw = st[(w * kRows + lane) * (D + 2) + D];
+    const float mw = stt[(w * kRows + n) * (D + 2) + D];
     a[w] = (mw == kNegInf) ? 0.f : exp2f(mw - M);
-    L += a[w] * st[(w * kRows + lane) * (D + 2) + D + 1];
+    L += a[w] * stt[(w * kRows + n) * (D + 2) + D + 1];
   }
-  if (!row_ok) return;
-  // chunk partial: normalised output and natural-log lse; this wave writes
-  // columns [wave * D / kSplit, (wave + 1) * D / kSplit) of the row
-  float lse_j = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
-  float inv = (L > 0.f) ? 1.f / L : 0.f;
+  // chunk partial: normalised output and natural-log lse, merged with the
+  // running state when there is one
+  const float lse_j = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
+  const float inv = (L > 0.f) ? 1.f / L : 0.f;
   const int64_t bh_row = (int64_t)b * p.Hq + h;
   float wi = 0.f, wj = 1.f, lse = lse_j;
-  if (p.o_in != nullptr) lse = lse_merge_weights(p.lse_in[bh_row * p.lse_in_hs + t], lse_j, wi, wj);
-  const int64_t ooff = b * p.oo_sb + h * p.oo_sh + (int64_t)t * p.oo_sn;
-  const int64_t ioff = b * p.oi_sb + h * p.oi_sh + (int64_t)t * p.oi_sn;
-  constexpr int kCols = D / kSplit;
-  const int e0 = wave * kCols;
+  if (p.o_in != nullptr) lse = lse_merge_weights(p.lse_in[bh_row * p.lse_in_hs + t_out], lse_j, wi, wj);
+  const int64_t ooff = b * p.oo_sb + h * p.oo_sh + (int64_t)t_out * p.oo_sn;
+  const int64_t ioff = b * p.oi_sb + h * p.oi_sh + (int64_t)t_out * p.oi_sn;
+  constexpr int kCols = D / 8;
+  const int e0 = (threadIdx.x % 8) * kCols;
 #pragma unroll
   for (int e = 0; e < kCols; e += 4) {
     float y[4];
@@ -169,7 +216,7 @@ __global__ void __launch_bounds__(kRows * F32Cfg<D>::SPLIT) attn_f32_kernel(Attn
     for (int i = 0; i < 4; ++i) {
       float acc = 0.f;
 #pragma unroll
-      for (int w = 0; w < kSplit; ++w) acc = fmaf(a[w], st[(w * kRows + lane) * (D + 2) + e0 + e + i], acc);
+      for (int w = 0; w < kSplit; ++w) acc = fmaf(a[w], stt[(w * kRows + n) * (D + 2) + e0 + e + i], acc);
       y[i] = (wj != 0.f) ? wj * (acc * inv) : 0.f;
     }
     if (p.o_in != nullptr && wi != 0.f) {
@@ -180,7 +227,7 @@ __global__ void __launch_bounds__(kRows * F32Cfg<D>::SPLIT) attn_f32_kernel(Attn
     }
     store4(p.o_out, ooff + e0 + e, p.out_dtype, y);
   }
-  if (wave == 0) p.lse_out[bh_row * p.lse_out_hs + t] = lse;
+  if (threadIdx.x % 8 == 0) p.lse_out[bh_row * p.lse_out_hs + t_out] = lse;
 }
 
 }  // namespace
@@ -192,12 +239,12 @@ hipError_t launch_attn_f32(const AttnParams& p, int d, hipStream_t s) {
     static std::atomic<uint64_t> lds_set{0};
     hipError_t e = allow_dyn_lds(reinterpret_cast<const void*>(&attn_f32_kernel<128>), F32Cfg<128>::FLOATS * 4, lds_set);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(kRows * F32Cfg<128>::SPLIT), F32Cfg<128>::FLOATS * 4, s, p);
+    hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64 * kSplit), F32Cfg<128>::FLOATS * 4, s, p);
   } else {
     static std::atomic<uint64_t> lds_set{0};
     hipError_t e = allow_dyn_lds(reinterpret_cast<const void*>(&attn_f32_kernel<64>), F32Cfg<64>::FLOATS * 4, lds_set);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(kRows * F32Cfg<64>::SPLIT), F32Cfg<64>::FLOATS * 4, s, p);
+    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64 * kSplit), F32Cfg<64>::FLOATS * 4, s, p);
   }
   return hipGetLastError();
 }
