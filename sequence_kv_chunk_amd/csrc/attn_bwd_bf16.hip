@@ -433,13 +433,14 @@ attn_bwd_dq_kernel(BwdParams p, int n_qtiles) {
 constexpr int kKvRows = 128;    // keys per workgroup
 constexpr int kKvStages = 3;    // LDS stages of (Q tile, dO tile, lse, D)
 
-// Two waves per SIMD, a pair of waves per 32 keys.  Waves w and w + 4 (one SIMD) take the same 32 keys.  Wave w (role 0)
-// holds the K rows of the keys and forms S = Q K^T and P; wave w + 4 (role 1)
-// holds the -V rows and forms D - dP and dS = P (dP - D).  Each accumulates
-// dV^T and dK^T for its own half of d, so a wave holds half the accumulators
-// of the one-wave kernel and the pair issues the same MFMAs as one wave
-// there.  P goes from role 0 to role 1, and dS back, through LDS (bf16, lane
-// to lane in the B-operand layout), with one barrier per 32-query block.
+// Two waves per SIMD, a pair of waves per 32 keys.  Waves w and w + 4 (one
+// SIMD) take the same 32 keys.  Wave w (role 0) holds the K rows of the keys
+// and forms S = Q K^T and P; wave w + 4 (role 1) holds the -V rows and forms
+// D - dP and dS = P (dP - D).  Each accumulates dV^T and dK^T for its own
+// half of d, so a wave holds half the accumulators a single wave over the
+// same keys would, and the pair issues the MFMAs of one such wave.  P goes
+// from role 0 to role 1, and dS back, through LDS (bf16, lane to lane in the
+// B-operand layout), with one barrier per 32-query block.
 // Step u (blocks u = 0, 1, ... of the walk; the step after the last block
 // only finishes dK):
 //   role 0: S of block u+1 and its P (written out), dV^T += dO^T P of block
@@ -447,15 +448,15 @@ constexpr int kKvStages = 3;    // LDS stages of (Q tile, dO tile, lse, D)
 //   role 1: D - dP of block u+1, dS of block u (P written by role 0 in step
 //           u-1, D - dP from its own step u-1, written out), dV^T of block u,
 //           dK^T of block u-1.
-// A step issues its LDS reads ahead of its MFMAs (those of dK after the
-// S or D - dP products are under way), so that the two waves of a SIMD see
-// the read latency about once per step.  Tiles sit in three
-// LDS stages (the three Q tiles, then the three dO tiles, so that every
-// fragment offset fits a read's immediate field); the copy of tile tau+2 is
-// issued after the barrier that ends block 2tau, the last one to read tile
-// tau-1, and waited for at the barrier that ends block 2tau+2.  The loop
-// runs three tiles (six steps) per iteration so that every stage index and
-// every register of the two-block rotation is a constant.
+// A step issues its LDS reads ahead of its MFMAs (those of dK after the S or
+// D - dP products are under way; the row fragments of an even step before
+// the barrier ahead of it), so that the two waves of a SIMD see the read
+// latency about once per step.  Tiles sit in three LDS stages (the three Q
+// tiles, then the three dO tiles, then their lse and D); the copy of tile
+// tau+2 is issued after the barrier that ends block 2tau, the last one to
+// read tile tau-1, and waited for at the barrier that ends block 2tau+2.
+// The loop runs three tiles (six steps) per iteration so that every stage
+// index and every register of the two-block rotation is a constant.
 constexpr int kKvWaves = 8;
 constexpr uint32_t kXchg = 2 * 1024;   // one block's P or dS: two 1 KiB halves of 64 lanes x 16 bytes
 
