@@ -47,6 +47,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 (published; matrix and vector alike)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 METRIC = "chunked-attention TFLOP/s (% bf16 MFMA peak); Ulysses permute GB/s (% HBM)"
 HEADLINE = "ring_bf16_128k_rank7_causal"
@@ -62,7 +63,7 @@ ATTN_COUNTERS = {
 PERMUTE_TRAFFIC_FILE = os.path.join(PROFILES, "ulysses_permute_131k_traffic.json")
 REPLICATION_TRAFFIC_FILE = os.path.join(PROFILES, "ulysses_gqa_replication_131k_traffic.json")
 EXTRAS = ("ring32k", "ulysses_share", "ulysses", "gqa_replication", "packed", "visit_lengths", "backward",
-          "causal_split", "usp", "lse_merge", "f32_tiny", "capacity_1m")
+          "causal_split", "usp", "lse_merge", "f32_tiny", "f32_chunk", "capacity_1m")
 
 
 def log(*a):
@@ -533,6 +534,31 @@ def bench_f32_tiny(api, torch, iters=20, cpu=False):
     return res
 
 
+def bench_f32_chunk(api, torch, iters=5):
+    """The exact fp32 path at a throughput size: one 4096 x 4096 chunk pair,
+    B=1, 32 heads, d=128, fp32 inputs and output, non-causal (4*d FLOP per
+    pair), against MI355X's fp32 peak."""
+    B, H, n, d = 1, 32, 4096, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    q = torch.randn((B, H, n, d), generator=g, device="cuda") * d ** -0.5
+    k = torch.randn((B, H, n, d), generator=g, device="cuda")
+    v = torch.randn((B, H, n, d), generator=g, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty(B * H * n, dtype=torch.float32, device="cuda")
+    ts, _ = timed_launches(torch, lambda: api.ra_chunk_attention(q, k, v, o, lse), 1, iters)
+    ms = sum(ts) / len(ts)
+    flops = 4 * d * n * n * H * B
+    tf = flops / (ms * 1e-3) / 1e12
+    res = {"ms": round(ms, 3), "TFLOP/s": round(tf, 1), "flops": flops,
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_F32_TFLOPS, 4)},
+           "workload": "fp32 chunk pair: B=1, 32 heads, d=128, 4096 queries x 4096 keys, non-causal"}
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_capacity_1m(api, torch):
     """Sequence-length capacity: causal attention over 1,048,576 tokens on one
     GPU in one call, the Ulysses-share head shape (4 query heads, 1 key/value
@@ -731,6 +757,7 @@ def run_extras(api, torch, chosen, cpu=False):
             ("usp", "usp_128k_causal", lambda: bench_usp(api, torch)),
             ("lse_merge", "lse_merge_128k_step", lambda: bench_lse_merge(api, torch)),
             ("f32_tiny", "ring_f32_tiny", lambda: bench_f32_tiny(api, torch, cpu=cpu)),
+            ("f32_chunk", "f32_chunk_4k", lambda: bench_f32_chunk(api, torch)),
             ("capacity_1m", "capacity_1m_causal", lambda: bench_capacity_1m(api, torch)))
     for key, name, fn in runs:
         if key not in chosen:

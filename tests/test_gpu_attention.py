@@ -350,6 +350,37 @@ def test_ring_f32_tiny(api):
         check_close(l, ref_l[:, :, i * n:(i + 1) * n], "f32", f"lse rank {i}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_chunk_f32_4k_sampled(api, causal):
+    """The exact fp32 path at the size bench.py times (one 4096 x 4096 chunk
+    pair, 32 heads, d=128; also causal): every output finite, and sampled
+    rows of four heads (the first and last row of every 32-row workgroup
+    among them) against the fp64 oracle at the fp32 bar."""
+    B, H, n, d = 1, 32, 4096, 128
+    say(f"fp32 chunk 4k causal={causal}")
+    rng = np.random.default_rng(4096 + int(causal))
+    q = rng.standard_normal((B, H, n, d), dtype=np.float32) * np.float32(d ** -0.5)
+    k = rng.standard_normal((B, H, n, d), dtype=np.float32)
+    v = rng.standard_normal((B, H, n, d), dtype=np.float32)
+    o = torch.full((B, H, n, d), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B * H * n,), float("nan"), dtype=torch.float32, device="cuda")
+    api.ra_chunk_attention(dev_f32(q), dev_f32(k), dev_f32(v), o, lse, causal=causal)
+    torch.cuda.synchronize()
+    og, lg = host_f64(o), host_f64(lse).reshape(B, H, n)
+    assert np.isfinite(og).all() and np.isfinite(lg).all()
+    heads = [0, 9, 22, H - 1]
+    # first and last row of every 32-row workgroup, and every 97th row
+    rows = np.array(sorted({*range(0, n, 32), *range(31, n, 32), *range(5, n, 97), n - 1}), dtype=np.int64)
+    qf, kf, vf = q[:, heads][:, :, rows], k[:, heads], v[:, heads]
+    if causal:
+        ref_o, ref_l = oracle.attention_at_positions_fp64(qf, kf, vf, rows, np.arange(n))
+    else:
+        ref_o, ref_l = oracle.attention_fp64(qf, kf, vf)
+    check_close(og[:, heads][:, :, rows], ref_o, "f32", "O sampled rows")
+    check_close(lg[:, heads][:, :, rows], ref_l, "f32", "lse sampled rows")
+    say(f"   {len(rows)} rows x {len(heads)} heads checked")
+
+
 def test_ring_f32_tiny_unfused_merge(api):
     """The same ring with each chunk's partial written out and merged by ra_lse_merge."""
     w = WORKLOADS["ring_f32_tiny"]
