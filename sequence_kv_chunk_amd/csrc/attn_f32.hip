@@ -97,16 +97,24 @@ __global__ void __launch_bounds__(64 * kSplit) attn_f32_kernel(AttnParams p) {
       // this wave's region only: the wave's own LDS accesses complete in
       // order, so no workgroup barrier is needed (and the waves may make
       // different numbers of tiles)
-      for (int i = lane; i < kTile * D / 4; i += 64) {
-        const int r = i / (D / 4), e = (i % (D / 4)) * 4;
-        const int64_t u = k0 + r;
-        float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
-        if (u < n_keys) {
-          kx = *reinterpret_cast<const float4*>(kb + u * p.k_sn + e);
-          vx = *reinterpret_cast<const float4*>(vb + u * p.v_sn + e);
+      {
+        // row r0 + kRpi * it of the tile, columns e .. e+3 (kRpi rows per pass)
+        constexpr int kRpi = 256 / D;
+        const int r0 = lane / (D / 4), e = (lane % (D / 4)) * 4;
+        const float* kr = kb + (k0 + r0) * p.k_sn + e;
+        const float* vr = vb + (k0 + r0) * p.v_sn + e;
+        const int nv = (int)min(n_keys - k0, (int64_t)kTile);   // valid rows of the tile
+#pragma unroll
+        for (int it = 0; it < kTile / kRpi; ++it) {
+          const int r = r0 + kRpi * it;
+          float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
+          if (r < nv) {
+            kx = *reinterpret_cast<const float4*>(kr + (int64_t)(kRpi * it) * p.k_sn);
+            vx = *reinterpret_cast<const float4*>(vr + (int64_t)(kRpi * it) * p.v_sn);
+          }
+          *reinterpret_cast<float4*>(ks + r * C::KROW + e) = kx;
+          *reinterpret_cast<float4*>(vs + r * D + e) = vx;
         }
-        *reinterpret_cast<float4*>(ks + r * C::KROW + e) = kx;
-        *reinterpret_cast<float4*>(vs + r * D + e) = vx;
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -123,13 +131,15 @@ __global__ void __launch_bounds__(64 * kSplit) attn_f32_kernel(AttnParams p) {
         st = mfma_f32(kx.w, q[e + 3], st);
       }
       // element jj: key 8 (jj/4) + 4 hi + jj%4 of the tile, masked past the
-      // chunk's visible keys and (causal) after the query
+      // chunk's visible keys and (causal) after the query: the lane sees the
+      // tile's keys up to `lim`
+      int64_t lim64 = n_keys - 1 - k0;
+      if (p.causal) lim64 = min(lim64, qpos - kpos0 - k0);
+      const int lim = (int)max(min(lim64, (int64_t)kTile), (int64_t)-1) - 4 * hi;
       float tmx = kNegInf;
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
-        const int64_t u = k0 + 8 * (jj / 4) + 4 * hi + (jj % 4);
-        const bool vis = u < n_keys && (!p.causal || kpos0 + u <= qpos);
-        st[jj] = vis ? st[jj] * c : kNegInf;
+        st[jj] = (8 * (jj / 4) + (jj % 4) <= lim) ? st[jj] * c : kNegInf;
         tmx = fmaxf(tmx, st[jj]);
       }
       tmx = fmaxf(tmx, __shfl_xor(tmx, 32));   // the query's other 16 keys
@@ -138,11 +148,13 @@ __global__ void __launch_bounds__(64 * kSplit) attn_f32_kernel(AttnParams p) {
       // keeps alpha = 1 and gets weights 0
       const float mn = fmaxf(m, tmx);
       const float alpha = (mn == kNegInf || m == mn) ? 1.f : exp2f(m - mn);
-      l *= alpha;
+      if (__any(alpha != 1.f)) {   // a wave-uniform branch: no MFMA inside
+        l *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) o[mb][jj] *= alpha;
+          for (int jj = 0; jj < 16; ++jj) o[mb][jj] *= alpha;
+      }
       m = mn;
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
