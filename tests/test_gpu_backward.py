@@ -58,6 +58,8 @@ CASES = [
     (1, 2, 2, 600, 600, 64, True, 0, 0, 1.0),        # diagonal over several query and key workgroups
     (1, 4, 2, 700, 450, 128, True, 0, 200, 1.0),     # key workgroups whose walks start at different tiles
     (2, 4, 1, 520, 260, 128, False, 0, 0, 0.9),      # GQA 4:1, B=2, ragged query and key tails
+    (2, 8, 1, 300, 520, 64, True, 100, 0, 1.1),      # GQA 8:1 at d=64, B=2, queries ahead of the keys
+    (1, 3, 3, 64, 1000, 128, False, 0, 0, 1.0),      # one query tile, eight key workgroups, odd head count
 ]
 
 
