@@ -82,99 +82,140 @@ __global__ void __launch_bounds__(64 * kSplit) attn_f32_kernel(AttnParams p) {
   const int64_t tmax = min((int64_t)q0 + kRows - 1, (int64_t)p.n_q - 1);
   float m = kNegInf;  // running max of logits, base-2 units (same in both lane halves)
   float l = 0.f;      // this lane's part of the running normaliser (its 16 keys of each tile)
-  int g = 0;          // tile number within the visit
-  // chunks in ring order: visit s reads chunk j = (rank - s) mod P
-  for (int s = 0; s < p.nseg; ++s) {
+  // The wave's tiles in the visit's order: tile g (counting the 32-key tiles
+  // of every chunk, chunks in ring order: visit s reads chunk
+  // j = (rank - s) mod P) goes to wave g mod kSplit.  A cursor (s, k0) names
+  // a tile; the wave holds its next tile's rows in registers while it works
+  // on the current one.
+  auto chunk = [&](int s, const float*& kb, const float*& vb, int64_t& kpos0) -> int64_t {
     const int j = (p.rank - s + p.P) % p.P;
-    const float* kb = kb0 + (int64_t)j * p.k_cs;
-    const float* vb = vb0 + (int64_t)j * p.v_cs;
-    const int64_t kpos0 = p.k_pos0 + (int64_t)j * p.k_posstride;
+    kb = kb0 + (int64_t)j * p.k_cs;
+    vb = vb0 + (int64_t)j * p.v_cs;
+    kpos0 = p.k_pos0 + (int64_t)j * p.k_posstride;
     // causal: keys u with kpos0 + u <= max query position of this block
     int64_t n_keys = p.n_k;
     if (p.causal) n_keys = max((int64_t)0, min(n_keys, p.q_pos0 + tmax - kpos0 + 1));
-    for (int64_t k0 = 0; k0 < n_keys; k0 += kTile, ++g) {
-      if (g % kSplit != wave) continue;
-      // this wave's region only: the wave's own LDS accesses complete in
-      // order, so no workgroup barrier is needed (and the waves may make
-      // different numbers of tiles)
-      {
-        // row r0 + kRpi * it of the tile, columns e .. e+3 (kRpi rows per pass)
-        constexpr int kRpi = 256 / D;
-        const int r0 = lane / (D / 4), e = (lane % (D / 4)) * 4;
-        const float* kr = kb + (k0 + r0) * p.k_sn + e;
-        const float* vr = vb + (k0 + r0) * p.v_sn + e;
-        const int nv = (int)min(n_keys - k0, (int64_t)kTile);   // valid rows of the tile
+    return n_keys;
+  };
+  // moves (s, k0) on by `steps` tiles; s = nseg past the last tile
+  auto advance = [&](int& s, int64_t& k0, int steps) {
+    k0 += (int64_t)steps * kTile;
+    while (s < p.nseg) {
+      const float* kb;
+      const float* vb;
+      int64_t kpos0;
+      const int64_t span = (chunk(s, kb, vb, kpos0) + kTile - 1) / kTile * kTile;
+      if (k0 < span) break;
+      k0 -= span;
+      ++s;
+    }
+  };
+  // row r0 + kRpi * it of a tile, columns e .. e+3 (kRpi rows per pass)
+  constexpr int kRpi = 256 / D;
+  constexpr int kPass = kTile / kRpi;
+  const int r0 = lane / (D / 4), e4 = (lane % (D / 4)) * 4;
+  float4 pk[kPass], pv[kPass];
+  auto fetch = [&](int s, int64_t k0) {
+    if (s >= p.nseg) return;
+    const float* kb;
+    const float* vb;
+    int64_t kpos0;
+    const int64_t n_keys = chunk(s, kb, vb, kpos0);
+    const int nv = (int)min(n_keys - k0, (int64_t)kTile);   // valid rows of the tile
+    const float* kr = kb + (k0 + r0) * p.k_sn + e4;
+    const float* vr = vb + (k0 + r0) * p.v_sn + e4;
 #pragma unroll
-        for (int it = 0; it < kTile / kRpi; ++it) {
-          const int r = r0 + kRpi * it;
-          float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
-          if (r < nv) {
-            kx = *reinterpret_cast<const float4*>(kr + (int64_t)(kRpi * it) * p.k_sn);
-            vx = *reinterpret_cast<const float4*>(vr + (int64_t)(kRpi * it) * p.v_sn);
-          }
-          *reinterpret_cast<float4*>(ks + r * C::KROW + e) = kx;
-          *reinterpret_cast<float4*>(vs + r * D + e) = vx;
-        }
+    for (int it = 0; it < kPass; ++it) {
+      pk[it] = pv[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (r0 + kRpi * it < nv) {
+        pk[it] = *reinterpret_cast<const float4*>(kr + (int64_t)(kRpi * it) * p.k_sn);
+        pv[it] = *reinterpret_cast<const float4*>(vr + (int64_t)(kRpi * it) * p.v_sn);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // S^T = K Q^T: step e pairs d = e (lane half 0) with d = D/2 + e (half 1)
-      f32x16_t st = (f32x16_t){};
-      const float* krow = ks + l32 * C::KROW + hi * (D / 2);
+    }
+  };
+  int cs = 0;
+  int64_t ck0 = 0;
+  advance(cs, ck0, wave);
+  fetch(cs, ck0);
+  while (cs < p.nseg) {
+    // this wave's LDS region only: the wave's own LDS accesses complete in
+    // order, so no workgroup barrier is needed (and the waves may make
+    // different numbers of tiles)
 #pragma unroll
-      for (int e = 0; e < D / 2; e += 4) {
-        const float4 kx = *reinterpret_cast<const float4*>(krow + e);
-        st = mfma_f32(kx.x, q[e], st);
-        st = mfma_f32(kx.y, q[e + 1], st);
-        st = mfma_f32(kx.z, q[e + 2], st);
-        st = mfma_f32(kx.w, q[e + 3], st);
-      }
-      // element jj: key 8 (jj/4) + 4 hi + jj%4 of the tile, masked past the
-      // chunk's visible keys and (causal) after the query: the lane sees the
-      // tile's keys up to `lim`
-      int64_t lim64 = n_keys - 1 - k0;
-      if (p.causal) lim64 = min(lim64, qpos - kpos0 - k0);
-      const int lim = (int)max(min(lim64, (int64_t)kTile), (int64_t)-1) - 4 * hi;
-      float tmx = kNegInf;
+    for (int it = 0; it < kPass; ++it) {
+      const int r = r0 + kRpi * it;
+      *reinterpret_cast<float4*>(ks + r * C::KROW + e4) = pk[it];
+      *reinterpret_cast<float4*>(vs + r * D + e4) = pv[it];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int ns = cs;
+    int64_t nk0 = ck0;
+    advance(ns, nk0, kSplit);
+    fetch(ns, nk0);   // the wave's next tile, in flight while this one is used
+    const float* kb;
+    const float* vb;
+    int64_t kpos0;
+    const int64_t n_keys = chunk(cs, kb, vb, kpos0);
+    const int64_t k0 = ck0;
+    // S^T = K Q^T: step e pairs d = e (lane half 0) with d = D/2 + e (half 1)
+    f32x16_t st = (f32x16_t){};
+    const float* krow = ks + l32 * C::KROW + hi * (D / 2);
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        st[jj] = (8 * (jj / 4) + (jj % 4) <= lim) ? st[jj] * c : kNegInf;
-        tmx = fmaxf(tmx, st[jj]);
-      }
-      tmx = fmaxf(tmx, __shfl_xor(tmx, 32));   // the query's other 16 keys
-      // no branch on the row's state: the matrix products below run for the
-      // whole wave whatever the lane mask, so a row that has seen no key yet
-      // keeps alpha = 1 and gets weights 0
-      const float mn = fmaxf(m, tmx);
-      const float alpha = (mn == kNegInf || m == mn) ? 1.f : exp2f(m - mn);
-      if (__any(alpha != 1.f)) {   // a wave-uniform branch: no MFMA inside
-        l *= alpha;
+    for (int e = 0; e < D / 2; e += 4) {
+      const float4 kx = *reinterpret_cast<const float4*>(krow + e);
+      st = mfma_f32(kx.x, q[e], st);
+      st = mfma_f32(kx.y, q[e + 1], st);
+      st = mfma_f32(kx.z, q[e + 2], st);
+      st = mfma_f32(kx.w, q[e + 3], st);
+    }
+    // element jj: key 8 (jj/4) + 4 hi + jj%4 of the tile, masked past the
+    // chunk's visible keys and (causal) after the query: the lane sees the
+    // tile's keys up to `lim`
+    int64_t lim64 = n_keys - 1 - k0;
+    if (p.causal) lim64 = min(lim64, qpos - kpos0 - k0);
+    const int lim = (int)max(min(lim64, (int64_t)kTile), (int64_t)-1) - 4 * hi;
+    float tmx = kNegInf;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int jj = 0; jj < 16; ++jj) o[mb][jj] *= alpha;
-      }
-      m = mn;
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        st[jj] = (st[jj] == kNegInf) ? 0.f : exp2f(st[jj] - m);
-        l += st[jj];
-      }
-      // O^T += V^T P^T: step (gg, x) pairs key 8gg + x (half 0) with key
-      // 8gg + 4 + x (half 1), i.e. element 4gg + x of each lane
+    for (int jj = 0; jj < 16; ++jj) {
+      st[jj] = (8 * (jj / 4) + (jj % 4) <= lim) ? st[jj] * c : kNegInf;
+      tmx = fmaxf(tmx, st[jj]);
+    }
+    tmx = fmaxf(tmx, __shfl_xor(tmx, 32));   // the query's other 16 keys
+    // no branch on the row's state: the matrix products below run for the
+    // whole wave whatever the lane mask, so a row that has seen no key yet
+    // keeps alpha = 1 and gets weights 0
+    const float mn = fmaxf(m, tmx);
+    const float alpha = (mn == kNegInf || m == mn) ? 1.f : exp2f(m - mn);
+    if (__any(alpha != 1.f)) {   // a wave-uniform branch: no MFMA inside
+      l *= alpha;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-          const float vx = vs[(8 * (jj / 4) + 4 * hi + (jj % 4)) * D + 32 * mb + l32];
-          o[mb] = mfma_f32(vx, st[jj], o[mb]);
-        }
-      // every lane's reads of this tile are done before the next one is staged
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int jj = 0; jj < 16; ++jj) o[mb][jj] *= alpha;
     }
+    m = mn;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      st[jj] = (st[jj] == kNegInf) ? 0.f : exp2f(st[jj] - m);
+      l += st[jj];
+    }
+    // O^T += V^T P^T: step (gg, x) pairs key 8gg + x (half 0) with key
+    // 8gg + 4 + x (half 1), i.e. element 4gg + x of each lane
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const float vx = vs[(8 * (jj / 4) + 4 * hi + (jj % 4)) * D + 32 * mb + l32];
+        o[mb] = mfma_f32(vx, st[jj], o[mb]);
+      }
+    // every lane's reads of this tile are done before the next one is written
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    cs = ns;
+    ck0 = nk0;
   }
   // Merge the waves' partial states of each row: state (o[D], m, l) of wave
   // w for row n sits at stt + (w * kRows + n) * (D + 2).
