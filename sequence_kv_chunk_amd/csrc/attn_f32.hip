@@ -124,12 +124,20 @@ __global__ void __launch_bounds__(64 * kSplit) attn_f32_kernel(AttnParams p) {
     const int nv = (int)min(n_keys - k0, (int64_t)kTile);   // valid rows of the tile
     const float* kr = kb + (k0 + r0) * p.k_sn + e4;
     const float* vr = vb + (k0 + r0) * p.v_sn + e4;
+    if (nv == kTile) {   // a whole tile (a uniform branch)
 #pragma unroll
-    for (int it = 0; it < kPass; ++it) {
-      pk[it] = pv[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (r0 + kRpi * it < nv) {
+      for (int it = 0; it < kPass; ++it) {
         pk[it] = *reinterpret_cast<const float4*>(kr + (int64_t)(kRpi * it) * p.k_sn);
         pv[it] = *reinterpret_cast<const float4*>(vr + (int64_t)(kRpi * it) * p.v_sn);
+      }
+    } else {             // the chunk's last keys: rows past them are zeros
+#pragma unroll
+      for (int it = 0; it < kPass; ++it) {
+        pk[it] = pv[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r0 + kRpi * it < nv) {
+          pk[it] = *reinterpret_cast<const float4*>(kr + (int64_t)(kRpi * it) * p.k_sn);
+          pv[it] = *reinterpret_cast<const float4*>(vr + (int64_t)(kRpi * it) * p.v_sn);
+        }
       }
     }
   };
@@ -183,19 +191,25 @@ __global__ void __launch_bounds__(64 * kSplit) attn_f32_kernel(AttnParams p) {
       tmx = fmaxf(tmx, st[jj]);
     }
     tmx = fmaxf(tmx, __shfl_xor(tmx, 32));   // the query's other 16 keys
-    // no branch on the row's state: the matrix products below run for the
-    // whole wave whatever the lane mask, so a row that has seen no key yet
-    // keeps alpha = 1 and gets weights 0
-    const float mn = fmaxf(m, tmx);
-    const float alpha = (mn == kNegInf || m == mn) ? 1.f : exp2f(m - mn);
-    if (__any(alpha != 1.f)) {   // a wave-uniform branch: no MFMA inside
+    // The row's reference m moves (and o, l are rescaled) only when the
+    // tile's maximum exceeds it by more than kSlack (base-2 units): weights
+    // then stay below 2^kSlack, which fp32 carries without loss, and the
+    // rescale is rare after the first tiles.  No branch on the row's state
+    // around the matrix products: they run for the whole wave whatever the
+    // lane mask, so a row that has seen no key yet keeps alpha = 1 and gets
+    // weights 0.
+    constexpr float kSlack = 8.f;
+    const bool bump = tmx != kNegInf && (m == kNegInf || tmx > m + kSlack);
+    if (__any(bump)) {   // a wave-uniform branch: no MFMA inside
+      const float mn = bump ? tmx : m;
+      const float alpha = (m == kNegInf || !bump) ? 1.f : exp2f(m - mn);
       l *= alpha;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) o[mb][jj] *= alpha;
+      m = mn;
     }
-    m = mn;
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
       st[jj] = (st[jj] == kNegInf) ? 0.f : exp2f(st[jj] - m);
