@@ -212,7 +212,9 @@ __global__ void __launch_bounds__(64 * kSplit) attn_f32_kernel(AttnParams p) {
     }
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
-      st[jj] = (st[jj] == kNegInf) ? 0.f : exp2f(st[jj] - m);
+      // v_exp_f32: within an ulp for normal results; a weight below 2^-126
+      // (flushed to 0) is far below the fp32 bar next to the row's largest (>= 1)
+      st[jj] = (st[jj] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(st[jj] - m);
       l += st[jj];
     }
     // O^T += V^T P^T: step (gg, x) pairs key 8gg + x (half 0) with key
