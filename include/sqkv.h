@@ -88,12 +88,14 @@ typedef struct sqkv_view {
  * BF16 (bf16 MFMA products, fp32 accumulation, softmax weights rounded to
  * bf16 for the P*V product); acc_dtype, out_dtype F32 or BF16.  Pointers must
  * be 16-byte aligned, every stride a multiple of 16 bytes and key/value row
- * strides below 16 MiB.  Keys a query cannot see (masked, or past the chunk)
+ * strides below 16 MiB; with BF16 inputs the key/value row strides must also
+ * be at least d (no overlapping rows).  Keys a query cannot see (masked, or
+ * past the chunk)
  * still pass through the P*V product with weight 0, so K and V must be
  * finite.
  * Returns SQKV_OK, SQKV_EINVAL (null pointer, Hq % Hkv != 0, negative size,
  * scale not finite and > 0, overlap), SQKV_EUNSUPPORTED (d, dtype,
- * alignment) or SQKV_EHIP.
+ * alignment, strides) or SQKV_EHIP.
  */
 sqkv_status ra_chunk_attention(sqkv_view q, sqkv_view k, sqkv_view v,
                                sqkv_view o_in, const float* lse_in,
@@ -197,10 +199,11 @@ sqkv_status ra_attention_bwd_preprocess(sqkv_view o, sqkv_view dout, float* D,
  * lse = -inf (no visible key anywhere) contribute nothing.  Supported: d in
  * {64, 128}, in_dtype BF16 (bf16 MFMA products, fp32 accumulation; P and dS
  * rounded to bf16 for the products that take them), pointers and strides
- * 16-byte aligned, row strides below 16 MiB.  Returns SQKV_OK, SQKV_EINVAL
+ * 16-byte aligned, row strides below 16 MiB and at least d (no overlapping
+ * rows in q, k, v or dout).  Returns SQKV_OK, SQKV_EINVAL
  * (null pointer, sizes, Hq % Hkv, scale, a gradient buffer overlapping an
- * input or another gradient), SQKV_EUNSUPPORTED (d, dtype, alignment) or
- * SQKV_EHIP.
+ * input or another gradient), SQKV_EUNSUPPORTED (d, dtype, alignment,
+ * strides) or SQKV_EHIP.
  */
 sqkv_status ra_chunk_attention_bwd(sqkv_view q, sqkv_view k, sqkv_view v, sqkv_view dout,
                                    const float* lse, const float* D,

@@ -113,7 +113,9 @@ def _view(t: torch.Tensor | None) -> SqkvView:
         return SqkvView(None, 0, 0, 0)
     if t.stride(-1) != 1:
         raise SqkvError(SQKV_EINVAL, "innermost (d) stride must be 1")
-    return SqkvView(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+    # a single row's stride is never used: pass one that cannot make rows overlap
+    sn = t.stride(2) if t.shape[2] != 1 else max(t.stride(2), t.shape[3])
+    return SqkvView(t.data_ptr(), t.stride(0), t.stride(1), sn)
 
 
 def _stream(t: torch.Tensor) -> int:

@@ -123,9 +123,13 @@ sqkv_status check_attention(const AttnCheck& a) {
     return fail(SQKV_EUNSUPPORTED, "output pointers and strides must be 16-byte aligned");
   if (((uintptr_t)a.lse_out) % 4 || ((uintptr_t)a.lse_in) % 4)
     return fail(SQKV_EUNSUPPORTED, "lse must be 4-byte aligned");
-  // the bf16 kernel addresses a key/value tile through a 32-bit byte range
+  // the attention kernels address a key/value tile through a 32-bit byte
+  // range; the bf16 kernel's range is rows x row stride, so its key/value
+  // rows must not overlap
   if (a.k.sn * ieb >= (1ll << 24) || a.v.sn * ieb >= (1ll << 24))
     return fail(SQKV_EUNSUPPORTED, "key/value row strides must be below 16 MiB");
+  if (a.in_dt == SQKV_BF16 && a.n_k > 0 && (a.k.sn < a.d || a.v.sn < a.d))
+    return fail(SQKV_EUNSUPPORTED, "bf16 key/value row strides must be at least d (rows may not overlap)");
   // aliasing: outputs may only coincide exactly with the running state
   const int64_t rows = (int64_t)a.B * a.Hq * a.n_q;
   Range ro = view_range(a.o_out, a.B, a.Hq, a.n_q, a.d, dtype_bytes(a.out_dt));
@@ -477,6 +481,9 @@ sqkv_status check_bwd(const sqkv_view& q, const sqkv_view& k, const sqkv_view& v
   if (((uintptr_t)lse | (uintptr_t)D) % 4) return fail(SQKV_EUNSUPPORTED, "lse and D must be 4-byte aligned");
   if (k.sn * 2 >= (1ll << 24) || v.sn * 2 >= (1ll << 24) || q.sn * 2 >= (1ll << 24) || dout.sn * 2 >= (1ll << 24))
     return fail(SQKV_EUNSUPPORTED, "row strides must be below 16 MiB");
+  // tiles are copied as rows x row stride bytes: rows may not overlap
+  if (k.sn < d || v.sn < d || q.sn < d || dout.sn < d)
+    return fail(SQKV_EUNSUPPORTED, "row strides of q, k, v and dout must be at least d (rows may not overlap)");
   const int64_t rows = (int64_t)B * Hq * n_q;
   Range rq = view_range(q, B, Hq, n_q, d, 2), ro = view_range(dout, B, Hq, n_q, d, 2);
   Range rk = view_range(k, B, Hkv, n_k, d, 2), rv = view_range(v, B, Hkv, n_k, d, 2);

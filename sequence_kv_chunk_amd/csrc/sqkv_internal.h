@@ -23,6 +23,22 @@ inline hipError_t allow_dyn_lds(const void* kernel, int bytes, std::atomic<uint6
   return e;
 }
 
+// Compute units of the current device, cached per device.
+inline hipError_t device_cu_count(int* n) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < kMaxDev;
+  if (cached && (*n = cache[dev].load(std::memory_order_relaxed)) > 0) return hipSuccess;
+  e = hipDeviceGetAttribute(n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (*n < 1) *n = 1;
+  if (cached) cache[dev].store(*n, std::memory_order_relaxed);
+  return hipSuccess;
+}
+
 enum DType : int { kF32 = 0, kBF16 = 1 };
 
 // One attention launch: a query chunk against `nseg` key/value chunks visited

@@ -122,6 +122,8 @@ ATTN_BAD = [   # (name, overrides built at call time, expected status)
     ("misaligned q ptr", lambda: dict(q=View(at(1 * GB + 8), 4 * 64 * 128, 64 * 128, 128)), EUNSUP),
     ("misaligned q stride", lambda: dict(q=View(at(1 * GB), 4 * 64 * 130, 64 * 130, 130)), EUNSUP),
     ("negative stride", lambda: dict(q=View(at(1 * GB), 0, -64 * 128, 128)), EINVAL),
+    ("bf16 key rows overlap", lambda: dict(k=View(at(2 * GB), 2 * 64 * 128, 64 * 128, 64)), EUNSUP),
+    ("bf16 value rows overlap", lambda: dict(v=View(at(3 * GB), 2 * 64 * 128, 64 * 128, 0)), EUNSUP),
     ("o_out overlaps q", lambda: dict(o_out=_dense(1 * GB + 4096, 4, 64, 128)), EINVAL),
     ("lse_out overlaps k", lambda: dict(lse_out=at(2 * GB + 64)), EINVAL),
     ("o_out partially overlaps o_in", lambda: dict(o_in=_dense(6 * GB, 4, 64, 128), lse_in=at(7 * GB),
@@ -256,6 +258,33 @@ def check_ulysses(lib):
     assert h2s(src, dst, 4, 10, 8, 2, 2, None) == EINVAL
     assert h2s(src, dst, 8, 16, 4, 2, 2, None) == EINVAL
     assert lib.sqkv_last_error().decode() != ""
+
+
+@no_gpu
+def test_bwd_rejects(lib):
+    check_bwd(lib)
+
+
+def check_bwd(lib):
+    """The backward copies q, dout, k and v tiles as rows x row stride, so a
+    view whose rows overlap (row stride below d) is refused."""
+    _setup(lib)
+    V, i, i64, f, vp = View, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+    lib.ra_chunk_attention_bwd.argtypes = [V, V, V, V, vp, vp, V, V, V, i, i, i, i, i, i, i, f, i, i64, i64, vp]
+    H, n, d = 2, 64, 128
+    views = dict(q=_dense(1 * GB, H, n, d), k=_dense(2 * GB, H, n, d), v=_dense(3 * GB, H, n, d),
+                 dout=_dense(4 * GB, H, n, d), dq=_dense(6 * GB, H, n, d), dk=_dense(7 * GB, H, n, d),
+                 dv=_dense(8 * GB, H, n, d))
+
+    def call(**kw):
+        a = dict(views, **kw)
+        return lib.ra_chunk_attention_bwd(a["q"], a["k"], a["v"], a["dout"], at(5 * GB), at(5 * GB + (1 << 20)),
+                                          a["dq"], a["dk"], a["dv"], 1, H, H, n, n, d, BF16, 1.0, 0, 0, 0, None)
+
+    for name in ("q", "k", "v", "dout"):
+        overlapping = View(at(views[name].ptr - BASE), H * n * d, n * d, 64)
+        assert call(**{name: overlapping}) == EUNSUP, name
+        assert b"overlap" in lib.sqkv_last_error()
 
 
 @no_gpu

@@ -92,6 +92,88 @@ def test_chunk_partial(api, case, in_dt):
         check_close(host_f64(lse).reshape(ref_l.shape), ref_l, tol, "lse")
 
 
+@pytest.mark.parametrize("Hq", [4, 256], ids=["split_kernel", "shared_kernel"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_f32_overlapping_key_rows(api, d, Hq):
+    """fp32 keys and values whose rows overlap in memory (row stride d/2: a
+    window sliding over one buffer, and a single row repeated with stride 0
+    for the values): every tile copy must read each row's whole d values,
+    not row count x row stride bytes.  4 query heads take the small-launch
+    fp32 kernel, 256 the shared-tile one."""
+    B, Hkv, nq, nk = 1, 2, 150, 77
+    say(f"f32 overlapping key/value rows, d={d}, Hq={Hq}")
+    rng = np.random.default_rng(6100 + d)
+    q = rng.standard_normal((B, Hq, nq, d), dtype=np.float32) * np.float32(d ** -0.5)
+    flat_k = rng.standard_normal(Hkv * (nk * d // 2 + d), dtype=np.float32)
+    flat_v = rng.standard_normal(Hkv * d, dtype=np.float32)
+    kd = dev_f32(flat_k).as_strided((B, Hkv, nk, d), (0, nk * d // 2 + d, d // 2, 1))
+    vd = dev_f32(flat_v).as_strided((B, Hkv, nk, d), (0, d, 0, 1))
+    k = kd.cpu().numpy().astype(np.float64)
+    v = vd.cpu().numpy().astype(np.float64)
+    ref_o, ref_l = oracle.attention_fp64(q.astype(np.float64), k, v, causal=True, q_pos0=40)
+    o, lse = _out(B, Hq, nq, d, torch.float32)
+    api.ra_chunk_attention(dev_f32(q), kd, vd, o, lse, causal=True, q_pos0=40)
+    torch.cuda.synchronize()
+    check_close(host_f64(o), ref_o, "f32", "O")
+    check_close(host_f64(lse).reshape(ref_l.shape), ref_l, "f32", "lse")
+    # the bf16 kernel copies rows x row stride bytes: such views are refused
+    with pytest.raises(api.SqkvError):
+        api.ra_chunk_attention(dev_f32(q).bfloat16(), kd.bfloat16().as_strided((B, Hkv, nk, d), (0, 0, 0, 1)),
+                               vd.bfloat16(), o, lse)
+
+
+# fp32 launches with at least one 128-row workgroup per compute unit (256 on
+# MI355X) take the shared-tile kernel: these shapes have 256 or more
+F32_WIDE_CASES = [
+    # B, Hq, Hkv, nq, nk, d, causal, q_pos0, k_pos0
+    (1, 256, 32, 130, 333, 128, True, 200, 0),    # ragged q-tile, causal diagonal, GQA 8:1
+    (2, 128, 128, 257, 65, 64, False, 0, 0),      # three q-tiles; 3 key tiles (split 1 gets one)
+    (1, 256, 256, 128, 1, 128, False, 0, 0),      # one key: split 1 has no tile at all
+    (1, 256, 64, 100, 300, 64, True, 0, 150),     # rows before every key see nothing
+]
+
+
+@pytest.mark.parametrize("case", F32_WIDE_CASES, ids=_ids([c + (1.0,) for c in F32_WIDE_CASES]))
+def test_f32_shared_kernel(api, case):
+    B, Hq, Hkv, nq, nk, d, causal, qp, kp = case
+    say(f"f32 shared-tile kernel {case}")
+    (q, k, v), (qd, kd, vd) = _inputs("f32", B, Hq, Hkv, nq, nk, d, seed=7000 + nq + nk)
+    ref_o, ref_l = oracle.attention_fp64(q, k, v, causal=causal, q_pos0=qp, k_pos0=kp)
+    o, lse = _out(B, Hq, nq, d, torch.float32)
+    api.ra_chunk_attention(qd, kd, vd, o, lse, causal=causal, q_pos0=qp, k_pos0=kp)
+    torch.cuda.synchronize()
+    check_close(host_f64(o), ref_o, "f32", "O")
+    check_close(host_f64(lse).reshape(ref_l.shape), ref_l, "f32", "lse")
+
+
+def test_f32_shared_kernel_accumulate_and_ring(api):
+    """The shared-tile fp32 kernel with a running state (fused merge, in
+    place) and over a causal ring of three chunks (every rank)."""
+    B, Hq, Hkv, n, d = 1, 256, 32, 140, 128
+    say("f32 shared-tile kernel: fused merge")
+    (q, k, v), (qd, kd, vd) = _inputs("f32", B, Hq, Hkv, n, 2 * n, d, seed=7100)
+    ref_o, ref_l = oracle.attention_fp64(q, k, v, causal=True, q_pos0=n, k_pos0=0)
+    o, lse = _out(B, Hq, n, d, torch.float32)
+    api.ra_chunk_attention(qd, kd[:, :, :n], vd[:, :, :n], o, lse, causal=True, q_pos0=n, k_pos0=0)
+    api.ra_chunk_attention(qd, kd[:, :, n:], vd[:, :, n:], o, lse, o_in=o, lse_in=lse, causal=True,
+                           q_pos0=n, k_pos0=n)
+    torch.cuda.synchronize()
+    check_close(host_f64(o), ref_o, "f32", "merged O")
+    check_close(host_f64(lse).reshape(ref_l.shape), ref_l, "f32", "merged lse")
+
+    P, n = 3, 96
+    say("f32 shared-tile kernel: causal ring of 3 chunks")
+    pool = [_rand((P, B, Hq if i == 0 else Hkv, n, d), 7200 + i, d ** -0.5 if i == 0 else 1.0) for i in range(3)]
+    ref_o, ref_l = oracle.attention_fp64(*[_full(x, "f32") for x in pool], causal=True)
+    kp, vp = dev_f32(pool[1]), dev_f32(pool[2])
+    for r in range(P):
+        o, lse = _out(B, Hq, n, d, torch.float32)
+        api.ra_ring_attention(dev_f32(pool[0][r]), kp, vp, o, lse, rank=r, scale=1.0, causal=True)
+        torch.cuda.synchronize()
+        check_close(host_f64(o), ref_o[:, :, r * n:(r + 1) * n], "f32", f"O rank {r}")
+        check_close(host_f64(lse).reshape(B, Hq, n), ref_l[:, :, r * n:(r + 1) * n], "f32", f"lse rank {r}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 def test_chunk_many_items_ragged_gqa(api, causal, d):
