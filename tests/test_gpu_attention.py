@@ -122,6 +122,23 @@ def test_f32_overlapping_key_rows(api, d, Hq):
                                vd.bfloat16(), o, lse)
 
 
+def test_one_key_row_with_any_stride(api):
+    """A one-row key/value view's row stride is never used: bf16 views with
+    row stride 0 go through the binding and match the oracle."""
+    B, Hq, Hkv, nq, d = 1, 4, 2, 70, 128
+    say("bf16, one key with a stride-0 row view")
+    (q, k, v), (qd, kd, vd) = _inputs("bf16", B, Hq, Hkv, nq, 1, d, seed=6300)
+    kx = kd.as_strided((B, Hkv, 1, d), (kd.stride(0), kd.stride(1), 0, 1))
+    vx = vd.as_strided((B, Hkv, 1, d), (vd.stride(0), vd.stride(1), 0, 1))
+    assert kx.stride(2) == 0 and vx.stride(2) == 0
+    ref_o, ref_l = oracle.attention_fp64(q, k, v)
+    o, lse = _out(B, Hq, nq, d, torch.bfloat16)
+    api.ra_chunk_attention(qd, kx, vx, o, lse)
+    torch.cuda.synchronize()
+    check_close(host_f64(o), ref_o, "bf16", "O")
+    check_close(host_f64(lse).reshape(ref_l.shape), ref_l, "bf16", "lse")
+
+
 # fp32 launches with at least one 128-row workgroup per compute unit (256 on
 # MI355X) take the shared-tile kernel: these shapes have 256 or more
 F32_WIDE_CASES = [
