@@ -163,10 +163,11 @@ def test_f32_shared_kernel(api, case):
     check_close(host_f64(lse).reshape(ref_l.shape), ref_l, "f32", "lse")
 
 
-def test_f32_shared_kernel_accumulate_and_ring(api):
+@pytest.mark.parametrize("d", [64, 128])
+def test_f32_shared_kernel_accumulate_and_ring(api, d):
     """The shared-tile fp32 kernel with a running state (fused merge, in
     place) and over a causal ring of three chunks (every rank)."""
-    B, Hq, Hkv, n, d = 1, 256, 32, 140, 128
+    B, Hq, Hkv, n = 1, 256, 32, 140
     say("f32 shared-tile kernel: fused merge")
     (q, k, v), (qd, kd, vd) = _inputs("f32", B, Hq, Hkv, n, 2 * n, d, seed=7100)
     ref_o, ref_l = oracle.attention_fp64(q, k, v, causal=True, q_pos0=n, k_pos0=0)
