@@ -31,6 +31,10 @@ CASES = [
     (4, 64, 2, 4, 4, 64, "bf16", "bf16"),
     (8, 48, 1, 2, 2, 128, "bf16", "bf16"),
     (4, 40, 1, 4, 2, 64, "f32", "f32"),
+    # 256 query heads: the fp32 launches take the shared-tile kernel (the
+    # third launch walks the pool backwards, with a negative chunk stride)
+    (4, 130, 1, 256, 32, 128, "f32", "f32"),
+    (3, 64, 1, 256, 64, 64, "f32", "f32"),
 ]
 
 
