@@ -34,10 +34,10 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-# Per-file flags.  The bf16 attention kernel never sees NaN by contract (its
-# inputs must be finite; -inf is used and kept), so its max operations need
+# Per-file flags.  The attention kernels never see NaN by contract (their
+# inputs must be finite; -inf is used and kept), so their max operations need
 # no NaN canonicalisation.
-EXTRA = {"attn_bf16.hip": ["-fno-honor-nans"]}
+EXTRA = {"attn_bf16.hip": ["-fno-honor-nans"], "attn_f32.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -57,6 +57,17 @@ __device__ __forceinline__ f32x16_t mfma_f32(float a, float b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// Max / sum with the lane 32 apart (the lane holding the query's other 16
+// keys): v_permlane32_swap of x with itself gives both values in every lane.
+__device__ __forceinline__ float max_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int I>
 using Int = std::integral_constant<int, I>;
 
@@ -135,7 +146,7 @@ __device__ __forceinline__ void softmax_pv(f32x16_t& st, f32x16_t (&o)[D / 32], 
   float tmx = st[0];
 #pragma unroll
   for (int jj = 1; jj < 16; ++jj) tmx = fmaxf(tmx, st[jj]);
-  tmx = fmaxf(tmx, __shfl_xor(tmx, 32));   // the query's other 16 keys
+  tmx = max_half(tmx);   // with the query's other 16 keys
   // The row's reference m moves (and o, l are rescaled) only when the tile's
   // maximum exceeds it by more than kSlack (base-2 units): weights then stay
   // below 2^kSlack, which fp32 carries without loss, and the rescale is rare
@@ -193,7 +204,7 @@ __device__ __forceinline__ void write_state(float* state, int l32, int hi, const
     for (int gg = 0; gg < 4; ++gg)
       *reinterpret_cast<float4*>(mine + 32 * mb + 8 * gg + 4 * hi) =
           make_float4(o[mb][4 * gg], o[mb][4 * gg + 1], o[mb][4 * gg + 2], o[mb][4 * gg + 3]);
-  const float lsum = l + __shfl_xor(l, 32);
+  const float lsum = sum_half(l);
   if (hi == 0) {
     mine[D] = m;
     mine[D + 1] = lsum;
@@ -404,9 +415,16 @@ attn_f32_shared(AttnParams p) {
   // lane addresses in stage 0 of the split: K row l32 (chunks of the lane's
   // half of d); V^T row l32 of d-block 0, its chunk holding keys 8 gg + 4 hi ..
   const SQKV_LDS unsigned char* sbase = (const SQKV_LDS unsigned char*)smem + ks * C::SPLIT;
-  const SQKV_LDS unsigned char* krow = sbase + l32 * C::ROWB;
-  const int kc0 = hi * (C::NCH / 2);          // first chunk of the lane's half of d
-  const int kswz = swz_k(l32);
+  // chunk g of the lane's half of d in stage 0, each a whole address held in
+  // a register (opaque to the compiler, which would otherwise split it into
+  // a shared base plus an offset and add them again for every read), so that
+  // a read adds only the stage offset as an immediate
+  uint32_t kaddr[D / 8];
+#pragma unroll
+  for (int g = 0; g < D / 8; ++g) {
+    kaddr[g] = (uint32_t)(size_t)(sbase + l32 * C::ROWB + (((hi * (C::NCH / 2) + g) ^ swz_k(l32)) * 16));
+    asm volatile("" : "+v"(kaddr[g]));
+  }
   int vto[4];
 #pragma unroll
   for (int gg = 0; gg < 4; ++gg) vto[gg] = C::TILE + l32 * 128 + (((2 * gg + hi) ^ swz_vt(l32)) * 16);
@@ -418,20 +436,23 @@ attn_f32_shared(AttnParams p) {
   int64_t dk0 = ck0;
   const int nsteps = (T + kSplits - 1) / kSplits;
   if (ks < T) issue(ds, dk0, 0);
-  for (int i = 0; i < nsteps; ++i) {
+  // step i: its tiles sit in stage i % 2 (a constant in each half of the
+  // unrolled loop, so that every LDS offset is an immediate)
+  auto step = [&](auto STG, int i) {
+    constexpr int stage = decltype(STG)::value;
     drain_and_sync();                         // step i's tiles landed; the other stage is free
     vis.advance(ds, dk0, kSplits);
-    if (kSplits * (i + 1) + ks < T) issue(ds, dk0, (i + 1) & 1);
+    if (kSplits * (i + 1) + ks < T) issue(ds, dk0, 1 - stage);
     if (kSplits * i + ks < T) {
-      const int stage = i & 1;
       const float* kb;
       const float* vb;
       int64_t kpos0;
       const int64_t n_keys = vis.chunk(cs, kb, vb, kpos0);
-      const SQKV_LDS unsigned char* kt = krow + stage * C::STAGE;
       // S^T = K Q^T: step e pairs d = e (lane half 0) with d = D/2 + e (half
       // 1); each group of four MFMAs takes the K operands read one group earlier
-      auto kread = [&](int g) { return *reinterpret_cast<const SQKV_LDS f32x4_t*>(kt + ((kc0 + g) ^ kswz) * 16); };
+      auto kread = [&](int g) {
+        return *reinterpret_cast<const SQKV_LDS f32x4_t*>((size_t)(kaddr[g] + stage * C::STAGE));
+      };
       f32x16_t st = (f32x16_t){};
       f32x4_t kb2[2];
       kb2[0] = kread(0);
@@ -456,6 +477,10 @@ attn_f32_shared(AttnParams p) {
       });
       vis.advance(cs, ck0, kSplits);
     }
+  };
+  for (int i = 0; i < nsteps; i += 2) {
+    step(Int<0>{}, i);
+    if (i + 1 < nsteps) step(Int<1>{}, i + 1);
   }
   drain_and_sync();   // every wave is done with the tiles: the LDS takes the states
   float* stt = reinterpret_cast<float*>(smem);
