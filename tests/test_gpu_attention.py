@@ -522,11 +522,15 @@ def test_ring_bf16_small(api, P, causal):
         check_close(l, ref_l[:, :, i * n:(i + 1) * n], "bf16", f"lse rank {i}")
 
 
-def test_deterministic(api):
-    (q, k, v), (qd, kd, vd) = _inputs("bf16", 1, 8, 2, 700, 900, 128, seed=21)
+@pytest.mark.parametrize("in_dt,Hq", [("bf16", 8), ("f32", 8), ("f32", 256)],
+                         ids=["bf16", "f32_split_kernel", "f32_shared_kernel"])
+def test_deterministic(api, in_dt, Hq):
+    """Two runs of the same call give bitwise the same outputs (no atomics,
+    a fixed merge order of the key splits)."""
+    (q, k, v), (qd, kd, vd) = _inputs(in_dt, 1, Hq, 2, 700, 900, 128, seed=21)
     res = []
     for _ in range(2):
-        o, lse = _out(1, 8, 700, 128, torch.float32)
+        o, lse = _out(1, Hq, 700, 128, torch.float32)
         api.ra_chunk_attention(qd, kd, vd, o, lse, causal=True, q_pos0=300)
         torch.cuda.synchronize()
         res.append((o.cpu().numpy().tobytes(), lse.cpu().numpy().tobytes()))
