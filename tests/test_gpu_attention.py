@@ -122,6 +122,24 @@ def test_f32_overlapping_key_rows(api, d, Hq):
                                vd.bfloat16(), o, lse)
 
 
+@pytest.mark.parametrize("Hq", [4, 256], ids=["split_kernel", "shared_kernel"])
+def test_f32_inputs_bf16_state_and_output(api, Hq):
+    """fp32 inputs merged into a bf16 running state, written as bf16: the
+    merge reads bf16 rows and the epilogue rounds to bf16 (bf16 tolerance)."""
+    B, Hkv, n, d = 1, 2, 150, 128
+    say(f"f32 inputs, bf16 running state and output, Hq={Hq}")
+    (q, k, v), (qd, kd, vd) = _inputs("f32", B, Hq, Hkv, n, 2 * n, d, seed=6400)
+    ref_o, ref_l = oracle.attention_fp64(q, k, v, causal=True, q_pos0=n, k_pos0=0)
+    o1, l1 = _out(B, Hq, n, d, torch.bfloat16)
+    api.ra_chunk_attention(qd, kd[:, :, :n], vd[:, :, :n], o1, l1, causal=True, q_pos0=n, k_pos0=0)
+    o2, l2 = _out(B, Hq, n, d, torch.bfloat16)
+    api.ra_chunk_attention(qd, kd[:, :, n:], vd[:, :, n:], o2, l2, o_in=o1, lse_in=l1, causal=True,
+                           q_pos0=n, k_pos0=n)
+    torch.cuda.synchronize()
+    check_close(host_f64(o2), ref_o, "bf16", "merged O")
+    check_close(host_f64(l2).reshape(ref_l.shape), ref_l, "bf16", "merged lse")
+
+
 def test_one_key_row_with_any_stride(api):
     """A one-row key/value view's row stride is never used: bf16 views with
     row stride 0 go through the binding and match the oracle."""
