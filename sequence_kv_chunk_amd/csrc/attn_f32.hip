@@ -86,7 +86,8 @@ __device__ __forceinline__ void static_for_n(F&& f) {
 // The visit of a block of query rows whose last row is tmax: chunk s of the
 // visit with its base pointers, the position of its key 0 and the keys the
 // block can see (causal: up to the block's last query position).  A cursor
-// (s, k0) names a tile: key k0 of the chunk of visit s.
+// (s, k0) names a tile: key k0 of the chunk of visit s; the Cursor struct
+// also carries its chunk's values.
 struct Visit {
   const AttnParams& p;
   const float* kb0;
@@ -114,6 +115,36 @@ struct Visit {
       if (k0 < span) break;
       k0 -= span;
       ++s;
+    }
+  }
+  // A cursor that keeps its chunk's values: they are recomputed only when it
+  // crosses into the next chunk.
+  struct Cursor {
+    int s;
+    int64_t k0, span, n_keys, kpos0;
+    const float* kb;
+    const float* vb;
+  };
+  __device__ void load(Cursor& c) const {
+    if (c.s < p.nseg) {
+      c.n_keys = chunk(c.s, c.kb, c.vb, c.kpos0);
+      c.span = (c.n_keys + kTile - 1) / kTile * kTile;
+    }
+  }
+  __device__ Cursor start(int steps) const {
+    Cursor c;
+    c.s = 0;
+    c.k0 = 0;
+    load(c);
+    move(c, steps);
+    return c;
+  }
+  __device__ void move(Cursor& c, int steps) const {
+    c.k0 += (int64_t)steps * kTile;
+    while (c.s < p.nseg && c.k0 >= c.span) {
+      c.k0 -= c.span;
+      ++c.s;
+      load(c);
     }
   }
   // tiles of the whole visit
@@ -394,15 +425,12 @@ attn_f32_shared(AttnParams p) {
   }
   const uint32_t split0 = lds0 + (uint32_t)(ks * C::SPLIT);
   const uint32_t m0_wave = (uint32_t)(rg * C::RPW * C::ROWB);
-  auto issue = [&](int s, int64_t k0, int stage) {
-    const float* kb;
-    const float* vb;
-    int64_t kpos0;
-    const int64_t n_keys = vis.chunk(s, kb, vb, kpos0);
-    const int nv = (int)min(n_keys - k0, (int64_t)kTile);   // valid rows of the tile (>= 1)
+  auto issue = [&](const Visit::Cursor& c, int stage) {
+    const int64_t k0 = c.k0;
+    const int nv = (int)min(c.n_keys - k0, (int64_t)kTile);   // valid rows of the tile (>= 1)
     // the byte range of rows 0 .. nv-1 exactly (row strides may be below a row)
-    const i32x4_t rk = buffer_rsrc(kb + k0 * p.k_sn, (uint32_t)((nv - 1) * k_snb + C::ROWB));
-    const i32x4_t rv = buffer_rsrc(vb + k0 * p.v_sn, (uint32_t)((nv - 1) * v_snb + C::ROWB));
+    const i32x4_t rk = buffer_rsrc(c.kb + k0 * p.k_sn, (uint32_t)((nv - 1) * k_snb + C::ROWB));
+    const i32x4_t rv = buffer_rsrc(c.vb + k0 * p.v_sn, (uint32_t)((nv - 1) * v_snb + C::ROWB));
     const uint32_t st = split0 + (uint32_t)(stage * C::STAGE);
 #pragma unroll
     for (int i = 0; i < C::NL; ++i) dma16(dko[i], rk, st + m0_wave + (uint32_t)(i * kRowWaves * C::RPW * C::ROWB));
@@ -429,25 +457,19 @@ attn_f32_shared(AttnParams p) {
 #pragma unroll
   for (int gg = 0; gg < 4; ++gg) vto[gg] = C::TILE + l32 * 128 + (((2 * gg + hi) ^ swz_vt(l32)) * 16);
 
-  int cs = 0;                                 // this wave's tile: step i is tile 2 i + ks
-  int64_t ck0 = 0;
-  vis.advance(cs, ck0, ks);
-  int ds = cs;                                // the next tile to copy
-  int64_t dk0 = ck0;
+  Visit::Cursor cc = vis.start(ks);          // this wave's tile: step i is tile 2 i + ks
+  Visit::Cursor dc = cc;                      // the next tile to copy
   const int nsteps = (T + kSplits - 1) / kSplits;
-  if (ks < T) issue(ds, dk0, 0);
+  if (ks < T) issue(dc, 0);
   // step i: its tiles sit in stage i % 2 (a constant in each half of the
   // unrolled loop, so that every LDS offset is an immediate)
   auto step = [&](auto STG, int i) {
     constexpr int stage = decltype(STG)::value;
     drain_and_sync();                         // step i's tiles landed; the other stage is free
-    vis.advance(ds, dk0, kSplits);
-    if (kSplits * (i + 1) + ks < T) issue(ds, dk0, 1 - stage);
+    vis.move(dc, kSplits);
+    if (kSplits * (i + 1) + ks < T) issue(dc, 1 - stage);
     if (kSplits * i + ks < T) {
-      const float* kb;
-      const float* vb;
-      int64_t kpos0;
-      const int64_t n_keys = vis.chunk(cs, kb, vb, kpos0);
+      const int64_t n_keys = cc.n_keys, kpos0 = cc.kpos0, ck0 = cc.k0;
       // S^T = K Q^T: step e pairs d = e (lane half 0) with d = D/2 + e (half
       // 1); each group of four MFMAs takes the K operands read one group earlier
       auto kread = [&](int g) {
@@ -475,7 +497,7 @@ attn_f32_shared(AttnParams p) {
       softmax_pv<D>(st, o, m, l, masked, lim, [&](int mb, int gg) {
         return *reinterpret_cast<const SQKV_LDS f32x4_t*>(vt + vto[gg] + mb * 32 * 128);
       });
-      vis.advance(cs, ck0, kSplits);
+      vis.move(cc, kSplits);
     }
   };
   for (int i = 0; i < nsteps; i += 2) {
