@@ -253,11 +253,15 @@ def test_chunk_accumulate(api, in_dt, inplace):
     check_close(host_f64(l2).reshape(ref_l.shape), ref_l, tol, "merged lse")
 
 
-@pytest.mark.parametrize("in_dt", ["f32", "bf16"])
-def test_running_max_rescale(api, in_dt):
-    """Keys that grow along the sequence force the running maximum up tile after tile."""
-    B, Hq, n, d = 1, 2, 256, 64
-    say(f"rescale path {in_dt}")
+@pytest.mark.parametrize("in_dt,Hq", [("f32", 2), ("f32", 160), ("bf16", 2)],
+                         ids=["f32-split_kernel", "f32-shared_kernel", "bf16"])
+def test_running_max_rescale(api, in_dt, Hq):
+    """Keys that grow along the sequence force the running maximum up tile after tile.
+
+    With 160 heads of two 128-row query tiles the fp32 launch has 320
+    workgroups and takes the shared-tile kernel; with 2 heads, the split one."""
+    B, n, d = 1, 256, 64
+    say(f"rescale path {in_dt} Hq={Hq}")
     (q, k, v), (qd, kd, vd) = _inputs(in_dt, B, Hq, Hq, n, 1000, d, seed=9, qscale=0.5, kramp=True)
     ref_o, ref_l = oracle.attention_fp64(q, k, v, scale=1.0)
     o, lse = _out(B, Hq, n, d, torch.float32)
