@@ -365,8 +365,11 @@ sqkv_status ulysses_head_to_seq(const void* src, void* dst, int P, int64_t L,
  *
  * Causal masking uses global positions (ring rows are contiguous runs).
  * EINVAL: P_u or P_r < 1, L % (P_u*P_r), H % H_kv, H % P_u, neither of H_kv,
- * P_u dividing the other, null pointers, overlapping buffers; otherwise the
- * status of the first failing phase.
+ * P_u dividing the other, null pointers, overlapping buffers.
+ * EUNSUPPORTED: d not in {64, 128}, S above 2^30 tokens, H/P_u above 65535,
+ * q, k, v, o or a work buffer not 16-byte aligned, lse not 4-byte aligned.
+ * These are checked before the first phase is enqueued; after that the
+ * status is that of the first failing phase (a HIP launch error).
  */
 sqkv_status usp_attention(const void* q, const void* k, const void* v, void* o,
                           void* work_q, void* work_k, void* work_v, void* work_o, float* lse,

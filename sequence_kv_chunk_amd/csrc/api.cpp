@@ -707,9 +707,17 @@ SQKV_EXPORT sqkv_status usp_attention(const void* q, const void* k, const void* 
   if (H % P_u) return fail(SQKV_EINVAL, "H (%d) must be a multiple of P_u (%d)", H, P_u);
   if (P_u % H_kv && H_kv % P_u)
     return fail(SQKV_EINVAL, "key/value heads (%d) and P_u (%d): one must divide the other", H_kv, P_u);
+  // what the attention phase would reject is rejected here, before the first
+  // phase is enqueued
+  if (d != 64 && d != 128) return fail(SQKV_EUNSUPPORTED, "head dim d=%d not in {64, 128}", d);
+  if (L / P_r > (1ll << 30)) return fail(SQKV_EUNSUPPORTED, "ring chunks of L/P_r=%lld tokens are above 2^30", (long long)(L / P_r));
+  if (H / P_u > 65535) return fail(SQKV_EUNSUPPORTED, "H/P_u must be <= 65535");
   if (L == 0) return ok();
   if (!q || !k || !v || !o || !work_q || !work_k || !work_v || !work_o || !lse)
     return fail(SQKV_EINVAL, "null pointer");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)work_q | (uintptr_t)work_k |
+       (uintptr_t)work_v | (uintptr_t)work_o) % 16 || ((uintptr_t)lse) % 4)
+    return fail(SQKV_EUNSUPPORTED, "q, k, v, o and the work buffers must be 16-byte aligned, lse 4-byte");
   const int64_t n = L / P, S = L / P_r;          // tokens per shard, per ring chunk (= P_u * n)
   const int Hl = H / P_u, Hkd = std::max(H_kv, P_u), Hkl = Hkd / P_u;
   const int64_t qe = (int64_t)P * n * H * d, ke = (int64_t)P * n * H_kv * d, we = (int64_t)P_r * P_u * S * Hkl * d;

@@ -207,8 +207,8 @@ def check_usp(lib):
     lib.usp_attention.argtypes = [vp] * 9 + [i, i, i64, i, i, i, f, i, vp]
     bufs = [at(g * GB) for g in range(1, 10)]
 
-    def call(P_u=2, P_r=2, L=1024, H=4, H_kv=2, bufs=bufs):
-        return lib.usp_attention(*bufs, P_u, P_r, L, H, H_kv, 128, 1.0, 1, None)
+    def call(P_u=2, P_r=2, L=1024, H=4, H_kv=2, bufs=bufs, d=128):
+        return lib.usp_attention(*bufs, P_u, P_r, L, H, H_kv, d, 1.0, 1, None)
 
     assert call(P_u=0) == EINVAL
     assert call(L=1023) == EINVAL               # not a multiple of P_u * P_r
@@ -216,6 +216,10 @@ def check_usp(lib):
     assert call(H=6, H_kv=3, P_u=2) == EINVAL   # H_kv and P_u: neither divides the other
     assert call(bufs=[None] + bufs[1:]) == EINVAL
     assert call(bufs=bufs[:4] + [bufs[0]] + bufs[5:]) == EINVAL   # work_q overlaps q
+    assert call(d=96) == EUNSUP
+    assert call(L=1 << 32) == EUNSUP                             # ring chunks of 2^31 tokens
+    assert call(bufs=bufs[:5] + [at(6 * GB + 8)] + bufs[6:]) == EUNSUP   # work_k misaligned
+    assert call(bufs=bufs[:8] + [at(9 * GB + 2)]) == EUNSUP              # lse misaligned
 
 
 @no_gpu
