@@ -130,6 +130,26 @@ def _same_device(*ts):
         raise SqkvError(SQKV_EINVAL, f"tensors on different devices: {devs}")
 
 
+def _same_dtype(what: str, *ts):
+    if len({t.dtype for t in ts}) != 1:
+        raise SqkvError(SQKV_EINVAL, f"{what} must share a dtype")
+
+
+def _ring_shapes(q, k_pool, v_pool, o):
+    """(P, B, Hq, Hkv, n, d) of a ring call, after checking that q, o
+    ([B, Hq, n, d]) and the pools ([P, B, Hkv, n, d]) agree."""
+    if k_pool.dim() != 5 or v_pool.shape != k_pool.shape:
+        raise SqkvError(SQKV_EINVAL, "k_pool, v_pool must be [P, B, Hkv, n, d]")
+    if q.dim() != 4:
+        raise SqkvError(SQKV_EINVAL, f"q must be [B, Hq, n, d], got {tuple(q.shape)}")
+    P, Bk, Hkv, nk, dk = k_pool.shape
+    B, Hq, n, d = q.shape
+    if tuple(o.shape) != (B, Hq, n, d) or (Bk, nk, dk) != (B, n, d):
+        raise SqkvError(SQKV_EINVAL, "shapes disagree")
+    _same_dtype("q, k_pool and v_pool", q, k_pool, v_pool)
+    return P, B, Hq, Hkv, n, d
+
+
 def _lse_ptr(t: torch.Tensor | None, rows: int):
     if t is None:
         return None
@@ -166,13 +186,8 @@ def ra_chunk_attention(q, k, v, o_out, lse_out, *, o_in=None, lse_in=None, scale
 def ra_ring_attention(q, k_pool, v_pool, o, lse, *, rank: int, scale: float = 1.0, causal: bool = False):
     """Ring attention of query chunk ``q`` ([B, Hq, n, d]) of virtual rank ``rank``
     over the P resident chunks of ``k_pool``/``v_pool`` ([P, B, Hkv, n, d])."""
-    if k_pool.dim() != 5 or v_pool.shape != k_pool.shape:
-        raise SqkvError(SQKV_EINVAL, "k_pool, v_pool must be [P, B, Hkv, n, d]")
     _same_device(q, k_pool, v_pool, o, lse)
-    P = k_pool.shape[0]
-    B, Hq, n, d = q.shape
-    if tuple(o.shape) != (B, Hq, n, d) or k_pool.shape[3] != n or k_pool.shape[1] != B:
-        raise SqkvError(SQKV_EINVAL, "shapes disagree")
+    P, B, Hq, Hkv, n, d = _ring_shapes(q, k_pool, v_pool, o)
     with torch.cuda.device(q.device):
         st = _lib.ra_ring_attention(_view(q), _view(k_pool[0]), _view(v_pool[0]), k_pool.stride(0),
                                     v_pool.stride(0), _view(o), _lse_ptr(lse, B * Hq * n),
@@ -185,15 +200,10 @@ def ra_ring_attention_packed(q, k_pool, v_pool, o, lse, seg_starts, *, rank: int
     """Causal ring attention of virtual rank ``rank`` over a packed sequence:
     ``seg_starts`` (int64 device tensor) holds the samples' start positions in
     the whole sequence; a query sees only keys of its own sample."""
-    if k_pool.dim() != 5 or v_pool.shape != k_pool.shape:
-        raise SqkvError(SQKV_EINVAL, "k_pool, v_pool must be [P, B, Hkv, n, d]")
     _same_device(q, k_pool, v_pool, o, lse, seg_starts)
     if seg_starts.dtype != torch.int64 or seg_starts.dim() != 1 or not seg_starts.is_contiguous():
         raise SqkvError(SQKV_EINVAL, "seg_starts must be a contiguous 1-D int64 tensor")
-    P = k_pool.shape[0]
-    B, Hq, n, d = q.shape
-    if tuple(o.shape) != (B, Hq, n, d) or k_pool.shape[3] != n or k_pool.shape[1] != B:
-        raise SqkvError(SQKV_EINVAL, "shapes disagree")
+    P, B, Hq, Hkv, n, d = _ring_shapes(q, k_pool, v_pool, o)
     with torch.cuda.device(q.device):
         st = _lib.ra_ring_attention_packed(_view(q), _view(k_pool[0]), _view(v_pool[0]), k_pool.stride(0),
                                            v_pool.stride(0), _view(o), _lse_ptr(lse, B * Hq * n), seg_starts.data_ptr(),
@@ -208,13 +218,8 @@ def ra_zigzag_attention(q, k_pool, v_pool, o, lse, *, rank: int, scale: float = 
     of the 2P-piece sequence, ``k_pool``/``v_pool`` ([P, B, Hkv, n, d]) every
     rank's shard in the same layout.  ``work`` = (work_o fp32 [B, Hq, n/2, d],
     work_lse fp32 [B*Hq*n/2]) scratch; allocated here when not given."""
-    if k_pool.dim() != 5 or v_pool.shape != k_pool.shape:
-        raise SqkvError(SQKV_EINVAL, "k_pool, v_pool must be [P, B, Hkv, n, d]")
     _same_device(q, k_pool, v_pool, o, lse)
-    P = k_pool.shape[0]
-    B, Hq, n, d = q.shape
-    if tuple(o.shape) != (B, Hq, n, d) or k_pool.shape[3] != n or k_pool.shape[1] != B:
-        raise SqkvError(SQKV_EINVAL, "shapes disagree")
+    P, B, Hq, Hkv, n, d = _ring_shapes(q, k_pool, v_pool, o)
     if work is None:
         work = (torch.empty((B, Hq, n // 2, d), dtype=torch.float32, device=q.device),
                 torch.empty(B * Hq * (n // 2), dtype=torch.float32, device=q.device))
@@ -236,13 +241,8 @@ def ra_zigzag_attention_noalloc(q, k_pool, v_pool, o, lse, *, rank: int, scale: 
     per-GPU scratch array instead of caller work buffers: allocates nothing,
     for callers that cannot.  Calls that overlap on one GPU race on that
     scratch.  B*Hq*n/2 rows must fit zigzag_noalloc_max_bytes()."""
-    if k_pool.dim() != 5 or v_pool.shape != k_pool.shape:
-        raise SqkvError(SQKV_EINVAL, "k_pool, v_pool must be [P, B, Hkv, n, d]")
     _same_device(q, k_pool, v_pool, o, lse)
-    P = k_pool.shape[0]
-    B, Hq, n, d = q.shape
-    if tuple(o.shape) != (B, Hq, n, d) or k_pool.shape[3] != n or k_pool.shape[1] != B:
-        raise SqkvError(SQKV_EINVAL, "shapes disagree")
+    P, B, Hq, Hkv, n, d = _ring_shapes(q, k_pool, v_pool, o)
     with torch.cuda.device(q.device):
         st = _lib.ra_zigzag_attention_noalloc(_view(q), _view(k_pool[0]), _view(v_pool[0]), k_pool.stride(0),
                                               v_pool.stride(0), _view(o), _lse_ptr(lse, B * Hq * n), B, Hq,
@@ -285,8 +285,9 @@ def ra_chunk_attention_bwd(q, k, v, dout, lse, D, dq, dk, dv, *, scale: float = 
     B, Hq, n_q, d = q4.shape
     Hkv, n_k = k4.shape[1], k4.shape[2]
     if o4.shape != q4.shape or g4.shape != q4.shape or v4.shape != k4.shape or gk4.shape != k4.shape \
-            or gv4.shape != k4.shape:
+            or gv4.shape != k4.shape or k4.shape[0] != B or k4.shape[3] != d:
         raise SqkvError(SQKV_EINVAL, "shapes disagree")
+    _same_dtype("q, k, v and dout", q4, k4, v4, o4)
     rows = B * Hq * n_q
     with torch.cuda.device(q4.device):
         st = _lib.ra_chunk_attention_bwd(_view(q4), _view(k4), _view(v4), _view(o4), _lse_ptr(lse, rows),
@@ -308,10 +309,10 @@ def ra_ring_attention_bwd(q, k_pool, v_pool, dout, lse, D, dq, dk_pool, dv_pool,
     _f32(dq, dk_pool, dv_pool)
     if dk_pool.stride(0) != dv_pool.stride(0):
         raise SqkvError(SQKV_EINVAL, "dk_pool and dv_pool must share a chunk stride")
-    P = k_pool.shape[0]
-    B, Hq, n, d = q.shape
-    if tuple(dout.shape) != (B, Hq, n, d) or tuple(dq.shape) != (B, Hq, n, d) or k_pool.shape[3] != n:
+    P, B, Hq, Hkv, n, d = _ring_shapes(q, k_pool, v_pool, dout)
+    if tuple(dq.shape) != (B, Hq, n, d):
         raise SqkvError(SQKV_EINVAL, "shapes disagree")
+    _same_dtype("q and dout", q, dout)
     rows = B * Hq * n
     with torch.cuda.device(q.device):
         st = _lib.ra_ring_attention_bwd(_view(q), _view(k_pool[0]), _view(v_pool[0]), k_pool.stride(0),
@@ -399,8 +400,11 @@ def usp_attention(q, k, v, o, *, P_u: int, scale: float = 1.0, causal: bool = Fa
     if lse is None:
         lse = torch.empty((P_r, P_u, H // P_u, S), dtype=torch.float32, device=q.device)
     wq, wk, wv, wo = work
+    _same_device(q, wq, wk, wv, wo, lse)
     for t in (wq, wk, wv, wo, lse):
         _dense(t, "work/lse")
+    if any(t.dtype != torch.bfloat16 for t in (wq, wk, wv, wo)):
+        raise SqkvError(SQKV_EINVAL, "work buffers must be bf16")
     if wq.numel() != q.numel() or wo.numel() != q.numel() or wk.numel() != P_r * P_u * S * Hk * d \
             or wv.numel() != wk.numel() or lse.numel() != P_r * P_u * (H // P_u) * S or lse.dtype != torch.float32:
         raise SqkvError(SQKV_EINVAL, "work buffers or lse have the wrong size")
