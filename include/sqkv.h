@@ -179,6 +179,7 @@ sqkv_status ra_ring_attention_packed(sqkv_view q, sqkv_view k, sqkv_view v,
  * ra_attention_bwd_preprocess: D[b,h,t] = sum_e dout[b,h,t,e] * o[b,h,t,e]
  * (o, dout [B, H, n, d] views of `dtype`, D dense float32 [B, H, n]).  Run it
  * once per query chunk on the final output before the backward calls.
+ * EUNSUPPORTED also when B*H*n is 2^28 - 16 rows or more.
  */
 sqkv_status ra_attention_bwd_preprocess(sqkv_view o, sqkv_view dout, float* D,
                                         int B, int H, int n, int d, sqkv_dtype dtype, void* stream);
@@ -203,7 +204,8 @@ sqkv_status ra_attention_bwd_preprocess(sqkv_view o, sqkv_view dout, float* D,
  * rows in q, k, v or dout).  Returns SQKV_OK, SQKV_EINVAL
  * (null pointer, sizes, Hq % Hkv, scale, a gradient buffer overlapping an
  * input or another gradient), SQKV_EUNSUPPORTED (d, dtype, alignment,
- * strides) or SQKV_EHIP.
+ * strides, B*Hq*ceil(n_q/256) or B*Hkv*ceil(n_k/128) at 2^23 or more) or
+ * SQKV_EHIP.
  */
 sqkv_status ra_chunk_attention_bwd(sqkv_view q, sqkv_view k, sqkv_view v, sqkv_view dout,
                                    const float* lse, const float* D,
@@ -311,7 +313,8 @@ size_t ra_zigzag_attention_noalloc_max_bytes(void);
  *   o_a, lse_a (a_dtype), o_b, lse_b (b_dtype) : [B, H, n, d] and [B, H, n]
  *   o_out, lse_out (out_dtype)                  : result
  * o_out may be exactly o_a or o_b (same pointer, strides, dtype); lse_out may
- * be exactly lse_a or lse_b.  d in {64, 128}; 16-byte alignment as above.
+ * be exactly lse_a or lse_b.  d in {64, 128}; 16-byte alignment as above;
+ * n*d/4 below 2^32 - 256 (else EUNSUPPORTED).
  */
 sqkv_status ra_lse_merge(sqkv_view o_a, const float* lse_a, sqkv_dtype a_dtype,
                          sqkv_view o_b, const float* lse_b, sqkv_dtype b_dtype,

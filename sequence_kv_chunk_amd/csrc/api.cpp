@@ -471,6 +471,9 @@ sqkv_status check_bwd(const sqkv_view& q, const sqkv_view& k, const sqkv_view& v
   if (B > 65535 || Hq > 65535) return fail(SQKV_EUNSUPPORTED, "B and Hq must be <= 65535");
   if (n_q > (1ll << 30) || n_k > (1ll << 30)) return fail(SQKV_EUNSUPPORTED, "chunk lengths above 2^30");
   if (n_q == 0 || n_k == 0) return ok();
+  // one-dimensional grids of 512-thread workgroups: at most 2^23 of each kind
+  if ((n_q + 255) / 256 * B * Hq >= (1ll << 23) || (n_k + 127) / 128 * B * Hkv >= (1ll << 23))
+    return fail(SQKV_EUNSUPPORTED, "B*Hq*ceil(n_q/256) and B*Hkv*ceil(n_k/128) must be below 2^23");
   if (!q.ptr || !k.ptr || !v.ptr || !dout.ptr || !lse || !D || !dq.ptr || !dk.ptr || !dv.ptr)
     return fail(SQKV_EINVAL, "null pointer");
   for (const sqkv_view* x : {&q, &k, &v, &dout, &dq, &dk, &dv})
@@ -538,6 +541,8 @@ SQKV_EXPORT sqkv_status ra_attention_bwd_preprocess(sqkv_view o, sqkv_view dout,
   if (d != 64 && d != 128) return fail(SQKV_EUNSUPPORTED, "head dim d=%d not in {64, 128}", d);
   if (!dtype_ok(dtype)) return fail(SQKV_EUNSUPPORTED, "dtype must be SQKV_F32 or SQKV_BF16");
   if (n == 0) return ok();
+  // 16 threads per row in a one-dimensional grid
+  if ((int64_t)B * H * n > (1ll << 28) - 16) return fail(SQKV_EUNSUPPORTED, "B*H*n must be below 2^28 - 16 rows");
   if (!o.ptr || !dout.ptr || !D) return fail(SQKV_EINVAL, "null pointer");
   if (!strides_nonneg(o) || !strides_nonneg(dout)) return fail(SQKV_EINVAL, "negative stride");
   const int eb = dtype_bytes(dtype);
@@ -603,6 +608,8 @@ SQKV_EXPORT sqkv_status ra_lse_merge(sqkv_view o_a, const float* lse_a, sqkv_dty
   if (!dtype_ok(a_dtype) || !dtype_ok(b_dtype) || !dtype_ok(out_dtype))
     return fail(SQKV_EUNSUPPORTED, "dtype must be SQKV_F32 or SQKV_BF16");
   if (B > 65535 || H > 65535) return fail(SQKV_EUNSUPPORTED, "B and H must be <= 65535");
+  // a grid row of four elements per thread per (b, h)
+  if ((int64_t)n * (d / 4) > 0xffffff00ll) return fail(SQKV_EUNSUPPORTED, "n*d/4 must be below 2^32 - 256");
   if (n == 0) return ok();
   if (!o_a.ptr || !o_b.ptr || !o_out.ptr || !lse_a || !lse_b || !lse_out)
     return fail(SQKV_EINVAL, "null pointer");

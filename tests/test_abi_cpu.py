@@ -231,14 +231,15 @@ def check_merge(lib):
     _setup(lib)
     a, b, o = _dense(1 * GB, 4, 8, 64), _dense(2 * GB, 4, 8, 64), _dense(3 * GB, 4, 8, 64)
 
-    def call(d=64, oa=a, ob=b, oo=o, la=4 * GB, lb=5 * GB, lo=6 * GB, dt=F32):
-        return lib.ra_lse_merge(oa, at(la), dt, ob, at(lb), dt, oo, at(lo), dt, 1, 4, 8, d, None)
+    def call(d=64, oa=a, ob=b, oo=o, la=4 * GB, lb=5 * GB, lo=6 * GB, dt=F32, n=8):
+        return lib.ra_lse_merge(oa, at(la), dt, ob, at(lb), dt, oo, at(lo), dt, 1, 4, n, d, None)
 
     assert call(d=32) == EUNSUP
     assert call(la=None) == EINVAL
     assert call(oo=_dense(1 * GB + 256, 4, 8, 64)) == EINVAL
     assert call(lo=4 * GB + 4) == EINVAL
     assert call(dt=5) == EUNSUP
+    assert call(n=1 << 27, d=128) == EUNSUP      # n*d/4 = 2^32 threads in one grid row
 
 
 @no_gpu
@@ -280,15 +281,38 @@ def check_bwd(lib):
                  dout=_dense(4 * GB, H, n, d), dq=_dense(6 * GB, H, n, d), dk=_dense(7 * GB, H, n, d),
                  dv=_dense(8 * GB, H, n, d))
 
-    def call(**kw):
+    def call(nq=n, nk=n, **kw):
         a = dict(views, **kw)
         return lib.ra_chunk_attention_bwd(a["q"], a["k"], a["v"], a["dout"], at(5 * GB), at(5 * GB + (1 << 20)),
-                                          a["dq"], a["dk"], a["dv"], 1, H, H, n, n, d, BF16, 1.0, 0, 0, 0, None)
+                                          a["dq"], a["dk"], a["dv"], 1, H, H, nq, nk, d, BF16, 1.0, 0, 0, 0, None)
 
     for name in ("q", "k", "v", "dout"):
         overlapping = View(at(views[name].ptr - BASE), H * n * d, n * d, 64)
         assert call(**{name: overlapping}) == EUNSUP, name
         assert b"overlap" in lib.sqkv_last_error()
+    # 2^23 workgroups of either kernel
+    assert call(nq=1 << 30) == EUNSUP and b"2^23" in lib.sqkv_last_error()
+    assert call(nk=1 << 29) == EUNSUP and b"2^23" in lib.sqkv_last_error()
+
+
+@no_gpu
+def test_bwd_preprocess_rejects(lib):
+    check_bwd_preprocess(lib)
+
+
+def check_bwd_preprocess(lib):
+    _setup(lib)
+    V, i, vp = View, ctypes.c_int, ctypes.c_void_p
+    lib.ra_attention_bwd_preprocess.argtypes = [V, V, vp, i, i, i, i, i, vp]
+
+    def call(H=2, n=64, d=128, D=3 * GB):
+        return lib.ra_attention_bwd_preprocess(_dense(1 * GB, H, n, d), _dense(2 * GB, H, n, d), at(D), 1, H, n, d,
+                                               BF16, None)
+
+    assert call(d=96) == EUNSUP
+    assert call(D=None) == EINVAL
+    assert call(D=1 * GB + 64) == EINVAL                    # D inside o
+    assert call(H=16, n=1 << 24) == EUNSUP                 # 2^28 rows of 16 threads
 
 
 @no_gpu
