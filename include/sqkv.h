@@ -89,7 +89,9 @@ typedef struct sqkv_view {
  * bf16 for the P*V product); acc_dtype, out_dtype F32 or BF16.  Pointers must
  * be 16-byte aligned, every stride a multiple of 16 bytes and key/value row
  * strides below 16 MiB; with BF16 inputs the key/value row strides must also
- * be at least d (no overlapping rows).  Keys a query cannot see (masked, or
+ * be at least d (no overlapping rows).  B and Hq at most 65535, n_q and n_k at
+ * most 2^30 (F32 queries: below 2^30 - 128), B*Hq*ceil(n_q/256) below 2^31.
+ * Keys a query cannot see (masked, or
  * past the chunk)
  * still pass through the P*V product with weight 0, so K and V must be
  * finite.

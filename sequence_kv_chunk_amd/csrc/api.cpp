@@ -108,6 +108,12 @@ sqkv_status check_attention(const AttnCheck& a) {
   if (a.B > 65535 || a.Hq > 65535) return fail(SQKV_EUNSUPPORTED, "B and Hq must be <= 65535");
   if (a.n_q > (1ll << 30) || a.n_k > (1ll << 30))
     return fail(SQKV_EUNSUPPORTED, "chunk lengths above 2^30 are not supported");
+  // the bf16 kernel numbers its 256-row work items with 32-bit ints; the fp32
+  // kernel's grid rows hold ceil(n_q/128) workgroups of 512 threads
+  if ((a.n_q + 255) / 256 * a.B * a.Hq > 0x7fffffffll)
+    return fail(SQKV_EUNSUPPORTED, "B*Hq*ceil(n_q/256) must be below 2^31");
+  if (a.in_dt == SQKV_F32 && a.n_q > (1ll << 30) - 128)
+    return fail(SQKV_EUNSUPPORTED, "fp32 query chunks must be below 2^30 - 128 rows");
   if (a.n_q == 0) return ok();
   if (!a.q.ptr || !a.o_out.ptr || !a.lse_out) return fail(SQKV_EINVAL, "null q, o_out or lse_out");
   if (a.n_k > 0 && (!a.k.ptr || !a.v.ptr)) return fail(SQKV_EINVAL, "null k or v");

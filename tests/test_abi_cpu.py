@@ -119,6 +119,8 @@ ATTN_BAD = [   # (name, overrides built at call time, expected status)
     ("o_in without lse_in", lambda: dict(o_in=_dense(6 * GB, 4, 64, 128)), EINVAL),
     ("negative size", lambda: dict(n_q=-1), EINVAL),
     ("bad dtype", lambda: dict(in_dt=7), EUNSUP),
+    ("2^32 bf16 work items", lambda: dict(n_q=1 << 30, Hq=1024), EUNSUP),
+    ("fp32 rows beyond the grid", lambda: dict(n_q=1 << 30, in_dt=F32), EUNSUP),
     ("misaligned q ptr", lambda: dict(q=View(at(1 * GB + 8), 4 * 64 * 128, 64 * 128, 128)), EUNSUP),
     ("misaligned q stride", lambda: dict(q=View(at(1 * GB), 4 * 64 * 130, 64 * 130, 130)), EUNSUP),
     ("negative stride", lambda: dict(q=View(at(1 * GB), 0, -64 * 128, 128)), EINVAL),
