@@ -28,29 +28,32 @@ CASES = [
     (2, 300, 2, 2, 64, list(range(0, 600, 17))),                    # many short samples, ragged chunks
     (1, 700, 2, 2, 128, [0, 64, 128, 129, 511, 512, 699]),          # one chunk; tile-aligned starts
     (8, 128, 2, 2, 128, [0, 5, 900]),                               # a sample over seven chunks
+    (3, 200, 4, 2, 64, [0, 70, 333, 450], 2),                       # two batch rows, one packing
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"P{c[0]}_n{c[1]}_s{len(c[5])}" for c in CASES])
+@pytest.mark.parametrize("case", CASES, ids=[f"P{c[0]}_n{c[1]}_s{len(c[5])}" + (f"_B{c[6]}" if len(c) > 6 else "")
+                                             for c in CASES])
 def test_packed_ring(api, case):
-    P, n, Hq, Hkv, d, starts = case
-    say(f"packed {case[:5]} {len(starts)} samples")
+    P, n, Hq, Hkv, d, starts = case[:6]
+    B = case[6] if len(case) > 6 else 1
+    say(f"packed {case[:5]} B={B} {len(starts)} samples")
     L = P * n
     rng = np.random.default_rng(5000 + L + len(starts))
-    qb = f32_to_bf16_bits(rng.standard_normal((P, 1, Hq, n, d), dtype=np.float32) * np.float32(d ** -0.5))
-    kb = f32_to_bf16_bits(rng.standard_normal((P, 1, Hkv, n, d), dtype=np.float32))
-    vb = f32_to_bf16_bits(rng.standard_normal((P, 1, Hkv, n, d), dtype=np.float32))
-    full = lambda x: bf16_bits_to_f64(x).transpose(1, 2, 0, 3, 4).reshape(1, x.shape[2], L, d)
+    qb = f32_to_bf16_bits(rng.standard_normal((P, B, Hq, n, d), dtype=np.float32) * np.float32(d ** -0.5))
+    kb = f32_to_bf16_bits(rng.standard_normal((P, B, Hkv, n, d), dtype=np.float32))
+    vb = f32_to_bf16_bits(rng.standard_normal((P, B, Hkv, n, d), dtype=np.float32))
+    full = lambda x: bf16_bits_to_f64(x).transpose(1, 2, 0, 3, 4).reshape(B, x.shape[2], L, d)
     ref_o, ref_l = oracle.attention_packed_fp64(full(qb), full(kb), full(vb), starts)
     kd, vd = dev_bf16(kb), dev_bf16(vb)
     seg = torch.tensor(starts, dtype=torch.int64, device="cuda")
     for r in range(P):
-        o = torch.full((1, Hq, n, d), float("nan"), dtype=torch.bfloat16, device="cuda")
-        lse = torch.full((Hq * n,), float("nan"), dtype=torch.float32, device="cuda")
+        o = torch.full((B, Hq, n, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((B * Hq * n,), float("nan"), dtype=torch.float32, device="cuda")
         api.ra_ring_attention_packed(dev_bf16(qb[r]), kd, vd, o, lse, seg, rank=r)
         torch.cuda.synchronize()
         check_close(host_f64(o), ref_o[:, :, r * n:(r + 1) * n], "bf16", f"O rank {r}")
-        check_close(host_f64(lse).reshape(1, Hq, n), ref_l[:, :, r * n:(r + 1) * n], "bf16", f"lse rank {r}")
+        check_close(host_f64(lse).reshape(B, Hq, n), ref_l[:, :, r * n:(r + 1) * n], "bf16", f"lse rank {r}")
 
 
 def test_packed_fast_pass_fallback(api):
