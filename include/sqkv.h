@@ -96,8 +96,8 @@ typedef struct sqkv_view {
  * still pass through the P*V product with weight 0, so K and V must be
  * finite.
  * Returns SQKV_OK, SQKV_EINVAL (null pointer, Hq % Hkv != 0, negative size,
- * scale not finite and > 0, overlap), SQKV_EUNSUPPORTED (d, dtype,
- * alignment, strides) or SQKV_EHIP.
+ * scale not finite and > 0, overlap, rows of o_out that share elements),
+ * SQKV_EUNSUPPORTED (d, dtype, alignment, strides) or SQKV_EHIP.
  */
 sqkv_status ra_chunk_attention(sqkv_view q, sqkv_view k, sqkv_view v,
                                sqkv_view o_in, const float* lse_in,
@@ -205,7 +205,8 @@ sqkv_status ra_attention_bwd_preprocess(sqkv_view o, sqkv_view dout, float* D,
  * 16-byte aligned, row strides below 16 MiB and at least d (no overlapping
  * rows in q, k, v or dout).  Returns SQKV_OK, SQKV_EINVAL
  * (null pointer, sizes, Hq % Hkv, scale, a gradient buffer overlapping an
- * input or another gradient), SQKV_EUNSUPPORTED (d, dtype, alignment,
+ * input or another gradient, rows of a gradient that share elements),
+ * SQKV_EUNSUPPORTED (d, dtype, alignment,
  * strides, B*Hq*ceil(n_q/256) or B*Hkv*ceil(n_k/128) at 2^23 or more) or
  * SQKV_EHIP.
  */
@@ -224,8 +225,9 @@ sqkv_status ra_chunk_attention_bwd(sqkv_view q, sqkv_view k, sqkv_view v, sqkv_v
  * (chunk 0 at dk/dv, chunk j dkv_chunk_stride elements further, float32)
  * receive the rank's share of every chunk's dK, dV -- calling it for every
  * rank accumulates the full pool gradients.  Same support and status codes
- * as ra_chunk_attention_bwd; additionally EINVAL for rank outside [0, P) and
- * EUNSUPPORTED for chunk strides that are not multiples of 16 bytes.
+ * as ra_chunk_attention_bwd; additionally EINVAL for rank outside [0, P) or
+ * pool chunks of dk or dv that share elements, and EUNSUPPORTED for chunk
+ * strides that are not multiples of 16 bytes.
  */
 sqkv_status ra_ring_attention_bwd(sqkv_view q, sqkv_view k, sqkv_view v,
                                   int64_t k_chunk_stride, int64_t v_chunk_stride,
@@ -316,7 +318,8 @@ size_t ra_zigzag_attention_noalloc_max_bytes(void);
  *   o_out, lse_out (out_dtype)                  : result
  * o_out may be exactly o_a or o_b (same pointer, strides, dtype); lse_out may
  * be exactly lse_a or lse_b.  d in {64, 128}; 16-byte alignment as above;
- * n*d/4 below 2^32 - 256 (else EUNSUPPORTED).
+ * n*d/4 below 2^32 - 256 (else EUNSUPPORTED); rows of o_out that share
+ * elements are refused (EINVAL).
  */
 sqkv_status ra_lse_merge(sqkv_view o_a, const float* lse_a, sqkv_dtype a_dtype,
                          sqkv_view o_b, const float* lse_b, sqkv_dtype b_dtype,

@@ -8,8 +8,10 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <initializer_list>
 #include <mutex>
 #include <string>
+#include <utility>
 
 #include "../../include/sqkv.h"
 #include "sqkv_internal.h"
@@ -83,6 +85,28 @@ bool view_aligned(const sqkv_view& v, int eb) {
 
 bool strides_nonneg(const sqkv_view& v) { return v.sb >= 0 && v.sh >= 0 && v.sn >= 0; }
 
+// No two rows (runs of d elements) of an output view share an element.  The
+// dimensions (stride, count) are sorted by stride and each stride must reach
+// past the span of those below it: sufficient, and exact for the nested
+// layouts of dense tensors and their transposes.
+bool rows_disjoint(int64_t d, std::initializer_list<std::pair<int64_t, int64_t>> dims) {
+  std::pair<int64_t, int64_t> s[4];
+  int n = 0;
+  for (const auto& x : dims)
+    if (x.second > 1 && n < 4) s[n++] = x;
+  std::sort(s, s + n);
+  int64_t span = d;
+  for (int i = 0; i < n; ++i) {
+    if (s[i].first < span) return false;
+    span += s[i].first * (s[i].second - 1);
+  }
+  return true;
+}
+
+bool rows_disjoint(const sqkv_view& v, int B, int H, int64_t n, int d) {
+  return rows_disjoint(d, {{v.sb, B}, {v.sh, H}, {v.sn, n}});
+}
+
 struct AttnCheck {
   sqkv_view q, k, v, o_in, o_out;
   const float* lse_in;
@@ -136,6 +160,7 @@ sqkv_status check_attention(const AttnCheck& a) {
     return fail(SQKV_EUNSUPPORTED, "key/value row strides must be below 16 MiB");
   if (a.in_dt == SQKV_BF16 && a.n_k > 0 && (a.k.sn < a.d || a.v.sn < a.d))
     return fail(SQKV_EUNSUPPORTED, "bf16 key/value row strides must be at least d (rows may not overlap)");
+  if (!rows_disjoint(a.o_out, a.B, a.Hq, a.n_q, a.d)) return fail(SQKV_EINVAL, "rows of o_out overlap each other");
   // aliasing: outputs may only coincide exactly with the running state
   const int64_t rows = (int64_t)a.B * a.Hq * a.n_q;
   Range ro = view_range(a.o_out, a.B, a.Hq, a.n_q, a.d, dtype_bytes(a.out_dt));
@@ -493,6 +518,8 @@ sqkv_status check_bwd(const sqkv_view& q, const sqkv_view& k, const sqkv_view& v
   // tiles are copied as rows x row stride bytes: rows may not overlap
   if (k.sn < d || v.sn < d || q.sn < d || dout.sn < d)
     return fail(SQKV_EUNSUPPORTED, "row strides of q, k, v and dout must be at least d (rows may not overlap)");
+  if (!rows_disjoint(dq, B, Hq, n_q, d) || !rows_disjoint(dk, B, Hkv, n_k, d) || !rows_disjoint(dv, B, Hkv, n_k, d))
+    return fail(SQKV_EINVAL, "rows of dq, dk or dv overlap each other");
   const int64_t rows = (int64_t)B * Hq * n_q;
   Range rq = view_range(q, B, Hq, n_q, d, 2), ro = view_range(dout, B, Hq, n_q, d, 2);
   Range rk = view_range(k, B, Hkv, n_k, d, 2), rv = view_range(v, B, Hkv, n_k, d, 2);
@@ -591,6 +618,9 @@ SQKV_EXPORT sqkv_status ra_ring_attention_bwd(sqkv_view q, sqkv_view k, sqkv_vie
                              (int64_t)(P - 1) * std::max(k_chunk_stride, v_chunk_stride) * 2,
                              (int64_t)(P - 1) * dkv_chunk_stride * 4, d, in_dtype, scale);
   if (st != SQKV_OK || n == 0) return st;
+  if (!rows_disjoint(d, {{dk.sb, B}, {dk.sh, Hkv}, {dk.sn, n}, {dkv_chunk_stride, P}}) ||
+      !rows_disjoint(d, {{dv.sb, B}, {dv.sh, Hkv}, {dv.sn, n}, {dkv_chunk_stride, P}}))
+    return fail(SQKV_EINVAL, "the chunks of dk or dv overlap each other");
   // chunks in ring order, the rank's own first: j = (rank - s) mod P; with a
   // causal mask the chunks after the rank's own are entirely in the future
   const int nseg = causal ? rank + 1 : P;
@@ -634,6 +664,7 @@ SQKV_EXPORT sqkv_status ra_lse_merge(sqkv_view o_a, const float* lse_a, sqkv_dty
   Range rla = dense_range(lse_a, rows, 4), rlb = dense_range(lse_b, rows, 4);
   bool alias_a = same_view(o_out, o_a) && out_dtype == a_dtype;
   bool alias_b = same_view(o_out, o_b) && out_dtype == b_dtype;
+  if (!rows_disjoint(o_out, B, H, n, d)) return fail(SQKV_EINVAL, "rows of o_out overlap each other");
   if ((!alias_a && overlap(ro, ra)) || (!alias_b && overlap(ro, rb)))
     return fail(SQKV_EINVAL, "o_out partially overlaps an input");
   if ((lse_out != lse_a && overlap(rl, rla)) || (lse_out != lse_b && overlap(rl, rlb)))

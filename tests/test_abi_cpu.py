@@ -127,6 +127,8 @@ ATTN_BAD = [   # (name, overrides built at call time, expected status)
     ("bf16 key rows overlap", lambda: dict(k=View(at(2 * GB), 2 * 64 * 128, 64 * 128, 64)), EUNSUP),
     ("bf16 value rows overlap", lambda: dict(v=View(at(3 * GB), 2 * 64 * 128, 64 * 128, 0)), EUNSUP),
     ("o_out overlaps q", lambda: dict(o_out=_dense(1 * GB + 4096, 4, 64, 128)), EINVAL),
+    ("o_out rows overlap", lambda: dict(o_out=View(at(4 * GB), 4 * 64 * 128, 64 * 128, 64)), EINVAL),
+    ("o_out heads alias", lambda: dict(o_out=View(at(4 * GB), 64 * 128, 0, 128)), EINVAL),
     ("lse_out overlaps k", lambda: dict(lse_out=at(2 * GB + 64)), EINVAL),
     ("o_out partially overlaps o_in", lambda: dict(o_in=_dense(6 * GB, 4, 64, 128), lse_in=at(7 * GB),
                                             o_out=_dense(6 * GB + 1024, 4, 64, 128), acc_dt=BF16), EINVAL),
@@ -242,6 +244,7 @@ def check_merge(lib):
     assert call(lo=4 * GB + 4) == EINVAL
     assert call(dt=5) == EUNSUP
     assert call(n=1 << 27, d=128) == EUNSUP      # n*d/4 = 2^32 threads in one grid row
+    assert call(oo=View(at(3 * GB), 4 * 8 * 64, 0, 64)) == EINVAL   # every head writes the same rows
 
 
 @no_gpu
@@ -295,6 +298,33 @@ def check_bwd(lib):
     # 2^23 workgroups of either kernel
     assert call(nq=1 << 30) == EUNSUP and b"2^23" in lib.sqkv_last_error()
     assert call(nk=1 << 29) == EUNSUP and b"2^23" in lib.sqkv_last_error()
+    # gradient rows that would be written twice
+    assert call(dq=View(at(6 * GB), H * n * d, n * d, d // 2)) == EINVAL
+    assert call(dk=View(at(7 * GB), H * n * d, 0, d)) == EINVAL        # both heads' dK in the same rows
+
+
+@no_gpu
+def test_ring_bwd_rejects(lib):
+    check_ring_bwd(lib)
+
+
+def check_ring_bwd(lib):
+    """dk and dv pools whose chunks overlap would mix chunks' gradients."""
+    _setup(lib)
+    V, i, i64, f, vp = View, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+    lib.ra_ring_attention_bwd.argtypes = [V, V, V, i64, i64, V, vp, vp, V, V, V, i64, i, i, i, i, i, i, i, i, f, i, vp]
+    P, H, n, d = 4, 2, 64, 128
+    cs = H * n * d
+
+    def call(dkv_cs=cs, rank=1):
+        return lib.ra_ring_attention_bwd(_dense(1 * GB, H, n, d), _dense(2 * GB, H, n, d), _dense(3 * GB, H, n, d),
+                                         cs, cs, _dense(4 * GB, H, n, d), at(5 * GB), at(5 * GB + (1 << 20)),
+                                         _dense(6 * GB, H, n, d), _dense(7 * GB, H, n, d), _dense(8 * GB, H, n, d),
+                                         dkv_cs, 1, H, H, n, d, P, rank, BF16, 1.0, 1, None)
+
+    assert call(rank=P) == EINVAL
+    assert call(dkv_cs=cs // 2) == EINVAL and b"chunks" in lib.sqkv_last_error()
+    assert call(dkv_cs=0) == EINVAL
 
 
 @no_gpu

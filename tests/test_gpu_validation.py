@@ -37,7 +37,7 @@ def test_chunk_attention_rejects(real_base, lib, name, kw, want):
     cases.check_attn_case(lib, name, kw, want)
 
 
-@pytest.mark.parametrize("check", ["ring", "zigzag", "usp", "merge", "ulysses", "bwd", "bwd_preprocess", "empty"])
+@pytest.mark.parametrize("check", ["ring", "zigzag", "usp", "merge", "ulysses", "bwd", "bwd_preprocess", "ring_bwd", "empty"])
 def test_entry_points_reject(real_base, lib, check):
     getattr(cases, f"check_{check}")(lib)
     torch.cuda.synchronize()
