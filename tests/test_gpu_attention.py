@@ -253,6 +253,34 @@ def test_chunk_accumulate(api, in_dt, inplace):
     check_close(host_f64(l2).reshape(ref_l.shape), ref_l, tol, "merged lse")
 
 
+@pytest.mark.parametrize("in_dt,Hq", [("f32", 4), ("f32", 256), ("bf16", 4)],
+                         ids=["f32-split_kernel", "f32-shared_kernel", "bf16"])
+def test_empty_key_chunk(api, in_dt, Hq):
+    """A chunk with no keys (n_k = 0, key/value tensors with no rows): its own
+    partial is O = 0, lse = -inf, and merged into a running result it leaves
+    that result as it was.  No key or value memory is read."""
+    B, Hkv, n, d = 1, 2, 130, 128
+    say(f"empty key chunk {in_dt} Hq={Hq}")
+    (q, k, v), (qd, kd, vd) = _inputs(in_dt, B, Hq, Hkv, n, 200, d, seed=21)
+    ke, ve = kd[:, :, :0], vd[:, :, :0]
+    ref_e, ref_le = oracle.attention_fp64(q, k[:, :, :0], v[:, :, :0])
+    o, lse = _out(B, Hq, n, d, torch.float32)
+    api.ra_chunk_attention(qd, ke, ve, o, lse)
+    torch.cuda.synchronize()
+    tol = "bf16" if in_dt == "bf16" else "f32"
+    check_close(host_f64(o), ref_e, tol, "empty partial O")
+    check_close(host_f64(lse).reshape(ref_le.shape), ref_le, tol, "empty partial lse")
+    # a running result from 200 real keys, then the empty chunk merged in
+    o1, l1 = _out(B, Hq, n, d, torch.float32)
+    api.ra_chunk_attention(qd, kd, vd, o1, l1)
+    o2, l2 = _out(B, Hq, n, d, torch.float32)
+    api.ra_chunk_attention(qd, ke, ve, o2, l2, o_in=o1, lse_in=l1)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.lse_merge_fp64(host_f64(o1), host_f64(l1).reshape(ref_le.shape), ref_e, ref_le)
+    check_close(host_f64(o2), ref_o, tol, "merged O")
+    check_close(host_f64(l2).reshape(ref_l.shape), ref_l, tol, "merged lse")
+
+
 @pytest.mark.parametrize("in_dt,Hq", [("f32", 2), ("f32", 160), ("bf16", 2)],
                          ids=["f32-split_kernel", "f32-shared_kernel", "bf16"])
 def test_running_max_rescale(api, in_dt, Hq):
